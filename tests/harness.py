@@ -1,0 +1,88 @@
+"""Shared test plumbing: running a synthetic workload through the CPU oracle,
+building tiny hand-made instances, and checking gathered rows against the
+content each token must hold."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import hs_gen
+import oracle
+
+ROW = hs_gen.ROW_BYTES
+PAGE = hs_gen.PAGE
+
+
+class OracleRun:
+    """The full state of a workload on the CPU, advanced step by step by the oracle."""
+
+    def __init__(self, wl: hs_gen.Workload):
+        self.wl = wl
+        self.pool = np.zeros((wl.L, wl.pool_rows, ROW), dtype=np.uint8)
+        self.host = np.zeros((wl.L, wl.host_rows, ROW), dtype=np.uint8)
+        wl.fill_device_pool(torch.from_numpy(self.pool))
+        wl.fill_host_pool(torch.from_numpy(self.host))
+        self.bt = wl.block_table.copy()
+        self.hbt = wl.host_block_table.copy()
+        self.hot = wl.hot_blocks.copy()
+        self.ctx = wl.ctx0.copy()
+        self.tok = np.full((wl.R, wl.L, wl.C), -1, dtype=np.int32)
+        self.stp = np.zeros((wl.R, wl.L, wl.C), dtype=np.uint32)
+
+    def pre(self, step: hs_gen.Step) -> None:
+        for r, p, v in step.hbt_set:
+            self.hbt[r, p] = v
+        for r, p, v in step.bt_set:
+            self.bt[r, p] = v
+        self.ctx = step.ctx.copy()
+
+    def resolve(self, step: hs_gen.Step, gather: bool = True, topk=None, stamp=None):
+        topk = step.topk if topk is None else topk
+        stamp = step.stamp if stamp is None else stamp
+        return oracle.resolve(self.pool, self.host, self.bt, self.hbt, self.ctx, self.hot,
+                              self.tok, self.stp, np.ascontiguousarray(topk), stamp, gather)
+
+    def post(self, step: hs_gen.Step) -> None:
+        if step.offload.shape[0]:
+            oracle.offload(self.pool, self.host, step.offload)
+
+
+def expected_content(wl: hs_gen.Workload, topk: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """What every gathered row must hold, from the token alone: its synthetic
+    content where a row was resolved (row id >= 0), zeros elsewhere."""
+    R, L = topk.shape[:2]
+    t = topk.reshape(R, L, -1).astype(np.int64)
+    lay = np.broadcast_to(np.arange(L)[None, :, None], t.shape)
+    src = np.broadcast_to(wl.src[:, None, None], t.shape)
+    exp = hs_gen.content_np(lay.ravel(), src.ravel(), t.ravel()).reshape(t.shape + (ROW,))
+    ok = rows.reshape(R, L, -1) >= 0
+    exp[~ok] = 0
+    return exp.reshape(topk.shape + (ROW,))
+
+
+def tiny_instance(page=4, ctx=24, C=8, hot_blocks=(9, 6), bt=(-1, -1, -1, -1, 7, 2),
+                  hbt=(3, 0, 5, 1, 4, 2), n_blocks=10, n_host=6, seed=7):
+    """The hand-worked instance: pool and host rows carry recognisable bytes
+    (row r of layer 0 starts with r as little-endian int32, plus a tag byte)."""
+    pool = np.zeros((1, n_blocks * page, ROW), dtype=np.uint8)
+    host = np.zeros((1, n_host * page, ROW), dtype=np.uint8)
+    for r in range(n_blocks * page):
+        pool[0, r, :4] = np.frombuffer(np.int32(r).tobytes(), np.uint8)
+        pool[0, r, 4] = 0xD0
+    for r in range(n_host * page):
+        host[0, r, :4] = np.frombuffer(np.int32(r).tobytes(), np.uint8)
+        host[0, r, 4] = 0x40
+    return dict(
+        page=page, pool=pool, host=host,
+        bt=np.array([bt], dtype=np.int32), hbt=np.array([hbt], dtype=np.int32),
+        ctx=np.array([ctx], dtype=np.int32), hot=np.array([hot_blocks], dtype=np.int32),
+        tok=np.full((1, 1, C), -1, dtype=np.int32), stp=np.zeros((1, 1, C), dtype=np.uint32))
+
+
+def run_tiny(inst, topk, stamp, gather=True):
+    t = np.asarray(topk, dtype=np.int32)
+    t = t.reshape((1, 1) + t.shape) if t.ndim == 1 else t.reshape((1, 1) + t.shape)
+    return oracle.resolve(inst["pool"], inst["host"], inst["bt"], inst["hbt"], inst["ctx"],
+                          inst["hot"], inst["tok"], inst["stp"], t, stamp, gather,
+                          page=inst["page"])
