@@ -52,16 +52,20 @@ def content_torch(layer, src, tok) -> torch.Tensor:
 
 
 def fill_rows(dst: torch.Tensor, rows: torch.Tensor, layer: int, src: torch.Tensor,
-              tok: torch.Tensor, chunk: int = 1 << 16) -> None:
+              tok: torch.Tensor, chunk: int = 1 << 16, compute_device=None) -> None:
     """Write content(layer, src[i], tok[i]) into row ``rows[i]`` of ``dst``.
 
     ``dst`` is a uint8 [n_rows, 656] view of one layer of a pool (any device);
-    ``rows``, ``src`` and ``tok`` are int64 tensors of equal length.
+    ``rows``, ``src`` and ``tok`` are int64 tensors of equal length.  The
+    content is computed on ``compute_device`` (default: dst's device) and
+    copied into ``dst``.
     """
     n = rows.numel()
-    dev = dst.device
+    dev = torch.device(compute_device) if compute_device is not None else dst.device
+    if dev.type != "cpu" or dst.device.type != "cpu":
+        chunk = max(chunk, 1 << 20)
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
-        r = rows[s:e].to(dev)
         lay = torch.full((e - s,), layer, dtype=torch.int64, device=dev)
-        dst.index_copy_(0, r, content_torch(lay, src[s:e].to(dev), tok[s:e].to(dev)))
+        rowsv = content_torch(lay, src[s:e].to(dev), tok[s:e].to(dev))
+        dst.index_copy_(0, rows[s:e].to(dst.device), rowsv.to(dst.device))

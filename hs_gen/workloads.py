@@ -91,22 +91,26 @@ class Workload:
         return self.R * self.L * self.P * self.K
 
     # -- content -----------------------------------------------------------
-    def fill_device_pool(self, pool: torch.Tensor) -> None:
+    def fill_device_pool(self, pool: torch.Tensor, compute_device=None, requests=None) -> None:
         """Write every resident page's rows into ``pool`` (uint8 [L, rows, 656]).
 
         Hot blocks and unused blocks are left as they are (callers pass a
         zeroed pool).  Pages that become resident later in the run are written
         up front; their tokens stay invalid until the context reaches them.
+        ``requests`` limits the fill to the pages of those requests.
         """
-        r, p, b = self.dev_pages[:, 0], self.dev_pages[:, 1], self.dev_pages[:, 2]
+        dp = self.dev_pages
+        if requests is not None:
+            dp = dp[np.isin(dp[:, 0], np.asarray(requests))]
+        r, p, b = dp[:, 0], dp[:, 1], dp[:, 2]
         o = np.arange(PAGE, dtype=np.int64)
         rows = torch.from_numpy((b[:, None] * PAGE + o[None, :]).ravel())
         toks = torch.from_numpy((p[:, None] * PAGE + o[None, :]).ravel())
         srcs = torch.from_numpy(np.repeat(self.src[r], PAGE))
         for layer in range(self.L):
-            fill_rows(pool[layer], rows, layer, srcs, toks)
+            fill_rows(pool[layer], rows, layer, srcs, toks, compute_device=compute_device)
 
-    def fill_host_pool(self, host: torch.Tensor) -> None:
+    def fill_host_pool(self, host: torch.Tensor, compute_device=None) -> None:
         """Write the initial host copies into ``host`` (uint8 [L, host_rows, 656])."""
         hb, base = self.host_pages[:, 0], self.host_pages[:, 1]
         o = np.arange(PAGE, dtype=np.int64)
@@ -114,7 +118,7 @@ class Workload:
         toks = torch.from_numpy((base[:, None] * PAGE + o[None, :]).ravel())
         srcs = torch.from_numpy(np.repeat(self.host_src, PAGE))
         for layer in range(self.L):
-            fill_rows(host[layer], rows, layer, srcs, toks)
+            fill_rows(host[layer], rows, layer, srcs, toks, compute_device=compute_device)
 
 
 # ---------------------------------------------------------------------------

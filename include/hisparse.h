@@ -1,0 +1,187 @@
+/*
+ * hisparse.h -- C ABI of the MI355X (gfx950) Hybrid HiSparse hot path:
+ * the fused sparse-MLA top-K resolver, the single-stride row gather, the
+ * post-forward prefix-page offload and the replayable per-step plan.
+ *
+ * Source of the method: "vLLM GLM 5.3 ... Hybrid HiSparse offloading, Part 1"
+ * (blog post, three renderings).  Sections cited:
+ *   "How it works"            -- residency states, null placeholders, the
+ *                                fused resolver, row ids, proactive copy,
+ *                                one post-forward launch over all layers;
+ *   "How it works" figure     -- a miss copies one row, a hit copies none;
+ *   "Integration with the rest of vLLM" -- replayable resolve plans for
+ *                                speculative decoding; 2 x top-K hot rows.
+ *
+ * General rules for every call below
+ *   - Asynchronous: work is enqueued on the caller's HIP stream; nothing waits
+ *     for the host ("nothing on the decode path waits on a CPU decision",
+ *     "How it works").  No call allocates memory.
+ *   - The caller owns every buffer.  Device pointers must come from hipMalloc
+ *     (or a PyTorch CUDA tensor); the host pool must be pinned, device-mapped
+ *     memory (hs_host_alloc) and is passed as its device-visible address.
+ *   - The return value reports only what the host can check before any
+ *     launch (null pointers, sizes, limits); on error nothing is enqueued.
+ *     Data-dependent outcomes are reported per entry (sentinel row ids) and
+ *     per request-layer (the stats record), never through the return value.
+ *   - Calls on disjoint state may run concurrently; calls that share state
+ *     (slot_token / slot_stamp / pool rows) must be ordered by the caller.
+ *
+ * Data layout (all little-endian, all row ids int32):
+ *   kv_pool    uint8 [L][pool_rows][row_bytes], layer l at l * pool_layer_stride
+ *              bytes.  Row id = block * page_size + offset, the same id in every
+ *              layer.  Resident pages and hot pages live in this one pool.
+ *   host_pool  uint8 [L][host_rows][row_bytes], layer stride host_layer_stride.
+ *   block_table, host_block_table   int32 [R][max_pages]; entry < 0 = null
+ *              placeholder / no host copy.
+ *   ctx_len    int32 [R]: tokens 0..ctx-1 are valid.
+ *   hot_blocks int32 [R][C / page_size]: the pool blocks leased as the
+ *              request's hot buffer; slot q lives at row
+ *              hot_blocks[q / page_size] * page_size + q % page_size.
+ *   slot_token int32  [R][L][C]: token held by each slot, < 0 = empty.
+ *   slot_stamp uint32 [R][L][C]: LRU stamp of each slot, 0 = never used.
+ *   topk       int32 [R][L][P][K] (P = 1 for hs_resolve); -1 = padding.
+ *   row_ids    int32, same shape as topk:  >= 0 pool row;  -1 padding;
+ *              -2 overflow (no hot slot left; only possible with P > 1);
+ *              -3 invalid (outside [0, ctx), or neither resident nor on host).
+ *   stats      int32 [R][L][8] = {resident, hit, miss, overflow, invalid,
+ *              pad, dup, 0}; the first five count distinct tokens, pad and
+ *              dup count entries; they always sum to P * K.
+ *   gather_out uint8 [R][L][P][K][row_bytes].
+ */
+#ifndef HISPARSE_H
+#define HISPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hs_status;
+#define HS_OK 0
+#define HS_ERR_INVALID_ARGUMENT 1 /* a null pointer, a size out of range */
+#define HS_ERR_UNSUPPORTED 2      /* valid, but beyond this build's kernel limits */
+#define HS_ERR_LAUNCH 3           /* the HIP runtime refused a launch */
+#define HS_ERR_HIP 4              /* another HIP runtime call failed */
+
+/* Limits of the resolver kernel (one workgroup per request-layer, state in LDS). */
+#define HS_MAX_ENTRIES 8192       /* P * K per request-layer */
+#define HS_MAX_HOT_CAPACITY 8192  /* C */
+
+typedef struct {
+  int32_t page_size;          /* tokens per page: a power of two, 1..4096 (64 here) */
+  int32_t row_bytes;          /* bytes per KV row: a positive multiple of 16 (656 here) */
+  int32_t num_layers;         /* L >= 1 */
+  int32_t hot_capacity;       /* C: hot slots per request-layer, a multiple of page_size */
+  int64_t pool_rows;          /* rows per layer in kv_pool: multiple of page_size, < 2^31 */
+  int64_t host_rows;          /* rows per layer in host_pool: multiple of page_size, < 2^31 */
+  int64_t pool_layer_stride;  /* bytes between layers of kv_pool, >= pool_rows * row_bytes */
+  int64_t host_layer_stride;  /* bytes between layers of host_pool, >= host_rows * row_bytes */
+} hs_layout;
+
+typedef struct {
+  int32_t num_reqs;                 /* R >= 0 */
+  int32_t max_pages;                /* columns of both block tables, >= 1 */
+  uint8_t* kv_pool;                 /* device; hot-slot rows are written */
+  const uint8_t* host_pool;         /* pinned host pool, device-visible address */
+  const int32_t* block_table;       /* device [R][max_pages] */
+  const int32_t* host_block_table;  /* device [R][max_pages] */
+  const int32_t* ctx_len;           /* device [R] */
+  const int32_t* hot_blocks;        /* device [R][C / page_size] */
+  int32_t* slot_token;              /* device [R][L][C], read and updated */
+  uint32_t* slot_stamp;             /* device [R][L][C], read and updated */
+} hs_batch;
+
+/*
+ * hs_resolve -- the fused top-K resolver ("How it works": mixed residency;
+ * the figure's solid and dotted arrows).  For every request r and layer l,
+ * resolves the K entries topk[r][l][*] to pool rows:
+ *   - a token whose page has a real block-table entry is read in place:
+ *     row = block * page_size + token % page_size; the hot buffer is not
+ *     consulted;
+ *   - the distinct remaining tokens are looked up in the request-layer's hot
+ *     buffer; a hit refreshes the slot's stamp to `stamp`, copies nothing;
+ *   - the distinct misses (tokens with a host copy, not in the buffer), in
+ *     ascending token order, take the non-hit slots in ascending
+ *     (stamp, slot) order -- least recently used first, empty slots first --
+ *     and each copies exactly one row from host_pool into its slot, which then
+ *     holds the token with stamp `stamp`;
+ *   - all decisions read the state as it was before the call.
+ * Slots whose hot block lies outside the pool are never used; block-table,
+ * host-table and pair entries outside their pools are treated as absent.
+ * Arguments: top_k = K (1..HS_MAX_ENTRIES); stamp > 0, normally the step
+ * counter (calling again with the same inputs and the same stamp leaves the
+ * state unchanged); gather_out may be NULL, otherwise it receives the rows
+ * gathered after every copy of this call (as hs_gather would).
+ * Errors: HS_ERR_INVALID_ARGUMENT (null pointer, stamp 0, bad layout),
+ * HS_ERR_UNSUPPORTED (K or C over the limits), HS_ERR_LAUNCH.
+ */
+hs_status hs_resolve(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                     int32_t top_k, uint32_t stamp, int32_t* row_ids, uint8_t* gather_out,
+                     int32_t* stats, hipStream_t stream);
+
+/*
+ * hs_gather -- the single-stride gather ("How it works": the resolver hands
+ * back a row id whether the row is resident or hot, and the rows are gathered
+ * at one stride).  out[r][l][i] = kv_pool[l][row_ids[r][l][i]] (row_bytes
+ * bytes); a row id < 0 or >= pool_rows yields a zero row.
+ * Arguments: kv_pool device; row_ids device int32 [num_reqs][L][rows_per_req_layer];
+ * out device uint8 [num_reqs][L][rows_per_req_layer][row_bytes].
+ * Errors: HS_ERR_INVALID_ARGUMENT, HS_ERR_LAUNCH.
+ */
+hs_status hs_gather(const hs_layout* layout, const uint8_t* kv_pool, const int32_t* row_ids,
+                    int32_t num_reqs, int32_t rows_per_req_layer, uint8_t* out,
+                    hipStream_t stream);
+
+/*
+ * hs_offload_prefix_pages -- the post-forward batched prefix copy ("How it
+ * works": completed cacheable prefix pages are copied to host while still
+ * served from the GPU, in one launch over all sparse layers, ordered on the
+ * model's stream).  For each pair i and every layer l, copies the
+ * page_size rows of device block pairs[i][0] to host block pairs[i][1].
+ * Pairs naming a block outside either pool are skipped.  Host blocks must be
+ * distinct within one call.  Stream-later work may reuse the device block at
+ * once; host readers must wait for the stream (an event or a sync).
+ * Arguments: pairs device int32 [n][2] = {device block, host block}; n >= 0.
+ * Errors: HS_ERR_INVALID_ARGUMENT, HS_ERR_LAUNCH.
+ */
+hs_status hs_offload_prefix_pages(const hs_layout* layout, const uint8_t* kv_pool,
+                                  uint8_t* host_pool, const int32_t* pairs, int32_t n,
+                                  hipStream_t stream);
+
+/*
+ * hs_plan_replay -- a per-step replayable resolve plan for speculative decoding
+ * ("Integration with the rest of vLLM": one plan per step sharing the
+ * request's hot state).  The P query positions of each request-layer are
+ * resolved as one list of P * K entries with one stamp commit (a token shared
+ * by several positions is resolved once and every position gets its row);
+ * then the optional gather, then the optional prefix offload of
+ * offload_pairs[n_offload][2] -- all on `stream`, in that order.
+ * num_pos = 1 with no offload is exactly hs_resolve.  Misses beyond the
+ * free slots overflow (row -2) and leave the state untouched for them.
+ * Errors: as hs_resolve; P * K over HS_MAX_ENTRIES is HS_ERR_UNSUPPORTED.
+ */
+hs_status hs_plan_replay(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                         int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
+                         uint8_t* gather_out, int32_t* stats, const int32_t* offload_pairs,
+                         int32_t n_offload, hipStream_t stream);
+
+/* A static English description of a status code. */
+const char* hs_status_string(hs_status status);
+
+/* Pinned host memory for the host pool, mapped into the device address space.
+ * *host_ptr is the host address; hs_host_device_pointer gives the address
+ * kernels use (equal on ROCm, but callers should not rely on that).
+ * Errors: HS_ERR_INVALID_ARGUMENT (null out-pointer), HS_ERR_HIP. */
+hs_status hs_host_alloc(size_t bytes, void** host_ptr);
+hs_status hs_host_free(void* host_ptr);
+hs_status hs_host_device_pointer(void* host_ptr, void** device_ptr);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HISPARSE_H */

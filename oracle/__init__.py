@@ -75,7 +75,7 @@ def gather(pool: np.ndarray, rows: np.ndarray, page: int = PAGE) -> np.ndarray:
     _check(rows, np.int32, "rows")
     L, pool_rows, rb = pool.shape
     R, L2, N = rows.shape
-    assert L2 == L and rb == ROW_BYTES
+    assert L2 == L and rb % 16 == 0
     out = np.empty((R, L, N, rb), dtype=np.uint8)
     _load().oracle_gather(page, rb, pool_rows, pool_rows * rb, R, L, N, _ptr(pool), _ptr(rows),
                           _ptr(out))
@@ -89,7 +89,7 @@ def offload(pool: np.ndarray, host: np.ndarray, pairs: np.ndarray, page: int = P
     pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
     L, pool_rows, rb = pool.shape
     L2, host_rows, rb2 = host.shape
-    assert L2 == L and rb == rb2 == ROW_BYTES
+    assert L2 == L and rb == rb2 and rb % 16 == 0
     _load().oracle_offload(page, rb, L, pool_rows, pool_rows * rb, host_rows, host_rows * rb,
                            _ptr(pool), _ptr(host), _ptr(pairs), pairs.shape[0])
 

@@ -1,0 +1,241 @@
+// C ABI of the Hybrid HiSparse hot path (declared in include/hisparse.h):
+// argument validation, launch shapes and HIP error mapping.  Every entry
+// point validates everything the host can see before enqueuing anything,
+// then enqueues its kernels on the caller's stream and returns without
+// waiting ("How it works": nothing on the decode path waits on the CPU).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hisparse.h"
+#include "hs_internal.h"
+
+namespace {
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+  int s = 0;
+  while ((int64_t(1) << s) < x) ++s;
+  return s;
+}
+
+// Checks shared by every call that reads the pool layout.
+hs_status check_layout(const hs_layout* lay) {
+  if (!lay) return HS_ERR_INVALID_ARGUMENT;
+  if (!is_pow2(lay->page_size) || lay->page_size > 4096) return HS_ERR_INVALID_ARGUMENT;
+  if (lay->row_bytes <= 0 || lay->row_bytes % 16 != 0 || lay->row_bytes > (1 << 20))
+    return HS_ERR_INVALID_ARGUMENT;
+  if (lay->num_layers < 1 || lay->num_layers > 65535) return HS_ERR_INVALID_ARGUMENT;
+  if (lay->pool_rows <= 0 || lay->pool_rows % lay->page_size != 0 || lay->pool_rows > INT32_MAX)
+    return HS_ERR_INVALID_ARGUMENT;
+  if (lay->host_rows < 0 || lay->host_rows % lay->page_size != 0 || lay->host_rows > INT32_MAX)
+    return HS_ERR_INVALID_ARGUMENT;
+  if (lay->num_layers > 1) {
+    if (lay->pool_layer_stride < lay->pool_rows * lay->row_bytes) return HS_ERR_INVALID_ARGUMENT;
+    if (lay->host_layer_stride < lay->host_rows * lay->row_bytes) return HS_ERR_INVALID_ARGUMENT;
+  }
+  return HS_OK;
+}
+
+hs_status check_hot(const hs_layout* lay) {
+  if (lay->hot_capacity < lay->page_size || lay->hot_capacity % lay->page_size != 0)
+    return HS_ERR_INVALID_ARGUMENT;
+  if (lay->hot_capacity > HS_MAX_HOT_CAPACITY) return HS_ERR_UNSUPPORTED;
+  return HS_OK;
+}
+
+hs_status from_hip(hipError_t e) { return e == hipSuccess ? HS_OK : HS_ERR_LAUNCH; }
+
+hs_status check_gather(const hs_layout* lay, int64_t n_rl, int64_t rows_per_rl) {
+  const int64_t pieces = lay->row_bytes / 16;
+  if (rows_per_rl * pieces >= (int64_t(1) << 32)) return HS_ERR_UNSUPPORTED;
+  const int64_t per = hs::kCopyThreads * hs::kCopyUnroll;
+  const int64_t blocks = n_rl * ((rows_per_rl * pieces + per - 1) / per);
+  if (blocks >= (int64_t(1) << 32)) return HS_ERR_UNSUPPORTED;
+  return HS_OK;
+}
+
+hs_status check_offload(int32_t n) {
+  if (n < 0) return HS_ERR_INVALID_ARGUMENT;
+  return HS_OK;
+}
+
+hs::OffloadParams offload_params(const hs_layout* lay, const uint8_t* pool, uint8_t* host,
+                                 const int32_t* pairs, int32_t n) {
+  hs::OffloadParams o;
+  o.pool = pool;
+  o.pool_stride = lay->pool_layer_stride;
+  o.pool_blocks = lay->pool_rows / lay->page_size;
+  o.host = host;
+  o.host_stride = lay->host_layer_stride;
+  o.host_blocks = lay->host_rows / lay->page_size;
+  o.page_bytes = (int64_t)lay->page_size * lay->row_bytes;
+  o.num_layers = lay->num_layers;
+  o.pairs = pairs;
+  o.n = n;
+  return o;
+}
+
+hs::GatherParams gather_params(const hs_layout* lay, const uint8_t* pool, const int32_t* rows,
+                               int32_t num_reqs, int32_t rows_per_rl, uint8_t* out) {
+  hs::GatherParams g;
+  g.pool = pool;
+  g.pool_rows = lay->pool_rows;
+  g.pool_stride = lay->pool_layer_stride;
+  g.row_bytes = lay->row_bytes;
+  g.num_layers = lay->num_layers;
+  g.row_ids = rows;
+  g.num_reqs = num_reqs;
+  g.rows_per_rl = rows_per_rl;
+  g.out = out;
+  return g;
+}
+
+// Shared body of hs_resolve and hs_plan_replay.
+hs_status resolve_common(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
+                         int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
+                         uint8_t* gather_out, int32_t* stats, const int32_t* offload_pairs,
+                         int32_t n_offload, hipStream_t stream) {
+  hs_status s = check_layout(lay);
+  if (s != HS_OK) return s;
+  if ((s = check_hot(lay)) != HS_OK) return s;
+  if (!b || !topk || !row_ids || !stats) return HS_ERR_INVALID_ARGUMENT;
+  if (b->num_reqs < 0 || b->max_pages < 1) return HS_ERR_INVALID_ARGUMENT;
+  if (num_pos < 1 || top_k < 1) return HS_ERR_INVALID_ARGUMENT;
+  if (stamp == 0) return HS_ERR_INVALID_ARGUMENT;
+  if ((int64_t)num_pos * top_k > HS_MAX_ENTRIES) return HS_ERR_UNSUPPORTED;
+  if ((s = check_offload(n_offload)) != HS_OK) return s;
+  if (n_offload > 0 && !offload_pairs) return HS_ERR_INVALID_ARGUMENT;
+  const int64_t n_rl = (int64_t)b->num_reqs * lay->num_layers;
+  if (n_rl > INT32_MAX) return HS_ERR_UNSUPPORTED;
+  const int32_t N = num_pos * top_k;
+  if (gather_out && (s = check_gather(lay, n_rl, N)) != HS_OK) return s;
+  if (b->num_reqs > 0) {
+    if (!b->kv_pool || !b->block_table || !b->host_block_table || !b->ctx_len ||
+        !b->hot_blocks || !b->slot_token || !b->slot_stamp)
+      return HS_ERR_INVALID_ARGUMENT;
+    if (!b->host_pool && lay->host_rows > 0) return HS_ERR_INVALID_ARGUMENT;
+  }
+  if (n_offload > 0 && (!b->kv_pool || !b->host_pool)) return HS_ERR_INVALID_ARGUMENT;
+
+  if (n_rl > 0) {
+    hs::ResolveParams p;
+    p.page_shift = log2i(lay->page_size);
+    p.row_bytes = lay->row_bytes;
+    p.num_layers = lay->num_layers;
+    p.hot_capacity = lay->hot_capacity;
+    p.pool_rows = lay->pool_rows;
+    p.host_rows = lay->host_rows;
+    p.pool_stride = lay->pool_layer_stride;
+    p.host_stride = lay->host_layer_stride;
+    p.num_reqs = b->num_reqs;
+    p.max_pages = b->max_pages;
+    p.pool = b->kv_pool;
+    p.host = b->host_pool;
+    p.block_table = b->block_table;
+    p.host_block_table = b->host_block_table;
+    p.ctx_len = b->ctx_len;
+    p.hot_blocks = b->hot_blocks;
+    p.slot_token = b->slot_token;
+    p.slot_stamp = b->slot_stamp;
+    p.topk = topk;
+    p.entries = N;
+    p.stamp = stamp;
+    p.row_ids = row_ids;
+    p.stats = stats;
+    if ((s = from_hip(hs::launch_resolve(p, stream))) != HS_OK) return s;
+    if (gather_out) {
+      hs::GatherParams g = gather_params(lay, b->kv_pool, row_ids, b->num_reqs, N, gather_out);
+      if ((s = from_hip(hs::launch_gather(g, stream))) != HS_OK) return s;
+    }
+  }
+  if (n_offload > 0) {
+    hs::OffloadParams o = offload_params(lay, b->kv_pool, const_cast<uint8_t*>(b->host_pool),
+                                         offload_pairs, n_offload);
+    if ((s = from_hip(hs::launch_offload(o, stream))) != HS_OK) return s;
+  }
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_resolve(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                     int32_t top_k, uint32_t stamp, int32_t* row_ids, uint8_t* gather_out,
+                     int32_t* stats, hipStream_t stream) {
+  return resolve_common(layout, batch, topk, 1, top_k, stamp, row_ids, gather_out, stats,
+                        nullptr, 0, stream);
+}
+
+hs_status hs_plan_replay(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                         int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
+                         uint8_t* gather_out, int32_t* stats, const int32_t* offload_pairs,
+                         int32_t n_offload, hipStream_t stream) {
+  return resolve_common(layout, batch, topk, num_pos, top_k, stamp, row_ids, gather_out, stats,
+                        offload_pairs, n_offload, stream);
+}
+
+hs_status hs_gather(const hs_layout* layout, const uint8_t* kv_pool, const int32_t* row_ids,
+                    int32_t num_reqs, int32_t rows_per_req_layer, uint8_t* out,
+                    hipStream_t stream) {
+  hs_status s = check_layout(layout);
+  if (s != HS_OK) return s;
+  if (num_reqs < 0 || rows_per_req_layer < 0) return HS_ERR_INVALID_ARGUMENT;
+  const int64_t n_rl = (int64_t)num_reqs * layout->num_layers;
+  if (n_rl == 0 || rows_per_req_layer == 0) return HS_OK;
+  if (!kv_pool || !row_ids || !out) return HS_ERR_INVALID_ARGUMENT;
+  if ((s = check_gather(layout, n_rl, rows_per_req_layer)) != HS_OK) return s;
+  return from_hip(hs::launch_gather(
+      gather_params(layout, kv_pool, row_ids, num_reqs, rows_per_req_layer, out), stream));
+}
+
+hs_status hs_offload_prefix_pages(const hs_layout* layout, const uint8_t* kv_pool,
+                                  uint8_t* host_pool, const int32_t* pairs, int32_t n,
+                                  hipStream_t stream) {
+  hs_status s = check_layout(layout);
+  if (s != HS_OK) return s;
+  if ((s = check_offload(n)) != HS_OK) return s;
+  if (n == 0) return HS_OK;
+  if (!kv_pool || !host_pool || !pairs) return HS_ERR_INVALID_ARGUMENT;
+  return from_hip(hs::launch_offload(offload_params(layout, kv_pool, host_pool, pairs, n), stream));
+}
+
+const char* hs_status_string(hs_status status) {
+  switch (status) {
+    case HS_OK: return "ok";
+    case HS_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case HS_ERR_UNSUPPORTED: return "unsupported size (beyond the kernel limits)";
+    case HS_ERR_LAUNCH: return "kernel launch failed";
+    case HS_ERR_HIP: return "HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+hs_status hs_host_alloc(size_t bytes, void** host_ptr) {
+  if (!host_ptr) return HS_ERR_INVALID_ARGUMENT;
+  *host_ptr = nullptr;
+  if (bytes == 0) return HS_ERR_INVALID_ARGUMENT;
+  void* p = nullptr;
+  if (hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocPortable) != hipSuccess)
+    return HS_ERR_HIP;
+  *host_ptr = p;
+  return HS_OK;
+}
+
+hs_status hs_host_free(void* host_ptr) {
+  if (!host_ptr) return HS_OK;
+  return hipHostFree(host_ptr) == hipSuccess ? HS_OK : HS_ERR_HIP;
+}
+
+hs_status hs_host_device_pointer(void* host_ptr, void** device_ptr) {
+  if (!host_ptr || !device_ptr) return HS_ERR_INVALID_ARGUMENT;
+  *device_ptr = nullptr;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, host_ptr, 0) != hipSuccess) return HS_ERR_HIP;
+  *device_ptr = d;
+  return HS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+"""Device-side driver for a workload: owns the GPU buffers of one batch (pool,
+pinned host pool, tables, hot-buffer state) and steps it through the hot path.
+
+Between steps it applies the scheduler's decisions the workload describes --
+nulling pages that left the resident tail, recording new host copies -- as
+plain device-tensor writes; these are host-side residency policy, not part of
+the hot path.  Each step then calls the C ABI through the binding:
+``hs_resolve`` (or ``hs_plan_replay`` for several query positions), whose
+gather runs on the same stream, and after the step ``hs_offload_prefix_pages``
+for the pages that completed.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .api import (HostPool, batch_of, hs_gather, hs_offload_prefix_pages, hs_plan_replay,
+                  hs_resolve, layout_of)
+
+PAGE = 64
+ROW = 656
+
+
+class DeviceRun:
+    def __init__(self, wl, device: str = "cuda", content_device: str | None = None):
+        self.wl = wl
+        dev = torch.device(device)
+        self.device = dev
+        cdev = content_device or device
+        self.pool = torch.zeros((wl.L, wl.pool_rows, ROW), dtype=torch.uint8, device=dev)
+        wl.fill_device_pool(self.pool, compute_device=cdev)
+        self.host_pool = HostPool(wl.L * wl.host_rows * ROW)
+        self.host = self.host_pool.tensor.view(wl.L, wl.host_rows, ROW)
+        self.host.zero_()
+        wl.fill_host_pool(self.host, compute_device=cdev)
+        i32 = torch.int32
+        self.bt = torch.from_numpy(wl.block_table).to(dev)
+        self.hbt = torch.from_numpy(wl.host_block_table).to(dev)
+        self.ctx = torch.from_numpy(wl.ctx0.astype(np.int32)).to(dev)
+        self.hot = torch.from_numpy(wl.hot_blocks).to(dev)
+        self.tok = torch.full((wl.R, wl.L, wl.C), -1, dtype=i32, device=dev)
+        self.stp = torch.zeros((wl.R, wl.L, wl.C), dtype=i32, device=dev)  # uint32 bits
+        N = wl.P * wl.K
+        self.rows = torch.empty((wl.R, wl.L, wl.P, wl.K), dtype=i32, device=dev)
+        self.stats = torch.empty((wl.R, wl.L, 8), dtype=i32, device=dev)
+        self.out = torch.empty((wl.R, wl.L, wl.P, wl.K, ROW), dtype=torch.uint8, device=dev)
+        self.layout = layout_of(PAGE, ROW, wl.L, wl.C, wl.pool_rows, wl.host_rows)
+        self.batch = batch_of(wl.R, wl.max_pages, self.pool, self.host_pool, self.bt, self.hbt,
+                              self.ctx, self.hot, self.tok, self.stp)
+        self.entries = N
+        self.topk = [None] * len(wl.steps)
+        self.pairs = [None] * len(wl.steps)
+
+    # -- scheduler side (between steps) ------------------------------------
+    def upload_steps(self) -> None:
+        """Put every step's top-K lists and offload pairs in device memory."""
+        for i, s in enumerate(self.wl.steps):
+            self.topk[i] = torch.from_numpy(np.ascontiguousarray(s.topk)).to(self.device)
+            self.pairs[i] = (torch.from_numpy(np.ascontiguousarray(s.offload)).to(self.device)
+                             if s.offload.shape[0] else None)
+
+    def pre(self, i: int) -> None:
+        s = self.wl.steps[i]
+        for arr, t in ((s.hbt_set, self.hbt), (s.bt_set, self.bt)):
+            if arr.shape[0]:
+                a = torch.from_numpy(arr).to(self.device)
+                t[a[:, 0], a[:, 1]] = a[:, 2].to(torch.int32)
+        self.ctx.copy_(torch.from_numpy(s.ctx.astype(np.int32)))
+
+    # -- hot path -----------------------------------------------------------
+    def resolve(self, i: int, gather: bool = True, stamp: int | None = None, topk=None,
+                stream=None) -> None:
+        s = self.wl.steps[i]
+        if topk is None:
+            if self.topk[i] is None:
+                self.topk[i] = torch.from_numpy(np.ascontiguousarray(s.topk)).to(self.device)
+            topk = self.topk[i]
+        stamp = s.stamp if stamp is None else stamp
+        out = self.out if gather else None
+        if self.wl.P == 1:
+            hs_resolve(self.layout, self.batch, topk, self.wl.K, stamp, self.rows, out,
+                       self.stats, stream)
+        else:
+            hs_plan_replay(self.layout, self.batch, topk, self.wl.P, self.wl.K, stamp, self.rows,
+                           out, self.stats, None, 0, stream)
+
+    def gather(self, stream=None) -> None:
+        hs_gather(self.layout, self.pool, self.rows, self.wl.R, self.entries, self.out, stream)
+
+    def post(self, i: int, stream=None) -> None:
+        s = self.wl.steps[i]
+        if s.offload.shape[0] == 0:
+            return
+        if self.pairs[i] is None:
+            self.pairs[i] = torch.from_numpy(np.ascontiguousarray(s.offload)).to(self.device)
+        hs_offload_prefix_pages(self.layout, self.pool, self.host_pool, self.pairs[i],
+                                s.offload.shape[0], stream)
+
+    def plan_step(self, i: int, gather: bool = True, stream=None) -> None:
+        """resolve + gather + offload of the step's completed pages, one call."""
+        s = self.wl.steps[i]
+        if self.topk[i] is None:
+            self.topk[i] = torch.from_numpy(np.ascontiguousarray(s.topk)).to(self.device)
+        n = s.offload.shape[0]
+        if n and self.pairs[i] is None:
+            self.pairs[i] = torch.from_numpy(np.ascontiguousarray(s.offload)).to(self.device)
+        hs_plan_replay(self.layout, self.batch, self.topk[i], self.wl.P, self.wl.K, s.stamp,
+                       self.rows, self.out if gather else None, self.stats,
+                       self.pairs[i] if n else None, n, stream)
+
+    def close(self) -> None:
+        self.host = None
+        self.host_pool.close()

@@ -15,46 +15,71 @@ PAGE = hs_gen.PAGE
 
 
 class OracleRun:
-    """The full state of a workload on the CPU, advanced step by step by the oracle."""
+    """The full state of a workload on the CPU, advanced step by step by the oracle.
 
-    def __init__(self, wl: hs_gen.Workload):
+    With ``requests`` only those requests are simulated (request-layers are
+    independent, so a subset resolves exactly as it does inside the batch):
+    their pages are written to a full-size pool (the rest stays zero), and the
+    tables, state, top-K lists and offload pairs are cut to the subset.
+    """
+
+    def __init__(self, wl: hs_gen.Workload, requests=None):
         self.wl = wl
+        self.req = np.arange(wl.R) if requests is None else np.asarray(requests, dtype=np.int64)
+        R = self.req.size
         self.pool = np.zeros((wl.L, wl.pool_rows, ROW), dtype=np.uint8)
         self.host = np.zeros((wl.L, wl.host_rows, ROW), dtype=np.uint8)
-        wl.fill_device_pool(torch.from_numpy(self.pool))
+        wl.fill_device_pool(torch.from_numpy(self.pool),
+                            requests=None if requests is None else self.req)
         wl.fill_host_pool(torch.from_numpy(self.host))
-        self.bt = wl.block_table.copy()
-        self.hbt = wl.host_block_table.copy()
-        self.hot = wl.hot_blocks.copy()
-        self.ctx = wl.ctx0.copy()
-        self.tok = np.full((wl.R, wl.L, wl.C), -1, dtype=np.int32)
-        self.stp = np.zeros((wl.R, wl.L, wl.C), dtype=np.uint32)
+        self.bt = np.ascontiguousarray(wl.block_table[self.req])
+        self.hbt = np.ascontiguousarray(wl.host_block_table[self.req])
+        self.hot = np.ascontiguousarray(wl.hot_blocks[self.req])
+        self.ctx = np.ascontiguousarray(wl.ctx0[self.req])
+        self.tok = np.full((R, wl.L, wl.C), -1, dtype=np.int32)
+        self.stp = np.zeros((R, wl.L, wl.C), dtype=np.uint32)
+        blocks = wl.dev_pages[np.isin(wl.dev_pages[:, 0], self.req), 2]
+        self.own_blocks = set(blocks.tolist())
+        self.pos = {int(r): i for i, r in enumerate(self.req)}
+
+    def _rows_of(self, arr):
+        keep = np.isin(arr[:, 0], self.req)
+        a = arr[keep].copy()
+        a[:, 0] = [self.pos[int(r)] for r in a[:, 0]]
+        return a
 
     def pre(self, step: hs_gen.Step) -> None:
-        for r, p, v in step.hbt_set:
+        for r, p, v in self._rows_of(step.hbt_set):
             self.hbt[r, p] = v
-        for r, p, v in step.bt_set:
+        for r, p, v in self._rows_of(step.bt_set):
             self.bt[r, p] = v
-        self.ctx = step.ctx.copy()
+        self.ctx = np.ascontiguousarray(step.ctx[self.req])
 
     def resolve(self, step: hs_gen.Step, gather: bool = True, topk=None, stamp=None):
-        topk = step.topk if topk is None else topk
+        topk = step.topk[self.req] if topk is None else topk
         stamp = step.stamp if stamp is None else stamp
         return oracle.resolve(self.pool, self.host, self.bt, self.hbt, self.ctx, self.hot,
                               self.tok, self.stp, np.ascontiguousarray(topk), stamp, gather)
 
+    def pairs(self, step: hs_gen.Step) -> np.ndarray:
+        keep = [i for i, (db, _) in enumerate(step.offload) if int(db) in self.own_blocks]
+        return np.ascontiguousarray(step.offload[keep]).reshape(-1, 2)
+
     def post(self, step: hs_gen.Step) -> None:
-        if step.offload.shape[0]:
-            oracle.offload(self.pool, self.host, step.offload)
+        pr = self.pairs(step)
+        if pr.shape[0]:
+            oracle.offload(self.pool, self.host, pr)
 
 
-def expected_content(wl: hs_gen.Workload, topk: np.ndarray, rows: np.ndarray) -> np.ndarray:
+def expected_content(wl: hs_gen.Workload, topk: np.ndarray, rows: np.ndarray,
+                     requests=None) -> np.ndarray:
     """What every gathered row must hold, from the token alone: its synthetic
     content where a row was resolved (row id >= 0), zeros elsewhere."""
     R, L = topk.shape[:2]
     t = topk.reshape(R, L, -1).astype(np.int64)
     lay = np.broadcast_to(np.arange(L)[None, :, None], t.shape)
-    src = np.broadcast_to(wl.src[:, None, None], t.shape)
+    srcs = wl.src if requests is None else wl.src[np.asarray(requests)]
+    src = np.broadcast_to(srcs[:, None, None], t.shape)
     exp = hs_gen.content_np(lay.ravel(), src.ravel(), t.ravel()).reshape(t.shape + (ROW,))
     ok = rows.reshape(R, L, -1) >= 0
     exp[~ok] = 0

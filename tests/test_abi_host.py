@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/hisparse.h declares, and rejects bad arguments with the
+documented status codes before touching the GPU."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import serving_memory_tier_amd as hs
+from serving_memory_tier_amd._lib import HsBatch, HsLayout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hs.LIB_PATH):
+        from serving_memory_tier_amd import build
+        build.build()
+    return hs.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "hisparse.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:hs_status|const char\*)\s+(hs_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(hs.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert hs.hs_status_string(0) == "ok"
+    assert "invalid" in hs.hs_status_string(1)
+    assert "unsupported" in hs.hs_status_string(2)
+    assert "launch" in hs.hs_status_string(3)
+    assert "unknown" in hs.hs_status_string(99)
+
+
+def _layout(**kw):
+    d = dict(page_size=64, row_bytes=656, num_layers=1, hot_capacity=4096, pool_rows=64 * 100,
+             host_rows=64 * 100)
+    d.update(kw)
+    lay = HsLayout(d["page_size"], d["row_bytes"], d["num_layers"], d["hot_capacity"],
+                   d["pool_rows"], d["host_rows"], d["pool_rows"] * d["row_bytes"],
+                   d["host_rows"] * d["row_bytes"])
+    for k in ("pool_layer_stride", "host_layer_stride"):
+        if k in kw:
+            setattr(lay, k, kw[k])
+    return lay
+
+
+def _batch(R=2):
+    fake = 0x1000  # never dereferenced: every call below fails validation first
+    return HsBatch(R, 16, fake, fake, fake, fake, fake, fake, fake, fake)
+
+
+def _resolve(lib, lay, bat, topk=0x1000, K=2048, stamp=1, rows=0x1000, stats=0x1000):
+    return lib.hs_resolve(ctypes.byref(lay) if lay is not None else None,
+                          ctypes.byref(bat) if bat is not None else None, topk, K,
+                          ctypes.c_uint32(stamp), rows, None, stats, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page_size=48), 1), (dict(page_size=0), 1), (dict(page_size=8192), 1),
+    (dict(row_bytes=650), 1), (dict(row_bytes=0), 1), (dict(num_layers=0), 1),
+    (dict(hot_capacity=100), 1), (dict(hot_capacity=0), 1), (dict(hot_capacity=16384), 2),
+    (dict(pool_rows=0), 1), (dict(pool_rows=100), 1), (dict(host_rows=-64), 1),
+    (dict(pool_rows=1 << 31), 1),
+    (dict(num_layers=2, pool_layer_stride=10), 1),
+])
+def test_resolve_rejects_bad_layout(lib, kw, code):
+    assert _resolve(lib, _layout(**kw), _batch()) == code
+
+
+def test_resolve_rejects_bad_call(lib):
+    lay = _layout()
+    assert _resolve(lib, None, _batch()) == 1
+    assert _resolve(lib, lay, None) == 1
+    assert _resolve(lib, lay, _batch(), topk=None) == 1
+    assert _resolve(lib, lay, _batch(), rows=None) == 1
+    assert _resolve(lib, lay, _batch(), stats=None) == 1
+    assert _resolve(lib, lay, _batch(), stamp=0) == 1
+    assert _resolve(lib, lay, _batch(), K=0) == 1
+    assert _resolve(lib, lay, _batch(), K=8193) == 2
+    bad = _batch()
+    bad.kv_pool = None
+    assert _resolve(lib, lay, bad) == 1
+    bad = _batch()
+    bad.max_pages = 0
+    assert _resolve(lib, lay, bad) == 1
+    bad = _batch(R=-1)
+    assert _resolve(lib, lay, bad) == 1
+
+
+def test_plan_rejects_bad_call(lib):
+    lay, bat = _layout(), _batch()
+    f = lambda P, K, pairs, n: lib.hs_plan_replay(ctypes.byref(lay), ctypes.byref(bat), 0x1000,
+                                                  P, K, ctypes.c_uint32(1), 0x1000, None, 0x1000,
+                                                  pairs, n, None)
+    assert f(0, 2048, None, 0) == 1
+    assert f(5, 2048, None, 0) == 2      # 10240 entries > 8192
+    assert f(4, 2048, None, -1) == 1
+    assert f(4, 2048, None, 3) == 1      # pairs missing
+
+
+def test_gather_and_offload_reject(lib):
+    lay = _layout()
+    g = lambda pool, rows, R, n, out: lib.hs_gather(ctypes.byref(lay), pool, rows, R, n, out, None)
+    assert g(None, 0x1000, 1, 10, 0x1000) == 1
+    assert g(0x1000, None, 1, 10, 0x1000) == 1
+    assert g(0x1000, 0x1000, 1, 10, None) == 1
+    assert g(0x1000, 0x1000, -1, 10, 0x1000) == 1
+    assert g(0x1000, 0x1000, 1, 200_000_000, 0x1000) == 2  # pieces per request-layer >= 2^32
+    assert g(0x1000, 0x1000, 0, 10, 0x1000) == 0            # nothing to do
+    o = lambda pool, host, pairs, n: lib.hs_offload_prefix_pages(ctypes.byref(lay), pool, host,
+                                                                pairs, n, None)
+    assert o(0x1000, 0x1000, 0x1000, -1) == 1
+    assert o(None, 0x1000, 0x1000, 1) == 1
+    assert o(0x1000, None, 0x1000, 1) == 1
+    assert o(0x1000, 0x1000, None, 1) == 1
+    assert o(0x1000, 0x1000, None, 0) == 0                  # nothing to do
+
+
+def test_host_alloc_rejects(lib):
+    p = ctypes.c_void_p()
+    assert lib.hs_host_alloc(0, ctypes.byref(p)) == 1
+    assert lib.hs_host_alloc(64, None) == 1
+    assert lib.hs_host_free(None) == 0
+    assert lib.hs_host_device_pointer(None, ctypes.byref(p)) == 1

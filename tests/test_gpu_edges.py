@@ -1,0 +1,295 @@
+"""GPU parity on hand-made and randomised edge cases, through the C ABI.
+
+Covers what the synthetic workloads do not: the hand-worked example (4-token
+pages, 8 slots), padding, duplicates, out-of-range tokens, null pages without
+host copies, table entries pointing outside the pools, unusable hot blocks,
+non-monotone stamps, ragged and maximal list sizes, maximal hot capacity,
+other page sizes and row sizes, an empty batch, and the gather and offload
+entry points on their own.
+"""
+
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from harness import run_tiny, tiny_instance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import serving_memory_tier_amd as hs
+    if not os.path.exists(hs.LIB_PATH):
+        from serving_memory_tier_amd import build
+        build.build()
+    assert torch.cuda.is_available()
+    hs.lib()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+class GpuCase:
+    """One batch in device memory, built from the same numpy arrays the oracle gets."""
+
+    def __init__(self, page, pool, host, bt, hbt, ctx, hot, tok, stp, C):
+        import serving_memory_tier_amd as hs
+        self.hs = hs
+        L, pool_rows, rb = pool.shape
+        host_rows = host.shape[1]
+        self.page, self.rb, self.L, self.C = page, rb, L, C
+        self.pool = torch.from_numpy(pool).cuda()
+        self.host_pool = hs.HostPool(max(1, host.size))
+        self.host = self.host_pool.tensor[:host.size].view(host.shape)
+        self.host.copy_(torch.from_numpy(host))
+        self.bt = torch.from_numpy(bt).cuda()
+        self.hbt = torch.from_numpy(hbt).cuda()
+        self.ctx = torch.from_numpy(ctx).cuda()
+        self.hot = torch.from_numpy(hot).cuda()
+        self.tok = torch.from_numpy(tok).cuda()
+        self.stp = torch.from_numpy(stp.view(np.int32)).cuda()
+        self.layout = hs.layout_of(page, rb, L, C, pool_rows, host_rows)
+        self.batch = hs.batch_of(bt.shape[0], bt.shape[1], self.pool, self.host_pool, self.bt,
+                                 self.hbt, self.ctx, self.hot, self.tok, self.stp)
+
+    def resolve(self, topk: np.ndarray, stamp: int, gather=True, pairs=None):
+        R, L = topk.shape[:2]
+        P, K = (1, topk.shape[2]) if topk.ndim == 3 else topk.shape[2:]
+        t = torch.from_numpy(np.ascontiguousarray(topk)).cuda()
+        rows = torch.empty(topk.shape, dtype=torch.int32, device="cuda")
+        stats = torch.empty((R, L, 8), dtype=torch.int32, device="cuda")
+        out = (torch.empty(topk.shape + (self.rb,), dtype=torch.uint8, device="cuda")
+               if gather else None)
+        pr = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda() \
+            if pairs is not None else None
+        if topk.ndim == 3 and pairs is None:
+            self.hs.hs_resolve(self.layout, self.batch, t, K, stamp, rows, out, stats)
+        else:
+            self.hs.hs_plan_replay(self.layout, self.batch, t, P, K, stamp, rows, out, stats,
+                                   pr, 0 if pairs is None else len(pairs))
+        torch.cuda.synchronize()
+        return (rows.cpu().numpy(), stats.cpu().numpy(),
+                None if out is None else out.cpu().numpy())
+
+    def state(self):
+        return (self.tok.cpu().numpy(), self.stp.cpu().numpy().view(np.uint32),
+                self.pool.cpu().numpy(), self.host.numpy().copy())
+
+    def close(self):
+        self.host = None
+        self.host_pool.close()
+
+
+def _compare(case, inst_or_arrays, topk, stamp, pairs=None, page=None):
+    a = inst_or_arrays
+    g_rows, g_stats, g_out = case.resolve(topk, stamp, pairs=pairs)
+    o_rows, o_stats, o_out = oracle.resolve(a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"],
+                                            a["hot"], a["tok"], a["stp"],
+                                            np.ascontiguousarray(topk), stamp, True,
+                                            page=case.page)
+    if pairs is not None and len(pairs):
+        oracle.offload(a["pool"], a["host"], np.asarray(pairs, np.int32), page=case.page)
+    tok, stp, pool, host = case.state()
+    assert np.array_equal(g_rows, o_rows)
+    assert np.array_equal(g_stats, o_stats)
+    assert np.array_equal(g_out, o_out)
+    assert np.array_equal(tok, a["tok"])
+    assert np.array_equal(stp, a["stp"])
+    assert np.array_equal(pool, a["pool"])
+    assert np.array_equal(host, a["host"])
+    return o_rows, o_stats
+
+
+def _case_from_tiny(inst):
+    return GpuCase(inst["page"], inst["pool"], inst["host"], inst["bt"], inst["hbt"],
+                   inst["ctx"], inst["hot"], inst["tok"].copy(), inst["stp"].copy(),
+                   inst["tok"].shape[2])
+
+
+def test_worked_example_on_gpu():
+    inst = tiny_instance()
+    case = _case_from_tiny(inst)
+    try:
+        lists = [[21, 5, 13, 2, 17, 9], [9, 1, 22, 13, 6, 14]]
+        rows, _ = _compare(case, inst, np.array([[lists[0]]], np.int32), 1)
+        assert rows.ravel().tolist() == [9, 37, 39, 36, 29, 38]
+        rows, _ = _compare(case, inst, np.array([[lists[1]]], np.int32), 2)
+        assert rows.ravel().tolist() == [38, 24, 10, 39, 25, 26]
+        inst["bt"][0, 4] = -1
+        case.bt[0, 4] = -1
+        rows, _ = _compare(case, inst, np.array([[[17, 2, 10, 6, 20, 3]]], np.int32), 3)
+        assert rows.ravel().tolist() == [38, 36, 37, 25, 8, 27]
+        rows, stats = _compare(case, inst, np.array([[[17, 2, 10, 6, 20, 3]]], np.int32), 4)
+        assert stats.ravel()[:3].tolist() == [1, 5, 0]
+    finally:
+        case.close()
+
+
+def test_worked_example_plan_and_overflow_on_gpu():
+    inst = tiny_instance(C=4, hot_blocks=(9,))
+    case = _case_from_tiny(inst)
+    try:
+        _compare(case, inst, np.array([[[21, 5, 13, 2, 17, 9]]], np.int32), 1)
+        rows, stats = _compare(case, inst, np.array([[[[9, 1, 22], [13, 6, 14]]]], np.int32), 2)
+        assert rows.tolist() == [[[[38, 36, 10], [39, 37, -2]]]]
+        assert stats.ravel().tolist() == [1, 2, 2, 1, 0, 0, 0, 0]
+    finally:
+        case.close()
+
+
+def random_arrays(rs: np.random.Generator, R, L, C, page, rb, n_pages, n_blocks, n_host,
+                  hostile=False):
+    """A random batch.  Hot blocks of different requests are disjoint (a
+    caller precondition); with ``hostile`` the tables also point outside the
+    pools, some hot blocks are unusable and stamps are non-monotone."""
+    pool = rs.integers(0, 256, size=(L, n_blocks * page, rb), dtype=np.uint8)
+    host = rs.integers(0, 256, size=(L, n_host * page, rb), dtype=np.uint8)
+    hb_per = C // page
+    perm = rs.permutation(n_blocks)
+    hot = perm[:R * hb_per].reshape(R, hb_per).astype(np.int32)
+    rest = perm[R * hb_per:]
+    bt = np.where(rs.random((R, n_pages)) < 0.5, -1,
+                  rs.choice(rest, size=(R, n_pages))).astype(np.int32)
+    hbt = np.where(rs.random((R, n_pages)) < 0.1, -1,
+                   rs.integers(0, n_host, size=(R, n_pages))).astype(np.int32)
+    ctx = rs.integers(page, n_pages * page + 1, size=R).astype(np.int32)
+    if hostile:
+        bt[rs.random((R, n_pages)) < 0.05] = n_blocks + 3
+        bt[rs.random((R, n_pages)) < 0.05] = -7
+        hbt[rs.random((R, n_pages)) < 0.05] = n_host + 1
+        hot[rs.random(hot.shape) < 0.1] = n_blocks + 5
+        ctx[0] = n_pages * page + 50  # context longer than the table
+    tok = np.full((R, L, C), -1, np.int32)
+    stp = np.zeros((R, L, C), np.uint32)
+    for r in range(R):
+        for layer in range(L):
+            k = rs.integers(0, C + 1)
+            q = rs.choice(C, size=k, replace=False)
+            tok[r, layer, q] = rs.choice(n_pages * page, size=k, replace=False)
+            stp[r, layer, q] = rs.integers(1, 9, size=k)
+            if hostile:
+                stp[r, layer, rs.choice(C, size=C // 8, replace=False)] = \
+                    rs.integers(1, 1 << 32, size=C // 8, dtype=np.uint64).astype(np.uint32)
+    return dict(pool=pool, host=host, bt=bt, hbt=hbt, ctx=ctx, hot=hot, tok=tok, stp=stp)
+
+
+def random_lists(rs, R, L, P, K, ctx, dup=0.1, pad=0.05, bad=0.03):
+    out = np.empty((R, L, P, K), np.int32)
+    for r in range(R):
+        c = int(ctx[r])
+        for layer in range(L):
+            for p in range(P):
+                v = rs.integers(0, c, size=K)
+                d = rs.random(K) < dup
+                v[d] = rs.choice(v, size=int(d.sum()))
+                v[rs.random(K) < pad] = -1
+                b = rs.random(K) < bad
+                v[b] = rs.choice([-5, c, c + 7, 1 << 30], size=int(b.sum()))
+                out[r, layer, p] = v
+    return out
+
+
+CASES = [
+    # name, R, L, P, K, C, page, rb, n_pages, hostile
+    ("ragged_k", 3, 2, 1, 1000, 2048, 64, 656, 200, False),
+    ("k1", 4, 1, 1, 1, 64, 64, 656, 30, False),
+    ("max_entries", 2, 1, 4, 2048, 8192, 64, 656, 400, False),
+    ("max_capacity", 2, 1, 1, 2048, 8192, 64, 656, 300, False),
+    ("min_capacity", 5, 1, 1, 300, 64, 64, 656, 40, False),
+    ("page16", 3, 2, 2, 700, 1024, 16, 656, 900, False),
+    ("page128_rb64", 3, 1, 1, 1500, 2048, 128, 64, 80, False),
+    ("rb1024", 2, 3, 1, 513, 512, 64, 1024, 50, False),
+    ("hostile", 4, 2, 3, 600, 2048, 64, 656, 100, True),
+    ("hostile_small", 6, 1, 1, 37, 128, 32, 656, 12, True),
+]
+
+
+@pytest.mark.parametrize("name,R,L,P,K,C,page,rb,n_pages,hostile", CASES,
+                         ids=[c[0] for c in CASES])
+def test_random_cases(name, R, L, P, K, C, page, rb, n_pages, hostile):
+    rs = np.random.default_rng(abs(hash(name)) % (1 << 31))
+    n_blocks = R * (C // page) + n_pages * R // 2 + 8
+    a = random_arrays(rs, R, L, C, page, rb, n_pages, n_blocks, n_pages, hostile)
+    case = GpuCase(page, a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"], a["hot"],
+                   a["tok"].copy(), a["stp"].copy(), C)
+    try:
+        for step in range(4):
+            _say(f"[edges] {name} step {step}")
+            lists = random_lists(rs, R, L, P, K, a["ctx"])
+            topk = lists[:, :, 0] if P == 1 else lists
+            pairs = None
+            if step == 2:
+                n = 5
+                pairs = np.stack([rs.integers(0, n_blocks, n), rs.choice(n_pages, n, replace=False)], 1)
+                if hostile:
+                    pairs[0, 0] = n_blocks + 1
+                    pairs[1, 1] = -2
+            _compare(case, a, topk, 10 + 3 * step - (step == 3) * 7, pairs=pairs)
+    finally:
+        case.close()
+
+
+def test_empty_batch_and_zero_pairs():
+    import serving_memory_tier_amd as hs
+    a = random_arrays(np.random.default_rng(1), 1, 1, 64, 64, 656, 4, 8, 4)
+    case = GpuCase(64, a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"], a["hot"],
+                   a["tok"].copy(), a["stp"].copy(), 64)
+    try:
+        empty = hs.batch_of(0, 4, case.pool, case.host_pool, case.bt, case.hbt, case.ctx,
+                            case.hot, case.tok, case.stp)
+        t = torch.zeros((8,), dtype=torch.int32, device="cuda")
+        hs.hs_resolve(case.layout, empty, t, 16, 1, t, None, t)
+        hs.hs_offload_prefix_pages(case.layout, case.pool, case.host_pool, t, 0)
+        hs.hs_gather(case.layout, case.pool, t, 0, 16, t)
+        torch.cuda.synchronize()
+    finally:
+        case.close()
+
+
+@pytest.mark.parametrize("rb", [656, 64, 1024])
+def test_gather_entry_point(rb):
+    import serving_memory_tier_amd as hs
+    rs = np.random.default_rng(rb)
+    L, rows_per_layer = 3, 64 * 50
+    pool = rs.integers(0, 256, size=(L, rows_per_layer, rb), dtype=np.uint8)
+    rows = rs.integers(-4, rows_per_layer + 9, size=(5, L, 1333)).astype(np.int32)
+    rows[0, 0, :7] = [-1, -2, -3, rows_per_layer, rows_per_layer - 1, 0, 2 ** 31 - 1]
+    lay = hs.layout_of(64, rb, L, 64, rows_per_layer, 0)
+    gp = torch.from_numpy(pool).cuda()
+    gr = torch.from_numpy(rows).cuda()
+    out = torch.empty((5, L, 1333, rb), dtype=torch.uint8, device="cuda")
+    hs.hs_gather(lay, gp, gr, 5, 1333, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.gather(pool, rows))
+
+
+def test_offload_entry_point():
+    import serving_memory_tier_amd as hs
+    rs = np.random.default_rng(9)
+    L, nb, nh = 4, 40, 30
+    pool = rs.integers(0, 256, size=(L, nb * 64, 656), dtype=np.uint8)
+    host = rs.integers(0, 256, size=(L, nh * 64, 656), dtype=np.uint8)
+    pairs = np.stack([rs.integers(0, nb, 12), rs.choice(nh, 12, replace=False)], 1).astype(np.int32)
+    pairs[3] = [nb, 2]
+    pairs[4] = [1, -1]
+    lay = hs.layout_of(64, 656, L, 64, nb * 64, nh * 64)
+    gp = torch.from_numpy(pool).cuda()
+    hp = hs.HostPool(host.size)
+    try:
+        hv = hp.tensor.view(host.shape)
+        hv.copy_(torch.from_numpy(host))
+        hs.hs_offload_prefix_pages(lay, gp, hp, torch.from_numpy(pairs).cuda(), 12)
+        torch.cuda.synchronize()
+        oracle.offload(pool, host, pairs)
+        assert np.array_equal(hv.numpy(), host)
+        assert np.array_equal(gp.cpu().numpy(), pool)
+    finally:
+        hv = None
+        hp.close()

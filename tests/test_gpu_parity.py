@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, bit-exact.
+
+Every comparison is element by element on the same seeded inputs: row ids,
+stats, hot-buffer tokens and stamps, every byte of the hot-slot rows, every
+gathered byte, and the host pool after each prefix offload.  The five
+workloads run at their full sizes; the two largest (64 x 16 request-layers,
+128 requests x 4 positions) are checked on a sample of requests the oracle
+simulates exactly (request-layers are independent).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import hs_gen
+from harness import OracleRun, expected_content
+
+pytestmark = pytest.mark.gpu
+
+ROW = hs_gen.ROW_BYTES
+PAGE = hs_gen.PAGE
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import serving_memory_tier_amd as hs
+    import os
+    if not os.path.exists(hs.LIB_PATH):
+        from serving_memory_tier_amd import build
+        build.build()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    hs.lib()
+
+
+def _hot_rows(hot_blocks: np.ndarray) -> np.ndarray:
+    return (hot_blocks.reshape(-1)[:, None] * PAGE + np.arange(PAGE)[None, :]).ravel()
+
+
+def _say(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def run_parity(wl, requests=None, n_steps=None, hit_replay=False, fused_plan=False,
+               check_content=True):
+    from serving_memory_tier_amd.runner import DeviceRun
+
+    dev = DeviceRun(wl)
+    dev.upload_steps()
+    ora = OracleRun(wl, requests)
+    req = torch.from_numpy(ora.req).cuda()
+    hot_rows = torch.from_numpy(_hot_rows(ora.hot)).cuda()
+    steps = wl.steps if n_steps is None else wl.steps[:n_steps]
+    totals = np.zeros(8, dtype=np.int64)
+    try:
+        for i, step in enumerate(steps):
+            _say(f"[parity] {wl.name} step {i} stamp {step.stamp}")
+            dev.pre(i)
+            ora.pre(step)
+            if fused_plan:
+                dev.plan_step(i)
+            else:
+                dev.resolve(i)
+            torch.cuda.synchronize()
+            rows, stats, out = ora.resolve(step)
+            totals += stats.sum(axis=(0, 1))
+            assert np.array_equal(dev.rows[req].cpu().numpy(), rows), f"row ids, step {i}"
+            assert np.array_equal(dev.stats[req].cpu().numpy(), stats), f"stats, step {i}"
+            assert np.array_equal(dev.tok[req].cpu().numpy(), ora.tok), f"slot tokens, step {i}"
+            assert np.array_equal(dev.stp[req].cpu().numpy().view(np.uint32), ora.stp), \
+                f"slot stamps, step {i}"
+            g_out = dev.out[req].cpu().numpy()
+            assert np.array_equal(g_out, out), f"gathered rows, step {i}"
+            if check_content:
+                assert np.array_equal(g_out, expected_content(wl, step.topk[ora.req], rows,
+                                                              ora.req)), f"content, step {i}"
+            assert np.array_equal(dev.pool[:, hot_rows].cpu().numpy(),
+                                  ora.pool[:, hot_rows.cpu().numpy()]), f"hot rows, step {i}"
+            if hit_replay:
+                # the same lists with the same stamp: every non-resident token
+                # is now a hit, nothing is copied, the state does not move
+                tok0, stp0 = dev.tok.clone(), dev.stp.clone()
+                dev.resolve(i)
+                torch.cuda.synchronize()
+                rows2, stats2, out2 = ora.resolve(step)
+                assert np.array_equal(dev.rows[req].cpu().numpy(), rows2)
+                assert np.array_equal(dev.stats[req].cpu().numpy(), stats2)
+                assert np.array_equal(dev.out[req].cpu().numpy(), out2)
+                assert int(stats2[..., 2].sum()) == 0
+                assert torch.equal(tok0, dev.tok) and torch.equal(stp0, dev.stp)
+            if not fused_plan:
+                dev.post(i)
+            ora.post(step)
+            pr = ora.pairs(step)
+            if pr.shape[0]:
+                torch.cuda.synchronize()
+                hb = torch.from_numpy((pr[:, 1].astype(np.int64)[:, None] * PAGE +
+                                       np.arange(PAGE)[None, :]).ravel())
+                assert np.array_equal(dev.host[:, hb].numpy(), ora.host[:, hb.numpy()]), \
+                    f"host pool after offload, step {i}"
+        torch.cuda.synchronize()
+        if requests is None:
+            assert np.array_equal(dev.pool.cpu().numpy(), ora.pool), "final pool"
+            assert np.array_equal(dev.host.numpy(), ora.host), "final host pool"
+    finally:
+        dev.close()
+    return totals
+
+
+def test_tiny():
+    totals = run_parity(hs_gen.tiny(), hit_replay=True)
+    assert totals[2] > 0 and totals[1] > 0
+
+
+def test_mixed_decode_full():
+    totals = run_parity(hs_gen.mixed_decode(), hit_replay=True)
+    _say(f"[parity] mixed_decode totals {totals.tolist()}")
+    assert totals[1] > 0 and totals[2] > 0 and totals[0] > 0
+
+
+def test_no_residency_full():
+    totals = run_parity(hs_gen.no_residency())
+    _say(f"[parity] no_residency totals {totals.tolist()}")
+    assert totals[2] >= 8 * 2048 * 0.99
+
+
+def test_mixed_state_full_sampled():
+    wl = hs_gen.mixed_state()
+    # two requests of each residency class plus the largest and smallest context
+    sample = []
+    for c in (0, 1, 2):
+        sample += list(np.nonzero(wl.classes == c)[0][:3])
+    sample += [int(np.argmax(wl.ctx0)), int(np.argmin(wl.ctx0))]
+    sample = sorted(set(int(s) for s in sample))
+    run_parity(wl, requests=sample, fused_plan=True)
+
+
+def test_multi_layer_full_sampled():
+    wl = hs_gen.multi_layer(turns=4)
+    run_parity(wl, requests=[0, 17, 63], fused_plan=False)
+
+
+def test_determinism_repeat():
+    """Two runs of the same steps give bitwise identical results."""
+    from serving_memory_tier_amd.runner import DeviceRun
+
+    wl = hs_gen.mixed_decode(R=8, steps=4)
+    res = []
+    for _ in range(2):
+        dev = DeviceRun(wl)
+        outs = []
+        for i in range(len(wl.steps)):
+            dev.pre(i)
+            dev.resolve(i)
+            outs.append((dev.rows.clone(), dev.stats.clone(), dev.out.clone()))
+        torch.cuda.synchronize()
+        res.append((outs, dev.tok.clone(), dev.stp.clone(), dev.pool.clone()))
+        dev.close()
+    for (a, b) in zip(res[0][0], res[1][0]):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+    for x, y in zip(res[0][1:], res[1][1:]):
+        assert torch.equal(x, y)
