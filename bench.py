@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the Hybrid HiSparse hot path on one MI355X.
+
+A step is one pass of the whole hot path over one decode batch of the
+mixed-residency workload (32 requests x 1 layer at a 74,160-token context,
+25 % resident tail, top-K 2048, 4096 hot rows per request, +1 token per
+step): the fused resolver (classify, hit refresh, LRU victims, one-row host
+copies of the misses, state commit), the single-stride gather of all
+65,536 rows, and -- in the steps where a page completes -- the batched
+prefix-page offload.  Inputs (top-K lists, tables, pools) are resident in
+device / pinned host memory before the timed region.
+
+Prints one JSON line: resolved top-K rows/s for the whole job, plus the
+roofline of the dominant kernel (per-launch duration from HIP events on the
+launch stream, algorithmic bytes per launch), the achieved HBM and host-link
+bandwidths, a hit-replay measurement of the HBM-bound path, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "resolved top-K rows/s + achieved HBM & host-link GB/s vs peak, 32 req x K=2048"
+HBM_PEAK_GBPS = 8000.0
+HOST_LINK_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction
+ROW = 656
+PAGE = 64
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="mixed_decode",
+                    choices=["mixed_decode", "no_residency", "mixed_state", "multi_layer"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bound on the oracle's CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hit-replays", type=int, default=50)
+    return ap.parse_args()
+
+
+def build_workload(name: str, n_steps: int):
+    import hs_gen
+    if name == "mixed_decode":
+        return hs_gen.mixed_decode(steps=n_steps)
+    if name == "no_residency":
+        return hs_gen.no_residency(steps=n_steps)
+    if name == "mixed_state":
+        return hs_gen.mixed_state(steps=n_steps)
+    return hs_gen.multi_layer(turns=n_steps)
+
+
+def resolve_hbm_bytes(wl, stats_sum, n_launches):
+    """Algorithmic HBM bytes of the resolver per launch.
+
+    Per request-layer: the slot tokens and stamps are read once (8 B/slot).
+    Per entry: the index (4 B), its block-table entry (4 B), its row id (4 B).
+    Per hit: the refreshed stamp (4 B).  Per miss: the host-table entry (4 B),
+    the 656-B row written into the hot slot and the new token and stamp (8 B).
+    """
+    R, L, N = wl.R, wl.L, wl.P * wl.K
+    hits, misses = stats_sum[1], stats_sum[2]
+    per = R * L * wl.C * 8 + R * L * N * 12
+    per += (hits * 4 + misses * (4 + ROW + 8)) / n_launches
+    return per
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(request-layers are independent, so a data-parallel run would be N copies "
+              "of this measurement).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import serving_memory_tier_amd as hs
+    from serving_memory_tier_amd.runner import DeviceRun
+
+    if not os.path.exists(hs.LIB_PATH):
+        from serving_memory_tier_amd import build
+        build.build()
+    torch.cuda.set_device(0)
+
+    W, K = args.warmup, args.steps
+    t_gen = time.time()
+    wl = build_workload(args.workload, W + K)
+    print(f"[bench] workload {wl.name}: R={wl.R} L={wl.L} P={wl.P} K={wl.K} C={wl.C} "
+          f"steps={len(wl.steps)} generated in {time.time() - t_gen:.1f}s", file=sys.stderr,
+          flush=True)
+    dev = DeviceRun(wl)
+    dev.upload_steps()
+    n_steps = len(wl.steps)
+    N = wl.P * wl.K
+    entries = wl.R * wl.L * N
+    # per-step context lengths and stats records live in device memory up front
+    ctx_all = torch.from_numpy(np.stack([s.ctx for s in wl.steps]).astype(np.int32)).cuda()
+    stats_all = torch.zeros((n_steps, wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
+    batches = [hs.batch_of(wl.R, wl.max_pages, dev.pool, dev.host_pool, dev.bt, dev.hbt,
+                           ctx_all[i], dev.hot, dev.tok, dev.stp) for i in range(n_steps)]
+    table_sets = []
+    for s in wl.steps:
+        sets = []
+        for arr, t in ((s.hbt_set, dev.hbt), (s.bt_set, dev.bt)):
+            if arr.shape[0]:
+                a = torch.from_numpy(arr).cuda()
+                sets.append((t, a[:, 0], a[:, 1], a[:, 2].to(torch.int32)))
+        table_sets.append(sets)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(i, ev=None):
+        for (t, r, p, v) in table_sets[i]:
+            t[r, p] = v
+        if ev is not None:
+            ev[0].record(stream)
+        if wl.P == 1:
+            hs.hs_resolve(dev.layout, batches[i], dev.topk[i], wl.K, wl.steps[i].stamp, dev.rows,
+                          None, stats_all[i], sp)
+        else:
+            hs.hs_plan_replay(dev.layout, batches[i], dev.topk[i], wl.P, wl.K,
+                              wl.steps[i].stamp, dev.rows, None, stats_all[i], None, 0, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        hs.hs_gather(dev.layout, dev.pool, dev.rows, wl.R, N, dev.out, sp)
+        if ev is not None:
+            ev[2].record(stream)
+        n_off = wl.steps[i].offload.shape[0]
+        if n_off:
+            hs.hs_offload_prefix_pages(dev.layout, dev.pool, dev.host_pool, dev.pairs[i], n_off,
+                                       sp)
+            if ev is not None:
+                ev[3].record(stream)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for j in range(K):
+        step(W + j, events[j])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+
+    res_ms = [events[j][0].elapsed_time(events[j][1]) for j in range(K)]
+    gat_ms = [events[j][1].elapsed_time(events[j][2]) for j in range(K)]
+    off = [(j, events[j][2].elapsed_time(events[j][3])) for j in range(K)
+           if wl.steps[W + j].offload.shape[0]]
+    st = stats_all[W:].sum(dim=(0, 1, 2)).cpu().numpy().astype(np.int64)
+    res_us = 1e3 * float(np.mean(res_ms))
+    gat_us = 1e3 * float(np.mean(gat_ms))
+    value = entries * K / wall
+
+    gat_bytes = entries * (4 + 2 * ROW)
+    res_bytes = resolve_hbm_bytes(wl, st, K)
+    host_bytes = st[2] * ROW / K
+    kernels = {
+        "resolve": {"us": round(res_us, 2), "hbm_bytes": int(res_bytes),
+                    "hbm_gbps": round(res_bytes / res_us / 1e3, 1),
+                    "host_link_bytes": int(host_bytes),
+                    "host_link_gbps": round(host_bytes / res_us / 1e3, 2)},
+        "gather": {"us": round(gat_us, 2), "hbm_bytes": int(gat_bytes),
+                   "hbm_gbps": round(gat_bytes / gat_us / 1e3, 1)},
+    }
+    if off:
+        page_layers = [wl.steps[W + j].offload.shape[0] * wl.L for j, _ in off]
+        off_us = 1e3 * float(np.mean([ms for _, ms in off]))
+        off_bytes = float(np.mean(page_layers)) * PAGE * ROW
+        kernels["offload"] = {"us": round(off_us, 2), "launches": len(off),
+                              "host_link_bytes": int(off_bytes),
+                              "host_link_gbps": round(off_bytes / off_us / 1e3, 2)}
+
+    # the hit-replay path: the last step's lists again with the same stamp --
+    # every non-resident token hits, no host traffic, HBM-bound
+    last = W + K - 1
+    rep = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.hit_replays)]
+    rep_stats = torch.zeros((wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
+    for j in range(args.hit_replays):
+        rep[j][0].record(stream)
+        if wl.P == 1:
+            hs.hs_resolve(dev.layout, batches[last], dev.topk[last], wl.K,
+                          wl.steps[last].stamp, dev.rows, None, rep_stats, sp)
+        else:
+            hs.hs_plan_replay(dev.layout, batches[last], dev.topk[last], wl.P, wl.K,
+                              wl.steps[last].stamp, dev.rows, None, rep_stats, None, 0, sp)
+        rep[j][1].record(stream)
+        hs.hs_gather(dev.layout, dev.pool, dev.rows, wl.R, N, dev.out, sp)
+        rep[j][2].record(stream)
+    torch.cuda.synchronize()
+    rs = rep_stats.sum(dim=(0, 1)).cpu().numpy()
+    rr_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in rep]))
+    rg_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in rep]))
+    rep_bytes = resolve_hbm_bytes(wl, rs, 1) + gat_bytes
+    hit_replay = {"resolve_us": round(rr_us, 2), "gather_us": round(rg_us, 2),
+                  "misses": int(rs[2]),
+                  "rows_per_s": round(entries / ((rr_us + rg_us) * 1e-6)),
+                  "hbm_gbps": round(rep_bytes / (rr_us + rg_us) / 1e3, 1),
+                  "hbm_frac": round(rep_bytes / (rr_us + rg_us) / 1e3 / HBM_PEAK_GBPS, 4)}
+
+    dominant = max(("resolve", res_us), ("gather", gat_us), key=lambda x: x[1])[0]
+    if dominant == "gather":
+        ach = gat_bytes / gat_us / 1e3
+        roofline = {"kernel": "gather", "bound": "hbm", "achieved": round(ach, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                    "traffic": None}
+    else:
+        ach = res_bytes / res_us / 1e3
+        roofline = {"kernel": "resolve", "bound": "hbm", "achieved": round(ach, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                    "traffic": None,
+                    "host_link": {"achieved": kernels["resolve"]["host_link_gbps"],
+                                  "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                                  "frac": round(kernels["resolve"]["host_link_gbps"] /
+                                                HOST_LINK_PEAK_GBPS, 4)}}
+    step_hbm = res_bytes + gat_bytes
+    line = {
+        "metric": METRIC, "value": round(value), "unit": "rows/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(1e3 * wall / K, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": wl.name, "requests": wl.R, "layers": wl.L, "positions": wl.P,
+                   "top_k": wl.K, "hot_capacity": wl.C, "context": int(wl.ctx0.max()),
+                   "row_bytes": ROW, "page_size": PAGE},
+        "hbm": {"achieved": round(step_hbm / (res_us + gat_us) / 1e3, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(step_hbm / (res_us + gat_us) / 1e3 / HBM_PEAK_GBPS, 4)},
+        "host_link": {"achieved": kernels["resolve"]["host_link_gbps"],
+                      "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                      "frac": round(kernels["resolve"]["host_link_gbps"] / HOST_LINK_PEAK_GBPS,
+                                    4)},
+        "per_step": {"hits": round(st[1] / K, 1), "misses": round(st[2] / K, 1),
+                     "resident": round(st[0] / K, 1)},
+        "kernels": kernels,
+        "hit_replay": hit_replay,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    dev.close()
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle as it stands, single-threaded, on the first steps of the same
+    workload (all requests, resolve + gather), until the time budget is used."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    pool = np.zeros((wl.L, wl.pool_rows, ROW), dtype=np.uint8)
+    host = np.zeros((wl.L, wl.host_rows, ROW), dtype=np.uint8)
+    wl.fill_device_pool(torch.from_numpy(pool))
+    wl.fill_host_pool(torch.from_numpy(host))
+    bt, hbt = wl.block_table.copy(), wl.host_block_table.copy()
+    tok = np.full((wl.R, wl.L, wl.C), -1, np.int32)
+    stp = np.zeros((wl.R, wl.L, wl.C), np.uint32)
+    done, spent = 0, 0.0
+    for s in wl.steps:
+        for r, p, v in s.hbt_set:
+            hbt[r, p] = v
+        for r, p, v in s.bt_set:
+            bt[r, p] = v
+        t = time.perf_counter()
+        oracle.resolve(pool, host, bt, hbt, s.ctx, wl.hot_blocks, tok, stp,
+                       np.ascontiguousarray(s.topk), s.stamp, True)
+        if s.offload.shape[0]:
+            oracle.offload(pool, host, s.offload)
+        spent += time.perf_counter() - t
+        done += 1
+        if spent >= budget_s:
+            break
+    rows = done * wl.R * wl.L * wl.P * wl.K
+    return {"value": round(rows / spent), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} steps of {wl.name} ({wl.R} requests x {wl.L} layers, "
+                      f"resolve + gather + offload), {spent:.1f}s single-threaded"}
+
+
+if __name__ == "__main__":
+    main()
