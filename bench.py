@@ -61,19 +61,28 @@ def build_workload(name: str, n_steps: int):
     return hs_gen.multi_layer(turns=n_steps)
 
 
-def resolve_hbm_bytes(wl, stats_sum, n_launches):
-    """Algorithmic HBM bytes of the resolver per launch.
+def decide_hbm_bytes(wl, stats_sum, n_launches):
+    """Algorithmic HBM bytes of the decision kernel per launch.
 
     Per request-layer: the slot tokens and stamps are read once (8 B/slot).
-    Per entry: the index (4 B), its block-table entry (4 B), its row id (4 B).
-    Per hit: the refreshed stamp (4 B).  Per miss: the host-table entry (4 B),
-    the 656-B row written into the hot slot and the new token and stamp (8 B).
+    Per entry: the index (4 B), its block-table entry (4 B), its row (4 B).
+    Per hit: the refreshed stamp (4 B).  Per miss: the host-table entry (4 B)
+    and the slot's new token and stamp (8 B).
     """
     R, L, N = wl.R, wl.L, wl.P * wl.K
     hits, misses = stats_sum[1], stats_sum[2]
-    per = R * L * wl.C * 8 + R * L * N * 12
-    per += (hits * 4 + misses * (4 + ROW + 8)) / n_launches
-    return per
+    return R * L * wl.C * 8 + R * L * N * 12 + (hits * 4 + misses * 12) / n_launches
+
+
+def move_hbm_bytes(wl, stats_sum, n_launches):
+    """Algorithmic HBM bytes of the row mover per launch: every entry reads its
+    row code (4 B) and writes its 656-B output row; every resident or hit entry
+    reads its 656-B row from the pool; every miss writes its row into the hot
+    slot (656 B) and its final row id (4 B) -- its read comes over the host link."""
+    R, L, N = wl.R, wl.L, wl.P * wl.K
+    entries = R * L * N
+    misses = stats_sum[2] / n_launches
+    return entries * (4 + ROW) + (entries - misses) * ROW + misses * (ROW + 4)
 
 
 def main():
@@ -127,15 +136,11 @@ def main():
             t[r, p] = v
         if ev is not None:
             ev[0].record(stream)
-        if wl.P == 1:
-            hs.hs_resolve(dev.layout, batches[i], dev.topk[i], wl.K, wl.steps[i].stamp, dev.rows,
-                          None, stats_all[i], sp)
-        else:
-            hs.hs_plan_replay(dev.layout, batches[i], dev.topk[i], wl.P, wl.K,
-                              wl.steps[i].stamp, dev.rows, None, stats_all[i], None, 0, sp)
+        hs.hs_resolve_decide(dev.layout, batches[i], dev.topk[i], wl.P, wl.K, wl.steps[i].stamp,
+                             dev.rows, stats_all[i], sp)
         if ev is not None:
             ev[1].record(stream)
-        hs.hs_gather(dev.layout, dev.pool, dev.rows, wl.R, N, dev.out, sp)
+        hs.hs_resolve_move(dev.layout, batches[i], dev.topk[i], wl.P, wl.K, dev.rows, dev.out, sp)
         if ev is not None:
             ev[2].record(stream)
         n_off = wl.steps[i].offload.shape[0]
@@ -156,25 +161,25 @@ def main():
     t1 = time.perf_counter()
     wall = t1 - t0
 
-    res_ms = [events[j][0].elapsed_time(events[j][1]) for j in range(K)]
-    gat_ms = [events[j][1].elapsed_time(events[j][2]) for j in range(K)]
+    dec_ms = [events[j][0].elapsed_time(events[j][1]) for j in range(K)]
+    mov_ms = [events[j][1].elapsed_time(events[j][2]) for j in range(K)]
     off = [(j, events[j][2].elapsed_time(events[j][3])) for j in range(K)
            if wl.steps[W + j].offload.shape[0]]
     st = stats_all[W:].sum(dim=(0, 1, 2)).cpu().numpy().astype(np.int64)
-    res_us = 1e3 * float(np.mean(res_ms))
-    gat_us = 1e3 * float(np.mean(gat_ms))
+    dec_us = 1e3 * float(np.mean(dec_ms))
+    mov_us = 1e3 * float(np.mean(mov_ms))
     value = entries * K / wall
 
-    gat_bytes = entries * (4 + 2 * ROW)
-    res_bytes = resolve_hbm_bytes(wl, st, K)
+    dec_bytes = decide_hbm_bytes(wl, st, K)
+    mov_bytes = move_hbm_bytes(wl, st, K)
     host_bytes = st[2] * ROW / K
     kernels = {
-        "resolve": {"us": round(res_us, 2), "hbm_bytes": int(res_bytes),
-                    "hbm_gbps": round(res_bytes / res_us / 1e3, 1),
-                    "host_link_bytes": int(host_bytes),
-                    "host_link_gbps": round(host_bytes / res_us / 1e3, 2)},
-        "gather": {"us": round(gat_us, 2), "hbm_bytes": int(gat_bytes),
-                   "hbm_gbps": round(gat_bytes / gat_us / 1e3, 1)},
+        "decide": {"us": round(dec_us, 2), "hbm_bytes": int(dec_bytes),
+                   "hbm_gbps": round(dec_bytes / dec_us / 1e3, 1)},
+        "move": {"us": round(mov_us, 2), "hbm_bytes": int(mov_bytes),
+                 "hbm_gbps": round(mov_bytes / mov_us / 1e3, 1),
+                 "host_link_bytes": int(host_bytes),
+                 "host_link_gbps": round(host_bytes / mov_us / 1e3, 2)},
     }
     if off:
         page_layers = [wl.steps[W + j].offload.shape[0] * wl.L for j, _ in off]
@@ -191,42 +196,46 @@ def main():
     rep_stats = torch.zeros((wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
     for j in range(args.hit_replays):
         rep[j][0].record(stream)
-        if wl.P == 1:
-            hs.hs_resolve(dev.layout, batches[last], dev.topk[last], wl.K,
-                          wl.steps[last].stamp, dev.rows, None, rep_stats, sp)
-        else:
-            hs.hs_plan_replay(dev.layout, batches[last], dev.topk[last], wl.P, wl.K,
-                              wl.steps[last].stamp, dev.rows, None, rep_stats, None, 0, sp)
+        hs.hs_resolve_decide(dev.layout, batches[last], dev.topk[last], wl.P, wl.K,
+                             wl.steps[last].stamp, dev.rows, rep_stats, sp)
         rep[j][1].record(stream)
-        hs.hs_gather(dev.layout, dev.pool, dev.rows, wl.R, N, dev.out, sp)
+        hs.hs_resolve_move(dev.layout, batches[last], dev.topk[last], wl.P, wl.K, dev.rows,
+                           dev.out, sp)
         rep[j][2].record(stream)
     torch.cuda.synchronize()
     rs = rep_stats.sum(dim=(0, 1)).cpu().numpy()
-    rr_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in rep]))
-    rg_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in rep]))
-    rep_bytes = resolve_hbm_bytes(wl, rs, 1) + gat_bytes
-    hit_replay = {"resolve_us": round(rr_us, 2), "gather_us": round(rg_us, 2),
+    rd_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in rep]))
+    rm_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in rep]))
+    rep_bytes = decide_hbm_bytes(wl, rs, 1) + move_hbm_bytes(wl, rs, 1)
+    hit_replay = {"decide_us": round(rd_us, 2), "move_us": round(rm_us, 2),
                   "misses": int(rs[2]),
-                  "rows_per_s": round(entries / ((rr_us + rg_us) * 1e-6)),
-                  "hbm_gbps": round(rep_bytes / (rr_us + rg_us) / 1e3, 1),
-                  "hbm_frac": round(rep_bytes / (rr_us + rg_us) / 1e3 / HBM_PEAK_GBPS, 4)}
+                  "rows_per_s": round(entries / ((rd_us + rm_us) * 1e-6)),
+                  "hbm_gbps": round(rep_bytes / (rd_us + rm_us) / 1e3, 1),
+                  "hbm_frac": round(rep_bytes / (rd_us + rm_us) / 1e3 / HBM_PEAK_GBPS, 4),
+                  "move_hbm_gbps": round(move_hbm_bytes(wl, rs, 1) / rm_us / 1e3, 1)}
 
-    dominant = max(("resolve", res_us), ("gather", gat_us), key=lambda x: x[1])[0]
-    if dominant == "gather":
-        ach = gat_bytes / gat_us / 1e3
-        roofline = {"kernel": "gather", "bound": "hbm", "achieved": round(ach, 1),
+    # the dominant kernel of a step and the resource that bounds it: the
+    # mover is bound by the host link when it carries misses (its HBM bytes
+    # would take a fraction of the time at HBM speed), by HBM otherwise
+    if mov_us >= dec_us:
+        host_t = host_bytes / (HOST_LINK_PEAK_GBPS * 1e3)
+        hbm_t = mov_bytes / (HBM_PEAK_GBPS * 1e3)
+        if host_t >= hbm_t:
+            ach = host_bytes / mov_us / 1e3
+            roofline = {"kernel": "move", "bound": "host_link", "achieved": round(ach, 2),
+                        "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(ach / HOST_LINK_PEAK_GBPS, 4), "traffic": None}
+        else:
+            ach = mov_bytes / mov_us / 1e3
+            roofline = {"kernel": "move", "bound": "hbm", "achieved": round(ach, 1),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
+    else:
+        ach = dec_bytes / dec_us / 1e3
+        roofline = {"kernel": "decide", "bound": "hbm", "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                     "traffic": None}
-    else:
-        ach = res_bytes / res_us / 1e3
-        roofline = {"kernel": "resolve", "bound": "hbm", "achieved": round(ach, 1),
-                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                    "traffic": None,
-                    "host_link": {"achieved": kernels["resolve"]["host_link_gbps"],
-                                  "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
-                                  "frac": round(kernels["resolve"]["host_link_gbps"] /
-                                                HOST_LINK_PEAK_GBPS, 4)}}
-    step_hbm = res_bytes + gat_bytes
+    step_hbm = dec_bytes + mov_bytes
     line = {
         "metric": METRIC, "value": round(value), "unit": "rows/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(1e3 * wall / K, 4), "higher_is_better": True,
@@ -234,12 +243,12 @@ def main():
         "config": {"workload": wl.name, "requests": wl.R, "layers": wl.L, "positions": wl.P,
                    "top_k": wl.K, "hot_capacity": wl.C, "context": int(wl.ctx0.max()),
                    "row_bytes": ROW, "page_size": PAGE},
-        "hbm": {"achieved": round(step_hbm / (res_us + gat_us) / 1e3, 1),
+        "hbm": {"achieved": round(step_hbm / (dec_us + mov_us) / 1e3, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(step_hbm / (res_us + gat_us) / 1e3 / HBM_PEAK_GBPS, 4)},
-        "host_link": {"achieved": kernels["resolve"]["host_link_gbps"],
+                "frac": round(step_hbm / (dec_us + mov_us) / 1e3 / HBM_PEAK_GBPS, 4)},
+        "host_link": {"achieved": round(host_bytes / (dec_us + mov_us) / 1e3, 2),
                       "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
-                      "frac": round(kernels["resolve"]["host_link_gbps"] / HOST_LINK_PEAK_GBPS,
+                      "frac": round(host_bytes / (dec_us + mov_us) / 1e3 / HOST_LINK_PEAK_GBPS,
                                     4)},
         "per_step": {"hits": round(st[1] / K, 1), "misses": round(st[2] / K, 1),
                      "resident": round(st[0] / K, 1)},

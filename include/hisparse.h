@@ -112,6 +112,9 @@ typedef struct {
  *   - all decisions read the state as it was before the call.
  * Slots whose hot block lies outside the pool are never used; block-table,
  * host-table and pair entries outside their pools are treated as absent.
+ * Precondition: a leased hot block belongs to one request only and is not
+ * also a resident block in any block table (otherwise the rows a copy writes
+ * and the rows a gather reads may overlap within one call).
  * Arguments: top_k = K (1..HS_MAX_ENTRIES); stamp > 0, normally the step
  * counter (calling again with the same inputs and the same stamp leaves the
  * state unchanged); gather_out may be NULL, otherwise it receives the rows
@@ -168,6 +171,29 @@ hs_status hs_plan_replay(const hs_layout* layout, const hs_batch* batch, const i
                          int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
                          uint8_t* gather_out, int32_t* stats, const int32_t* offload_pairs,
                          int32_t n_offload, hipStream_t stream);
+
+/*
+ * The two halves of hs_resolve / hs_plan_replay, for callers that time or
+ * schedule them separately.  hs_resolve(...) is exactly
+ *   hs_resolve_decide(layout, batch, topk, 1, top_k, stamp, row_ids, stats, s);
+ *   hs_resolve_move(layout, batch, topk, 1, top_k, row_ids, gather_out, s);
+ * and hs_plan_replay the same with num_pos positions followed by
+ * hs_offload_prefix_pages.  decide runs one workgroup per request-layer:
+ * it classifies, finds hits and victims and commits the hot-buffer state;
+ * row_ids then hold final rows except for assigned misses, which hold the
+ * code -(8 + 2 * slot + c) (c = 1 on exactly one entry per missed token).
+ * move runs on the whole chip: it copies each missed row from the host pool
+ * into its slot, gathers every row into gather_out (NULL: copies only) and
+ * replaces the codes by the slots' row ids.  Until move has run on the same
+ * stream, the hot slots of the misses do not yet hold their rows.
+ * Errors: as hs_resolve.
+ */
+hs_status hs_resolve_decide(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                            int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
+                            int32_t* stats, hipStream_t stream);
+hs_status hs_resolve_move(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                          int32_t num_pos, int32_t top_k, int32_t* row_ids, uint8_t* gather_out,
+                          hipStream_t stream);
 
 /* A static English description of a status code. */
 const char* hs_status_string(hs_status status);

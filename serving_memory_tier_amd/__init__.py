@@ -13,12 +13,13 @@ from ._lib import (EXPORTS, HS_ERR_HIP, HS_ERR_INVALID_ARGUMENT, HS_ERR_LAUNCH,
                    HsBatch, HsError, HsLayout, lib)
 from .api import (HostPool, batch_of, hs_gather, hs_host_alloc, hs_host_device_pointer,
                   hs_host_free, hs_offload_prefix_pages, hs_plan_replay, hs_resolve,
-                  hs_status_string, layout_of)
+                  hs_resolve_decide, hs_resolve_move, hs_status_string, layout_of)
 
 __all__ = [
     "EXPORTS", "HS_OK", "HS_ERR_INVALID_ARGUMENT", "HS_ERR_UNSUPPORTED", "HS_ERR_LAUNCH",
     "HS_ERR_HIP", "HS_MAX_ENTRIES", "HS_MAX_HOT_CAPACITY", "LIB_PATH", "HsLayout", "HsBatch",
     "HsError", "HostPool", "lib", "layout_of", "batch_of", "hs_resolve", "hs_gather",
-    "hs_offload_prefix_pages", "hs_plan_replay", "hs_status_string", "hs_host_alloc",
+    "hs_offload_prefix_pages", "hs_plan_replay", "hs_resolve_decide", "hs_resolve_move",
+    "hs_status_string", "hs_host_alloc",
     "hs_host_free", "hs_host_device_pointer",
 ]

@@ -78,6 +78,20 @@ def hs_plan_replay(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: 
            "hs_plan_replay")
 
 
+def hs_resolve_decide(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: int,
+                      stamp: int, row_ids, stats, stream=None) -> None:
+    _check(lib().hs_resolve_decide(ctypes.byref(layout), ctypes.byref(batch), _ptr(topk), num_pos,
+                                   top_k, ctypes.c_uint32(stamp), _ptr(row_ids), _ptr(stats),
+                                   _stream(stream)), "hs_resolve_decide")
+
+
+def hs_resolve_move(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: int, row_ids,
+                    gather_out, stream=None) -> None:
+    _check(lib().hs_resolve_move(ctypes.byref(layout), ctypes.byref(batch), _ptr(topk), num_pos,
+                                 top_k, _ptr(row_ids), _ptr(gather_out), _stream(stream)),
+           "hs_resolve_move")
+
+
 def hs_gather(layout: HsLayout, kv_pool, row_ids, num_reqs: int, rows_per_req_layer: int, out,
               stream=None) -> None:
     _check(lib().hs_gather(ctypes.byref(layout), _ptr(kv_pool), _ptr(row_ids), num_reqs,

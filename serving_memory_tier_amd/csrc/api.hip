@@ -48,11 +48,9 @@ hs_status check_hot(const hs_layout* lay) {
 hs_status from_hip(hipError_t e) { return e == hipSuccess ? HS_OK : HS_ERR_LAUNCH; }
 
 hs_status check_gather(const hs_layout* lay, int64_t n_rl, int64_t rows_per_rl) {
-  const int64_t pieces = lay->row_bytes / 16;
-  if (rows_per_rl * pieces >= (int64_t(1) << 32)) return HS_ERR_UNSUPPORTED;
-  const int64_t per = hs::kCopyThreads * hs::kCopyUnroll;
-  const int64_t blocks = n_rl * ((rows_per_rl * pieces + per - 1) / per);
-  if (blocks >= (int64_t(1) << 32)) return HS_ERR_UNSUPPORTED;
+  (void)lay;
+  const int64_t chunks = (rows_per_rl + hs::kMoveEntriesPerWave - 1) / hs::kMoveEntriesPerWave;
+  if (n_rl * chunks >= (int64_t(1) << 31)) return HS_ERR_UNSUPPORTED;
   return HS_OK;
 }
 
@@ -77,14 +75,16 @@ hs::OffloadParams offload_params(const hs_layout* lay, const uint8_t* pool, uint
   return o;
 }
 
-hs::GatherParams gather_params(const hs_layout* lay, const uint8_t* pool, const int32_t* rows,
-                               int32_t num_reqs, int32_t rows_per_rl, uint8_t* out) {
-  hs::GatherParams g;
+hs::MoveParams move_params(const hs_layout* lay, const uint8_t* pool, int32_t* rows,
+                           int32_t num_reqs, int32_t rows_per_rl, uint8_t* out) {
+  hs::MoveParams g{};
   g.pool = pool;
   g.pool_rows = lay->pool_rows;
   g.pool_stride = lay->pool_layer_stride;
   g.row_bytes = lay->row_bytes;
   g.num_layers = lay->num_layers;
+  g.page_shift = log2i(lay->page_size);
+  g.hot_capacity = lay->hot_capacity;
   g.row_ids = rows;
   g.num_reqs = num_reqs;
   g.rows_per_rl = rows_per_rl;
@@ -92,64 +92,91 @@ hs::GatherParams gather_params(const hs_layout* lay, const uint8_t* pool, const 
   return g;
 }
 
-// Shared body of hs_resolve and hs_plan_replay.
-hs_status resolve_common(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
-                         int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
-                         uint8_t* gather_out, int32_t* stats, const int32_t* offload_pairs,
-                         int32_t n_offload, hipStream_t stream) {
+// Checks shared by hs_resolve, hs_plan_replay and their two halves.
+hs_status check_resolve(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
+                        int32_t num_pos, int32_t top_k, const int32_t* row_ids) {
   hs_status s = check_layout(lay);
   if (s != HS_OK) return s;
   if ((s = check_hot(lay)) != HS_OK) return s;
-  if (!b || !topk || !row_ids || !stats) return HS_ERR_INVALID_ARGUMENT;
+  if (!b || !topk || !row_ids) return HS_ERR_INVALID_ARGUMENT;
   if (b->num_reqs < 0 || b->max_pages < 1) return HS_ERR_INVALID_ARGUMENT;
   if (num_pos < 1 || top_k < 1) return HS_ERR_INVALID_ARGUMENT;
-  if (stamp == 0) return HS_ERR_INVALID_ARGUMENT;
   if ((int64_t)num_pos * top_k > HS_MAX_ENTRIES) return HS_ERR_UNSUPPORTED;
-  if ((s = check_offload(n_offload)) != HS_OK) return s;
-  if (n_offload > 0 && !offload_pairs) return HS_ERR_INVALID_ARGUMENT;
   const int64_t n_rl = (int64_t)b->num_reqs * lay->num_layers;
   if (n_rl > INT32_MAX) return HS_ERR_UNSUPPORTED;
-  const int32_t N = num_pos * top_k;
-  if (gather_out && (s = check_gather(lay, n_rl, N)) != HS_OK) return s;
+  if ((s = check_gather(lay, n_rl, (int64_t)num_pos * top_k)) != HS_OK) return s;
   if (b->num_reqs > 0) {
     if (!b->kv_pool || !b->block_table || !b->host_block_table || !b->ctx_len ||
         !b->hot_blocks || !b->slot_token || !b->slot_stamp)
       return HS_ERR_INVALID_ARGUMENT;
     if (!b->host_pool && lay->host_rows > 0) return HS_ERR_INVALID_ARGUMENT;
   }
-  if (n_offload > 0 && (!b->kv_pool || !b->host_pool)) return HS_ERR_INVALID_ARGUMENT;
+  return HS_OK;
+}
 
-  if (n_rl > 0) {
-    hs::ResolveParams p;
-    p.page_shift = log2i(lay->page_size);
-    p.row_bytes = lay->row_bytes;
-    p.num_layers = lay->num_layers;
-    p.hot_capacity = lay->hot_capacity;
-    p.pool_rows = lay->pool_rows;
-    p.host_rows = lay->host_rows;
-    p.pool_stride = lay->pool_layer_stride;
-    p.host_stride = lay->host_layer_stride;
-    p.num_reqs = b->num_reqs;
-    p.max_pages = b->max_pages;
-    p.pool = b->kv_pool;
-    p.host = b->host_pool;
-    p.block_table = b->block_table;
-    p.host_block_table = b->host_block_table;
-    p.ctx_len = b->ctx_len;
-    p.hot_blocks = b->hot_blocks;
-    p.slot_token = b->slot_token;
-    p.slot_stamp = b->slot_stamp;
-    p.topk = topk;
-    p.entries = N;
-    p.stamp = stamp;
-    p.row_ids = row_ids;
-    p.stats = stats;
-    if ((s = from_hip(hs::launch_resolve(p, stream))) != HS_OK) return s;
-    if (gather_out) {
-      hs::GatherParams g = gather_params(lay, b->kv_pool, row_ids, b->num_reqs, N, gather_out);
-      if ((s = from_hip(hs::launch_gather(g, stream))) != HS_OK) return s;
-    }
-  }
+hs_status launch_decide(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
+                        int32_t N, uint32_t stamp, int32_t* row_ids, int32_t* stats,
+                        hipStream_t stream) {
+  if ((int64_t)b->num_reqs * lay->num_layers == 0) return HS_OK;
+  hs::ResolveParams p;
+  p.page_shift = log2i(lay->page_size);
+  p.row_bytes = lay->row_bytes;
+  p.num_layers = lay->num_layers;
+  p.hot_capacity = lay->hot_capacity;
+  p.pool_rows = lay->pool_rows;
+  p.host_rows = lay->host_rows;
+  p.pool_stride = lay->pool_layer_stride;
+  p.host_stride = lay->host_layer_stride;
+  p.num_reqs = b->num_reqs;
+  p.max_pages = b->max_pages;
+  p.pool = b->kv_pool;
+  p.host = b->host_pool;
+  p.block_table = b->block_table;
+  p.host_block_table = b->host_block_table;
+  p.ctx_len = b->ctx_len;
+  p.hot_blocks = b->hot_blocks;
+  p.slot_token = b->slot_token;
+  p.slot_stamp = b->slot_stamp;
+  p.topk = topk;
+  p.entries = N;
+  p.stamp = stamp;
+  p.row_ids = row_ids;
+  p.stats = stats;
+  return from_hip(hs::launch_resolve(p, stream));
+}
+
+hs_status launch_fused_move(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
+                            int32_t N, int32_t* row_ids, uint8_t* gather_out,
+                            hipStream_t stream) {
+  if ((int64_t)b->num_reqs * lay->num_layers == 0) return HS_OK;
+  hs::MoveParams g = move_params(lay, b->kv_pool, row_ids, b->num_reqs, N, gather_out);
+  g.pool_w = b->kv_pool;
+  g.host = b->host_pool;
+  g.host_rows = lay->host_rows;
+  g.host_stride = lay->host_layer_stride;
+  g.max_pages = b->max_pages;
+  g.topk = topk;
+  g.host_block_table = b->host_block_table;
+  g.hot_blocks = b->hot_blocks;
+  return from_hip(hs::launch_move(g, true, stream));
+}
+
+// Shared body of hs_resolve and hs_plan_replay: decisions, then the misses'
+// host-link copies and the gather on the whole chip, then the offload -- all
+// on the caller's stream.
+hs_status resolve_common(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
+                         int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
+                         uint8_t* gather_out, int32_t* stats, const int32_t* offload_pairs,
+                         int32_t n_offload, hipStream_t stream) {
+  hs_status s = check_resolve(lay, b, topk, num_pos, top_k, row_ids);
+  if (s != HS_OK) return s;
+  if (!stats || stamp == 0) return HS_ERR_INVALID_ARGUMENT;
+  if ((s = check_offload(n_offload)) != HS_OK) return s;
+  if (n_offload > 0 && (!offload_pairs || !b->kv_pool || !b->host_pool))
+    return HS_ERR_INVALID_ARGUMENT;
+  const int32_t N = num_pos * top_k;
+  if ((s = launch_decide(lay, b, topk, N, stamp, row_ids, stats, stream)) != HS_OK) return s;
+  if ((s = launch_fused_move(lay, b, topk, N, row_ids, gather_out, stream)) != HS_OK) return s;
   if (n_offload > 0) {
     hs::OffloadParams o = offload_params(lay, b->kv_pool, const_cast<uint8_t*>(b->host_pool),
                                          offload_pairs, n_offload);
@@ -177,6 +204,23 @@ hs_status hs_plan_replay(const hs_layout* layout, const hs_batch* batch, const i
                         offload_pairs, n_offload, stream);
 }
 
+hs_status hs_resolve_decide(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                            int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
+                            int32_t* stats, hipStream_t stream) {
+  hs_status s = check_resolve(layout, batch, topk, num_pos, top_k, row_ids);
+  if (s != HS_OK) return s;
+  if (!stats || stamp == 0) return HS_ERR_INVALID_ARGUMENT;
+  return launch_decide(layout, batch, topk, num_pos * top_k, stamp, row_ids, stats, stream);
+}
+
+hs_status hs_resolve_move(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                          int32_t num_pos, int32_t top_k, int32_t* row_ids, uint8_t* gather_out,
+                          hipStream_t stream) {
+  hs_status s = check_resolve(layout, batch, topk, num_pos, top_k, row_ids);
+  if (s != HS_OK) return s;
+  return launch_fused_move(layout, batch, topk, num_pos * top_k, row_ids, gather_out, stream);
+}
+
 hs_status hs_gather(const hs_layout* layout, const uint8_t* kv_pool, const int32_t* row_ids,
                     int32_t num_reqs, int32_t rows_per_req_layer, uint8_t* out,
                     hipStream_t stream) {
@@ -187,8 +231,10 @@ hs_status hs_gather(const hs_layout* layout, const uint8_t* kv_pool, const int32
   if (n_rl == 0 || rows_per_req_layer == 0) return HS_OK;
   if (!kv_pool || !row_ids || !out) return HS_ERR_INVALID_ARGUMENT;
   if ((s = check_gather(layout, n_rl, rows_per_req_layer)) != HS_OK) return s;
-  return from_hip(hs::launch_gather(
-      gather_params(layout, kv_pool, row_ids, num_reqs, rows_per_req_layer, out), stream));
+  return from_hip(hs::launch_move(
+      move_params(layout, kv_pool, const_cast<int32_t*>(row_ids), num_reqs, rows_per_req_layer,
+                  out),
+      false, stream));
 }
 
 hs_status hs_offload_prefix_pages(const hs_layout* layout, const uint8_t* kv_pool,

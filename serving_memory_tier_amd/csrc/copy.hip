@@ -1,17 +1,22 @@
-// Streaming copy kernels for gfx950: the single-stride row gather and the
-// post-forward prefix-page offload.
+// Streaming kernels for gfx950: the row mover (single-stride gather, fused
+// with the host-link copies of the resolver's misses) and the post-forward
+// prefix-page offload.
 //
 // Method: "vLLM GLM 5.3 ... Hybrid HiSparse offloading, Part 1", section
 // "How it works": the resolver hands back a row id whether the row is
-// resident or hot, and the rows are gathered at one stride; completed prefix
-// pages are copied to host while still served from the GPU, all sparse layers
-// in one launch after the forward, ordered on the model's stream.
+// resident or hot, and the rows are gathered at one stride; a miss copies
+// one row from pinned host memory into its hot slot; completed prefix pages
+// are copied to host while still served from the GPU, all sparse layers in
+// one launch after the forward, ordered on the model's stream.
 //
-// Both kernels are bound by memory bandwidth (HBM for the gather, the host
-// link for the offload), not by arithmetic, so they are written as wide,
-// coalesced 16-byte streams: consecutive lanes move consecutive 16-byte
-// pieces, each lane keeps kCopyUnroll loads in flight before storing, and
-// the grid is large enough to cover all 256 compute units several times.
+// Both kernels are bound by memory bandwidth -- HBM for the gather, the host
+// link for miss rows and offloaded pages -- not by arithmetic.  They move
+// 16-byte pieces, consecutive lanes on consecutive pieces, several loads in
+// flight per lane before any store, on grids that cover all 256 CUs many
+// times over.  In the mover each wave owns kMoveEntriesPerWave whole entries:
+// host-link reads of the misses and HBM reads of the resident and hot rows
+// are interleaved across every wave of the chip, so the two links run at the
+// same time instead of one after the other.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,41 +30,100 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kT = kCopyThreads;
 constexpr int kU = kCopyUnroll;
-constexpr int kPiecesPerBlock = kT * kU;
+constexpr int kWavesPerBlock = kT / 64;
+constexpr int kEPW = kMoveEntriesPerWave;
 
-// One workgroup moves kPiecesPerBlock consecutive 16-byte pieces of one
-// request-layer's output; blocks_per_rl workgroups cover a request-layer.
 // PIECES = row_bytes / 16 when known at compile time (0 = runtime).
-template <int PIECES>
-__global__ void __launch_bounds__(kT) gather_kernel(GatherParams p, int32_t blocks_per_rl) {
-  const int32_t rl = blockIdx.x / blocks_per_rl;
-  const int32_t bx = blockIdx.x - rl * blocks_per_rl;
-  const int32_t layer = rl % p.num_layers;
+template <int PIECES, bool FUSED>
+__global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_per_rl,
+                                                  int32_t total_chunks) {
+  const int lane = threadIdx.x & 63;
+  const int32_t c = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (c >= total_chunks) return;  // the whole wave leaves together
+  const int32_t rl = c / chunks_per_rl;
+  const int32_t e0 = (c - rl * chunks_per_rl) * kEPW;
+  const int32_t N = p.rows_per_rl;
+  const int32_t ne = min(kEPW, N - e0);
+  const int32_t r = rl / p.num_layers;
+  const int32_t layer = rl - r * p.num_layers;
   const int32_t pieces = PIECES > 0 ? PIECES : (p.row_bytes >> 4);
-  const uint32_t rl_pieces = (uint32_t)p.rows_per_rl * (uint32_t)pieces;
-  const int32_t* rows = p.row_ids + (int64_t)rl * p.rows_per_rl;
+  const int32_t npieces = ne * pieces;
+  const int ps = p.page_shift;
+  const int32_t pm = (1 << ps) - 1;
+  int32_t* rows = p.row_ids + (int64_t)rl * N + e0;
   const uint8_t* pool_l = p.pool + (int64_t)layer * p.pool_stride;
-  uint8_t* out = p.out + (int64_t)rl * p.rows_per_rl * p.row_bytes;
-  const uint32_t base = (uint32_t)bx * kPiecesPerBlock + threadIdx.x;
+  uint8_t* out = p.out ? p.out + ((int64_t)rl * N + e0) * p.row_bytes : nullptr;
 
-  u32x4 v[kU];
+  const int32_t* topk = nullptr;
+  const int32_t* hbt = nullptr;
+  const int32_t* hot = nullptr;
+  const uint8_t* host_l = nullptr;
+  uint8_t* slot_l = nullptr;
+  int64_t host_blocks = 0;
+  if (FUSED) {
+    topk = p.topk + (int64_t)rl * N + e0;
+    hbt = p.host_block_table + (int64_t)r * p.max_pages;
+    hot = p.hot_blocks + (int64_t)r * (p.hot_capacity >> ps);
+    host_l = p.host + (int64_t)layer * p.host_stride;
+    slot_l = p.pool_w + (int64_t)layer * p.pool_stride;
+    host_blocks = p.host_rows >> ps;
+  }
+
+  for (int32_t base = 0; base < npieces; base += 64 * kU) {
+    u32x4 v[kU];
+    uint8_t* slot_dst[kU];
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const uint32_t g = base + u * kT;
-    v[u] = u32x4{0u, 0u, 0u, 0u};
-    if (g < rl_pieces) {
-      const uint32_t e = g / (uint32_t)pieces;
-      const uint32_t pc = g - e * (uint32_t)pieces;
-      const int32_t row = rows[e];
-      if (row >= 0 && row < p.pool_rows)
-        v[u] = *reinterpret_cast<const u32x4*>(pool_l + (int64_t)row * p.row_bytes + pc * 16u);
+    for (int u = 0; u < kU; ++u) {
+      const int32_t g = base + u * 64 + lane;
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      slot_dst[u] = nullptr;
+      if (g < npieces) {
+        const int32_t el = g / pieces;
+        const int32_t pc = g - el * pieces;
+        const int32_t code = rows[el];
+        if (code >= 0) {
+          if (out && code < p.pool_rows)
+            v[u] = *reinterpret_cast<const u32x4*>(pool_l + (int64_t)code * p.row_bytes +
+                                                   pc * 16);
+        } else if (FUSED && code <= -8) {
+          const int32_t q = (-code - 8) >> 1;
+          const bool copier = ((-code - 8) & 1) != 0;
+          if (out || copier) {
+            const int32_t t = topk[el];
+            if (t >= 0 && (t >> ps) < p.max_pages && q < p.hot_capacity) {
+              const int32_t hb = hbt[t >> ps];
+              if (hb >= 0 && hb < host_blocks) {
+                const int64_t srow = ((int64_t)hb << ps) | (t & pm);
+                v[u] = *reinterpret_cast<const u32x4*>(host_l + srow * p.row_bytes + pc * 16);
+                const int32_t hblk = hot[q >> ps];
+                if (copier && hblk >= 0 && hblk < (p.pool_rows >> ps)) {
+                  const int64_t drow = ((int64_t)hblk << ps) | (q & pm);
+                  slot_dst[u] = slot_l + drow * p.row_bytes + pc * 16;
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t g = base + u * 64 + lane;
+      if (g < npieces) {
+        if (out)
+          __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + (int64_t)g * 16));
+        if (FUSED && slot_dst[u]) *reinterpret_cast<u32x4*>(slot_dst[u]) = v[u];
+      }
     }
   }
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const uint32_t g = base + u * kT;
-    if (g < rl_pieces)
-      __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + (uint64_t)g * 16u));
+  if (FUSED && lane < ne) {
+    // only this wave reads these entries' codes, and all its reads are done
+    const int32_t code = rows[lane];
+    if (code <= -8) {
+      const int32_t q = (-code - 8) >> 1;
+      rows[lane] = q < p.hot_capacity ? (int32_t)(((int64_t)hot[q >> ps] << ps) | (q & pm))
+                                      : -3;
+    }
   }
 }
 
@@ -73,7 +137,7 @@ __global__ void __launch_bounds__(kT) offload_kernel(OffloadParams p) {
   const uint8_t* src = p.pool + (int64_t)layer * p.pool_stride + db * p.page_bytes;
   uint8_t* dst = p.host + (int64_t)layer * p.host_stride + hb * p.page_bytes;
   const int32_t n = (int32_t)(p.page_bytes >> 4);
-  for (int32_t b = threadIdx.x; b < n; b += kPiecesPerBlock) {
+  for (int32_t b = threadIdx.x; b < n; b += kT * kU) {
     u32x4 v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -88,20 +152,29 @@ __global__ void __launch_bounds__(kT) offload_kernel(OffloadParams p) {
   }
 }
 
+template <int PIECES>
+void launch_move_pieces(const MoveParams& p, bool fused, int32_t chunks_per_rl, int32_t total,
+                        uint32_t grid, hipStream_t stream) {
+  if (fused)
+    hipLaunchKernelGGL((move_kernel<PIECES, true>), dim3(grid), dim3(kT), 0, stream, p,
+                       chunks_per_rl, total);
+  else
+    hipLaunchKernelGGL((move_kernel<PIECES, false>), dim3(grid), dim3(kT), 0, stream, p,
+                       chunks_per_rl, total);
+}
+
 }  // namespace
 
-hipError_t launch_gather(const GatherParams& p, hipStream_t stream) {
+hipError_t launch_move(const MoveParams& p, bool fused, hipStream_t stream) {
   const int64_t n_rl = (int64_t)p.num_reqs * p.num_layers;
   if (n_rl == 0 || p.rows_per_rl == 0) return hipSuccess;
-  const int64_t rl_pieces = (int64_t)p.rows_per_rl * (p.row_bytes >> 4);
-  const int64_t blocks_per_rl = (rl_pieces + kPiecesPerBlock - 1) / kPiecesPerBlock;
-  const int64_t grid = n_rl * blocks_per_rl;
+  const int32_t chunks_per_rl = (p.rows_per_rl + kEPW - 1) / kEPW;
+  const int64_t total = n_rl * chunks_per_rl;
+  const uint32_t grid = (uint32_t)((total + kWavesPerBlock - 1) / kWavesPerBlock);
   if (p.row_bytes == 656)
-    hipLaunchKernelGGL(gather_kernel<41>, dim3((uint32_t)grid), dim3(kT), 0, stream, p,
-                       (int32_t)blocks_per_rl);
+    launch_move_pieces<41>(p, fused, chunks_per_rl, (int32_t)total, grid, stream);
   else
-    hipLaunchKernelGGL(gather_kernel<0>, dim3((uint32_t)grid), dim3(kT), 0, stream, p,
-                       (int32_t)blocks_per_rl);
+    launch_move_pieces<0>(p, fused, chunks_per_rl, (int32_t)total, grid, stream);
   return hipGetLastError();
 }
 

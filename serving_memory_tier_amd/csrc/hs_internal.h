@@ -7,8 +7,9 @@
 
 namespace hs {
 
-// Threads per resolver workgroup: 16 wave64s, one workgroup per request-layer.
-constexpr int kResolveThreads = 1024;
+// Threads per resolver workgroup: 8 wave64s, one workgroup per request-layer
+// (with 256 VGPRs per lane available, every size variant runs without spills).
+constexpr int kResolveThreads = 512;
 // Threads per copy workgroup (gather / offload) and 16-byte pieces per thread
 // per iteration.
 constexpr int kCopyThreads = 256;
@@ -46,19 +47,39 @@ hipError_t launch_resolve(const ResolveParams& p, hipStream_t stream);
 // Bytes of dynamic LDS the resolver needs for N entries and C slots.
 size_t resolve_lds_bytes(int32_t entries, int32_t hot_capacity);
 
-struct GatherParams {
+// The row mover: the single-stride gather, and (fused) the host-link copies
+// of the misses the resolver assigned.  Row ids in [0, pool_rows) are
+// gathered from the pool; in fused mode a code -(8 + 2 q + c) names a miss
+// assigned to hot slot q whose row is read from the host pool (and, when
+// c = 1, also written into the slot), after which the code is replaced by
+// the slot's row id; every other row id yields a zero row.
+struct MoveParams {
   const uint8_t* pool;
+  uint8_t* pool_w;              // hot-slot writes (fused mode)
   int64_t pool_rows;
   int64_t pool_stride;
+  const uint8_t* host;          // fused mode
+  int64_t host_rows;
+  int64_t host_stride;
   int32_t row_bytes;
   int32_t num_layers;
-  const int32_t* row_ids;
+  int32_t page_shift;
+  int32_t max_pages;
+  int32_t hot_capacity;
+  const int32_t* topk;              // fused mode
+  const int32_t* host_block_table;  // fused mode
+  const int32_t* hot_blocks;        // fused mode
+  int32_t* row_ids;
   int32_t num_reqs;
   int32_t rows_per_rl;
-  uint8_t* out;
+  uint8_t* out;                 // may be null in fused mode (copies only)
 };
 
-hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
+// Entries per wave in the row mover: a wave owns whole entries, so the codes
+// it reads are rewritten only by itself.
+constexpr int kMoveEntriesPerWave = 16;
+
+hipError_t launch_move(const MoveParams& p, bool fused, hipStream_t stream);
 
 struct OffloadParams {
   const uint8_t* pool;

@@ -1,4 +1,4 @@
-// The fused top-K resolver for gfx950 (CDNA4).
+// The fused top-K resolver for gfx950 (CDNA4): the decision half.
 //
 // Method: "vLLM GLM 5.3 ... Hybrid HiSparse offloading, Part 1", section
 // "How it works" (mixed residency: one fused kernel resolves the indexer's
@@ -8,26 +8,33 @@
 // on a miss, dotted = reuse without copy); section "Integration with the rest
 // of vLLM" (a per-step replayable plan shares the request's hot state).
 //
-// One workgroup (16 wave64s) resolves one request-layer.  Everything the
-// decision needs lives in LDS:
-//   A  load the N top-K entries (one per lane per round), classify each
-//      (pad / invalid / resident / non-resident) and write the rows of every
-//      entry that does not need the hot buffer;
-//   B  bitonic-sort the non-pad tokens in LDS; the first element of each run
-//      is a distinct token; compact the distinct non-resident ones (ballot +
-//      mbcnt, order kept) into an ascending list U;
+// One workgroup (8 wave64s) decides one request-layer; the row movement --
+// the host-link copies of the misses and the gather -- is left to the wide
+// streaming kernel in copy.hip, which runs next on the same stream, so that
+// the host link and HBM are driven by the whole chip instead of one CU per
+// request-layer.  Phases:
+//   A  load the N top-K entries in sort layout, classify each (pad / invalid
+//      / resident / non-resident), write the final row of every entry that
+//      does not need the hot buffer;
+//   B  sort the non-pad tokens: a bitonic network run in registers, lane
+//      exchanges by wave shuffles, cross-wave strides through LDS (one barrier
+//      each); the first element of each run is a distinct token; the distinct
+//      non-resident ones are compacted (ballot + mbcnt, order kept) into an
+//      ascending list U;
 //   C  every slot binary-searches its token in U: a hit records the slot
 //      (the smallest slot wins if the state ever held a token twice);
 //   D  hits take the new stamp; distinct misses with a host copy are
 //      compacted in ascending token order;
-//   E  the usable non-hit slots are compacted in slot order and stably
-//      radix-sorted by stamp (one ballot split per stamp bit that varies), so
-//      they end in ascending (stamp, slot) order; the j-th miss takes the
-//      j-th slot; each assigned miss streams its one row from the host pool
-//      into its slot (16-byte loads over the host link, four in flight per
-//      lane), and the slot's token and stamp are written back;
-//   H  the non-resident entries look their token up in U and write their row.
-// No step depends on the order in which lanes or waves run: every result is
+//   E  the usable non-hit slots, in ascending (stamp, slot) order, are
+//      handed to the misses: if the least-recent stamp group is large enough
+//      it is taken in slot order, otherwise the candidates are stably
+//      radix-sorted by stamp (one ballot split per varying stamp bit); the
+//      slot's token and stamp are written back;
+//   H  every non-resident entry looks its token up in U and writes its row:
+//      a hit's hot row, or for an assigned miss the code -(8 + 2 slot + c)
+//      where c = 1 marks the single entry (the first occurrence) that will
+//      copy the row into the slot; overflow -2, invalid -3.
+// Nothing depends on the order in which lanes or waves run: every result is
 // fixed by the sort and the scans, so repeated runs are bitwise identical.
 
 #include <hip/hip_runtime.h>
@@ -35,24 +42,38 @@
 
 #include "hs_internal.h"
 
+// Phase markers for timing builds; empty in the library.
+#ifndef HS_PHASE_MARK
+#define HS_PHASE_MARK(i)
+#endif
+
 namespace hs {
 namespace {
 
 constexpr int kThreads = kResolveThreads;
 constexpr int kWaves = kThreads / 64;
-constexpr int32_t kNone = 0x7fffffff;   // "no slot yet" / sort padding
+constexpr int32_t kNone = 0x7fffffff;    // "no slot yet" / sort padding
+constexpr int32_t kNoHost = 0x7ffffffe;  // not resident, no host copy (unless it hits)
+// ures of an assigned miss: kMissBase | first_entry << 13 | slot, so that one
+// atomicMin over the token's entries marks its first occurrence
+constexpr int32_t kMissBase = 1 << 30;
+constexpr int32_t kMissInit = kMissBase | (0x1fff << 13);
+// stamp groups taken one at a time before falling back to a full radix sort
+constexpr int kMaxGroups = 16;
 constexpr int32_t kRowPad = -1;
 constexpr int32_t kRowOverflow = -2;
 constexpr int32_t kRowInvalid = -3;
 
-enum : int8_t { K_EMPTY = 0, K_PAD = 1, K_INVALID = 2, K_RESIDENT = 3, K_NONRES = 4 };
+enum : uint32_t { K_EMPTY = 0, K_PAD = 1, K_OTHER = 2, K_NONRES = 3 };
 
 // LDS carve-up (byte offsets), identical on host and device.
 struct LdsPlan {
-  int32_t sort_n;      // power of two >= N
-  uint32_t off_keys;   // int32[max(sort_n, 2 * C / 2)]: sort keys, later victim lists
-  uint32_t off_unr;    // int32[N]: ascending distinct non-resident tokens
-  uint32_t off_ures;   // int32[N]: per distinct token: slot, or a negative row code
+  int32_t sort_n;      // kThreads * ES >= N
+  uint32_t off_keys;   // int32[max(sort_n, C, N)]: sorted keys; then two uint16
+                       // victim lists of C; then first-occurrence indices
+  uint32_t off_unr;    // int32[max(N, sort_n / 2)]: distinct non-resident tokens
+  uint32_t off_ures;   // int32[max(N, sort_n / 2)]: per distinct token: slot or code
+                       // (unr and ures together are the sort's exchange buffer)
   uint32_t off_mk;     // uint16[N]: miss rank -> index into the distinct list
   uint32_t off_stp;    // uint32[C]: slot stamps
   uint32_t off_flag;   // uint8[C]: 0 free, 1 hit, 2 unusable
@@ -60,30 +81,23 @@ struct LdsPlan {
   uint32_t total;
 };
 
-constexpr int kRed = 8 * kWaves + 64;
+constexpr int kRed = 256;
 
 __host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
+__host__ __device__ inline int32_t imax(int32_t a, int32_t b) { return a > b ? a : b; }
 
-__host__ __device__ inline int32_t next_pow2(int32_t n) {
-  int32_t s = 1;
-  while (s < n) s <<= 1;
-  return s < 2 ? 2 : s;
-}
-
-__host__ __device__ inline LdsPlan make_plan(int32_t N, int32_t C) {
+__host__ __device__ inline LdsPlan make_plan(int32_t N, int32_t C, int32_t ES) {
   LdsPlan p;
-  p.sort_n = next_pow2(N);
-  uint32_t keys_bytes = (uint32_t)p.sort_n * 4u;
-  uint32_t vict_bytes = (uint32_t)C * 2u * 2u;  // two uint16 lists of C slots
-  if (vict_bytes > keys_bytes) keys_bytes = vict_bytes;
+  p.sort_n = kThreads * ES;
+  const int32_t half = imax(N, p.sort_n / 2);
   uint32_t o = 0;
-  p.off_keys = o; o = align16(o + keys_bytes);
-  p.off_unr = o;  o = align16(o + (uint32_t)N * 4u);
-  p.off_ures = o; o = align16(o + (uint32_t)N * 4u);
-  p.off_mk = o;   o = align16(o + (uint32_t)N * 2u);
-  p.off_stp = o;  o = align16(o + (uint32_t)C * 4u);
+  p.off_keys = o; o = align16(o + 4u * (uint32_t)imax(imax(p.sort_n, C), N));
+  p.off_unr = o;  o += 4u * (uint32_t)half;   // contiguous with ures (sort exchange)
+  p.off_ures = o; o = align16(o + 4u * (uint32_t)half);
+  p.off_mk = o;   o = align16(o + 2u * (uint32_t)N);
+  p.off_stp = o;  o = align16(o + 4u * (uint32_t)C);
   p.off_flag = o; o = align16(o + (uint32_t)C);
-  p.off_red = o;  o = align16(o + (uint32_t)kRed * 4u);
+  p.off_red = o;  o = align16(o + 4u * (uint32_t)kRed);
   p.total = o;
   return p;
 }
@@ -134,7 +148,115 @@ __device__ int block_compact(const bool (&pred)[E], int (&pos)[E], int* red) {
   return total;
 }
 
-// Block-wide sums of up to four counters at once.
+// block_compact plus block-wide sums of NS per-thread counters, in the same
+// two barriers (and the trailing one).
+template <int E, int NS>
+__device__ int block_compact_sum(const bool (&pred)[E], int (&pos)[E], int (&sums)[NS],
+                                 int* red) {
+  const int w = wave_id(), l = lane_id();
+  constexpr int n = E * kWaves;
+  int below[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const uint64_t b = __ballot(pred[j]);
+    below[j] = lanes_below(b);
+    if (l == 0) red[j * kWaves + w] = __popcll(b);
+  }
+#pragma unroll
+  for (int c = 0; c < NS; ++c) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) sums[c] += __shfl_xor(sums[c], d);
+    if (l == 0) red[n + 1 + c * kWaves + w] = sums[c];
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int i0 = 2 * l, i1 = 2 * l + 1;
+    const int v0 = i0 < n ? red[i0] : 0;
+    const int v1 = i1 < n ? red[i1] : 0;
+    const int s = v0 + v1;
+    int inc = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(inc, d);
+      if (l >= d) inc += t;
+    }
+    const int ex = inc - s;
+    if (i0 < n) red[i0] = ex;
+    if (i1 < n) red[i1] = ex + v0;
+    if (l == 63) red[n] = inc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < E; ++j) pos[j] = red[j * kWaves + w] + below[j];
+  const int total = red[n];
+#pragma unroll
+  for (int c = 0; c < NS; ++c) {
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) t += red[n + 1 + c * kWaves + i];
+    sums[c] = t;
+  }
+  __syncthreads();
+  return total;
+}
+
+// Block-wide (smallest value, how many hold it, sum of s): v = 0xffffffff
+// with c = 0 means "none".
+__device__ inline void block_mincount(uint32_t& v, int& c, int& s, int* red) {
+  const int w = wave_id(), l = lane_id();
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t ov = (uint32_t)__shfl_xor((int)v, d);
+    const int oc = __shfl_xor(c, d);
+    s += __shfl_xor(s, d);
+    if (ov < v) {
+      v = ov;
+      c = oc;
+    } else if (ov == v) {
+      c += oc;
+    }
+  }
+  if (l == 0) {
+    red[w] = (int)v;
+    red[kWaves + w] = c;
+    red[2 * kWaves + w] = s;
+  }
+  __syncthreads();
+  v = 0xffffffffu;
+  c = 0;
+  s = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const uint32_t ov = (uint32_t)red[i];
+    const int oc = red[kWaves + i];
+    s += red[2 * kWaves + i];
+    if (ov < v) {
+      v = ov;
+      c = oc;
+    } else if (ov == v) {
+      c += oc;
+    }
+  }
+  __syncthreads();
+}
+
+// lower_bound of E values in the ascending list a[0..n) at once: a fixed,
+// lane-uniform number of steps, so the E searches overlap their LDS latency.
+template <int E>
+__device__ inline void lower_bound_multi(const int32_t* a, int n, const int32_t (&v)[E],
+                                         int (&k)[E]) {
+  int step = 1;
+  while (step * 2 <= n) step *= 2;
+#pragma unroll
+  for (int j = 0; j < E; ++j) k[j] = 0;
+  for (; step > 0; step >>= 1) {
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if (k[j] + step <= n && a[k[j] + step - 1] < v[j]) k[j] += step;
+  }
+}
+
+// Block-wide sums of four counters at once.
 __device__ inline void block_sum4(int (&v)[4], int* red) {
   const int w = wave_id(), l = lane_id();
 #pragma unroll
@@ -176,23 +298,91 @@ __device__ inline void block_minmax(uint32_t& mn, uint32_t& mx, int* red) {
   __syncthreads();
 }
 
-// Ascending bitonic sort of S (a power of two) int32 keys in LDS.
-__device__ void bitonic_sort(int32_t* keys, int S) {
-  for (int k = 2; k <= S; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < (S >> 1); i += kThreads) {
-        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const int hi = lo + j;
-        const int32_t a = keys[lo], b = keys[hi];
-        const bool up = (lo & k) == 0;
-        if ((a > b) == up) {
-          keys[lo] = b;
-          keys[hi] = a;
-        }
+// x ^ lane distance J within a wave64, for compile-time J: DPP moves for 1, 2,
+// 4 and 8 (quad permutes, half-row mirror + quad mirror, row rotate by 8),
+// a swizzle for 16, a permute through the LDS crossbar for 32.
+template <int J>
+__device__ __forceinline__ int32_t lane_xor(int32_t v) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const int32_t m = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // half mirror
+    return __builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false);   // quad_perm [3,2,1,0]
+  } else if constexpr (J == 8) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (J == 16) {
+    return __builtin_amdgcn_ds_swizzle(v, 0x401F);                     // xor 16 in 32 lanes
+  } else {
+    return __shfl_xor(v, J);
+  }
+}
+
+// One stage (k = K, j = J) of an ascending bitonic network over kThreads * ES
+// keys held in registers: element i = wave * 64 * ES + s * 64 + lane is x[s].
+// Strides below 64 exchange with lane_xor, strides within a thread swap
+// registers, strides across waves go through LDS.  Cross-wave stages use two
+// buffers in turn, so each needs one barrier: a buffer is written again only
+// two cross-wave stages later, after every reader has passed the barrier in
+// between.  XW counts the cross-wave stages done so far.
+template <int ES, int K, int J, int XW>
+__device__ __forceinline__ void bitonic_stage(int32_t (&x)[ES], int32_t* b0, int32_t* b1,
+                                              int base, int l) {
+  constexpr int S = kThreads * ES;
+  constexpr int WSPAN = 64 * ES;
+  constexpr bool cross = J >= WSPAN;
+  if constexpr (cross) {
+    int32_t* b = (XW & 1) ? b1 : b0;
+#pragma unroll
+    for (int s = 0; s < ES; ++s) b[base + s * 64 + l] = x[s];
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < ES; ++s) {
+      const int i = base + s * 64 + l;
+      const int32_t y = b[i ^ J];
+      const bool up = (i & K) == 0;
+      const bool lower = (i & J) == 0;
+      x[s] = (lower == up) ? min(x[s], y) : max(x[s], y);
+    }
+  } else if constexpr (J >= 64) {
+    constexpr int js = J / 64;
+#pragma unroll
+    for (int s = 0; s < ES; ++s) {
+      if ((s & js) == 0) {
+        const int i = base + s * 64 + l;
+        const bool up = (i & K) == 0;
+        const int32_t a = x[s], c = x[s | js];
+        const int32_t lo = min(a, c), hi = max(a, c);
+        x[s] = up ? lo : hi;
+        x[s | js] = up ? hi : lo;
       }
-      __syncthreads();
+    }
+  } else {
+    const bool lower = (l & J) == 0;
+#pragma unroll
+    for (int s = 0; s < ES; ++s) {
+      const int i = base + s * 64 + l;
+      const bool up = (i & K) == 0;
+      const int32_t y = lane_xor<J>(x[s]);
+      x[s] = (lower == up) ? min(x[s], y) : max(x[s], y);
     }
   }
+  constexpr int XW2 = XW + (cross ? 1 : 0);
+  if constexpr (J > 1) {
+    bitonic_stage<ES, K, J / 2, XW2>(x, b0, b1, base, l);
+  } else if constexpr (K < S) {
+    bitonic_stage<ES, 2 * K, K, XW2>(x, b0, b1, base, l);
+  }
+}
+
+// Ascending sort of the kThreads * ES keys; ends with a barrier, so the buffers
+// may be reused at once.
+template <int ES>
+__device__ __forceinline__ void bitonic_sort_regs(int32_t (&x)[ES], int32_t* b0, int32_t* b1) {
+  const int l = lane_id(), w = wave_id();
+  bitonic_stage<ES, 2, 1, 0>(x, b0, b1, w * 64 * ES, l);
+  __syncthreads();
 }
 
 __device__ inline int lower_bound(const int32_t* a, int n, int32_t v) {
@@ -205,16 +395,16 @@ __device__ inline int lower_bound(const int32_t* a, int n, int32_t v) {
   return lo;
 }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 struct KernelArgs {
   ResolveParams p;
   LdsPlan plan;
 };
 
-// E = rounds of kThreads elements needed to cover max(sort_n, C).
-// PIECES = row_bytes / 16 when known at compile time, 0 for any row size.
-template <int E, int PIECES>
+// ES: sort elements per thread (kThreads * ES >= N); EC: slots per thread
+// (kThreads * EC >= C).
+// All global stores happen after the last barrier, so no barrier ever waits
+// for store acknowledgements.
+template <int ES, int EC>
 __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const ResolveParams& p = args.p;
@@ -228,12 +418,12 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   int* red = reinterpret_cast<int*>(lds + plan.off_red);
 
   const int tid = threadIdx.x;
+  const int l = lane_id(), w = wave_id();
   const int rl = blockIdx.x;
   const int r = rl / p.num_layers;
-  const int layer = rl - r * p.num_layers;
   const int ps = p.page_shift;
   const int32_t pm = (1 << ps) - 1;
-  const int N = p.entries, C = p.hot_capacity, S = plan.sort_n;
+  const int N = p.entries, C = p.hot_capacity;
   const int32_t ctx = p.ctx_len[r];
   const int32_t* bt = p.block_table + (int64_t)r * p.max_pages;
   const int32_t* hbt = p.host_block_table + (int64_t)r * p.max_pages;
@@ -244,70 +434,87 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   uint32_t* sstp = p.slot_stamp + (int64_t)rl * C;
   const int64_t pool_blocks = p.pool_rows >> ps;
   const int64_t host_blocks = p.host_rows >> ps;
+  const int sbase = w * 64 * ES + l;  // element s of this thread: sbase + 64 * s
 
-  // ---- A: load, classify, rows of entries that need no hot lookup --------
-  int32_t t[E];
-  int8_t kind[E];
-  int cnt[4] = {0, 0, 0, 0};  // pads
+  HS_PHASE_MARK(0);
+  // ---- A: load in sort layout and classify; stage the slots ------------
+  int32_t x[ES];     // sort keys
+  int32_t tv[ES];    // the entries' tokens
+  int32_t rowA[ES];  // final rows of entries that need no hot lookup
+  uint32_t kinds = 0;  // 2 bits per entry
+  int cnt[4] = {0, 0, 0, 0};
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int e = j * kThreads + tid;
-    kind[j] = K_EMPTY;
-    t[j] = kNone;
-    if (e < N) {
-      const int32_t v = topk[e];
-      t[j] = v;
-      int32_t row = 0;
-      if (v == -1) {
-        kind[j] = K_PAD;
-        row = kRowPad;
-        cnt[0] += 1;
-      } else if (v < 0 || v >= ctx || (v >> ps) >= p.max_pages) {
-        kind[j] = K_INVALID;
-        row = kRowInvalid;
-      } else {
-        const int32_t b = bt[v >> ps];
-        if (b >= 0) {
-          if (b < pool_blocks) {
-            kind[j] = K_RESIDENT;
-            row = (b << ps) | (v & pm);
-          } else {
-            kind[j] = K_INVALID;
-            row = kRowInvalid;
-          }
-        } else {
-          kind[j] = K_NONRES;
-        }
-      }
-      if (kind[j] != K_NONRES) rows[e] = row;
-    }
-    if (e < S) keys[e] = (kind[j] == K_PAD || kind[j] == K_EMPTY) ? kNone : t[j];
+  for (int s = 0; s < ES; ++s) {
+    const int i = sbase + 64 * s;
+    x[s] = kNone;
+    tv[s] = kNone;
+    rowA[s] = 0;
+    if (i < N) tv[s] = topk[i];
   }
-  // slot stamps and usability
+  int32_t btv[ES], hbv[ES];
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
+  for (int s = 0; s < ES; ++s) {
+    const int32_t v = tv[s];
+    const bool inrange = sbase + 64 * s < N && v >= 0 && v < ctx && (v >> ps) < p.max_pages;
+    // the host-table entry is fetched with the block-table entry: it warms the
+    // lines the distinct-token pass reads again
+    btv[s] = inrange ? bt[v >> ps] : -1;
+    hbv[s] = inrange ? hbt[v >> ps] : -1;
+  }
+  int32_t tokq[EC];
+#pragma unroll
+  for (int j = 0; j < EC; ++j) {
     const int q = j * kThreads + tid;
+    tokq[j] = -1;
     if (q < C) {
+      tokq[j] = stok[q];
       sst[q] = sstp[q];
       const int32_t hb = hot[q >> ps];
       sflag[q] = (hb >= 0 && hb < pool_blocks) ? 0 : 2;
     }
   }
-  block_sum4(cnt, red);  // also the barrier before the sort
+#pragma unroll
+  for (int s = 0; s < ES; ++s) {
+    const int i = sbase + 64 * s;
+    if (i >= N) continue;
+    const int32_t v = tv[s];
+    uint32_t kind = K_OTHER;
+    if (v == -1) {
+      kind = K_PAD;
+      rowA[s] = kRowPad;
+      cnt[0] += 1;
+    } else if (v < 0 || v >= ctx || (v >> ps) >= p.max_pages) {
+      rowA[s] = kRowInvalid;
+    } else if (btv[s] < 0) {
+      kind = K_NONRES;
+      cnt[1] += hbv[s] < 0 ? 1 : 0;  // keeps the warming load alive
+    } else {
+      rowA[s] = btv[s] < pool_blocks ? ((btv[s] << ps) | (v & pm)) : kRowInvalid;
+    }
+    if (kind != K_PAD) x[s] = v;
+    kinds |= kind << (2 * s);
+  }
+
+  HS_PHASE_MARK(1);
+  // ---- B: sort, distinct tokens, compact the non-resident ones ----------
+  bitonic_sort_regs<ES>(x, keys, unr);
+#pragma unroll
+  for (int s = 0; s < ES; ++s) keys[sbase + 64 * s] = x[s];
+  block_sum4(cnt, red);  // barrier: keys complete
+  HS_PHASE_MARK(2);
   const int pads = cnt[0];
   const int n_nonpad = N - pads;
 
-  // ---- B: sort, distinct tokens, compact the non-resident ones ----------
-  bitonic_sort(keys, S);
-  bool pred[E];
-  int pos[E];
-  int32_t sv[E];
-  int ucnt[4] = {0, 0, 0, 0};  // distinct, distinct resident, distinct invalid
+  bool predS[ES];
+  int posS[ES];
+  int32_t sv[ES], sinit[ES];
+  int ucnt[3] = {0, 0, 0};  // distinct, distinct resident, distinct invalid
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
+  for (int j = 0; j < ES; ++j) {
     const int i = j * kThreads + tid;
-    pred[j] = false;
+    predS[j] = false;
     sv[j] = 0;
+    sinit[j] = kNone;
     if (i < n_nonpad) {
       const int32_t v = keys[i];
       sv[j] = v;
@@ -321,167 +528,241 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
             if (b < pool_blocks) ucnt[1] += 1;
             else ucnt[2] += 1;
           } else {
-            pred[j] = true;
+            predS[j] = true;
+            const int32_t hb = hbt[v >> ps];
+            sinit[j] = (hb >= 0 && hb < host_blocks) ? kNone : kNoHost;
           }
         }
       }
     }
   }
-  const int n_u = block_compact<E>(pred, pos, red);
+  const int n_u = block_compact_sum<ES, 3>(predS, posS, ucnt, red);
 #pragma unroll
-  for (int j = 0; j < E; ++j)
-    if (pred[j]) unr[pos[j]] = sv[j];
-  for (int k = tid; k < n_u; k += kThreads) ures[k] = kNone;
-  block_sum4(ucnt, red);  // barrier: unr and ures complete
+  for (int j = 0; j < ES; ++j)
+    if (predS[j]) {
+      unr[posS[j]] = sv[j];
+      ures[posS[j]] = sinit[j];
+    }
+  __syncthreads();  // unr and ures complete
 
+  HS_PHASE_MARK(3);
   // ---- C: hot-map lookup (each slot searches its token) -----------------
+  if (n_u > 0) {
+    int kq[EC];
+    lower_bound_multi<EC>(unr, n_u, tokq, kq);
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int q = j * kThreads + tid;
-    if (q < C && sflag[q] == 0) {
-      const int32_t tk = stok[q];
-      if (tk >= 0 && n_u > 0) {
-        const int k = lower_bound(unr, n_u, tk);
-        if (k < n_u && unr[k] == tk) atomicMin(&ures[k], q);
-      }
+    for (int j = 0; j < EC; ++j) {
+      const int q = j * kThreads + tid;
+      const int32_t tk = tokq[j];
+      if (q < C && tk >= 0 && sflag[q] == 0 && kq[j] < n_u && unr[kq[j]] == tk)
+        atomicMin(&ures[kq[j]], q);
     }
   }
   __syncthreads();
 
-  // ---- D: hits refresh their stamp; misses are listed in token order ----
-  int dcnt[4] = {0, 0, 0, 0};  // hits, distinct invalid (no host copy)
+  HS_PHASE_MARK(4);
+  // ---- D: hits are marked; misses are listed in token order -------------
+  int dcnt[2] = {0, 0};  // hits, distinct invalid (no host copy)
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
+  for (int j = 0; j < ES; ++j) {
     const int k = j * kThreads + tid;
-    pred[j] = false;
+    predS[j] = false;
     if (k < n_u) {
       const int32_t q = ures[k];
-      if (q != kNone) {
+      if (q < C) {
         dcnt[0] += 1;
         sflag[q] = 1;
-        sstp[q] = p.stamp;
+      } else if (q == kNoHost) {
+        dcnt[1] += 1;
+        ures[k] = kRowInvalid;
       } else {
-        const int32_t u = unr[k];
-        const int32_t hb = hbt[u >> ps];
-        if (hb >= 0 && hb < host_blocks) {
-          pred[j] = true;
-        } else {
-          dcnt[1] += 1;
-          ures[k] = kRowInvalid;
-        }
+        predS[j] = true;
       }
     }
   }
-  const int M = block_compact<E>(pred, pos, red);
+  const int M = block_compact_sum<ES, 2>(predS, posS, dcnt, red);
 #pragma unroll
-  for (int j = 0; j < E; ++j)
-    if (pred[j]) mk[pos[j]] = (uint16_t)(j * kThreads + tid);
-  block_sum4(dcnt, red);  // barrier: mk and sflag complete
+  for (int j = 0; j < ES; ++j)
+    if (predS[j]) mk[posS[j]] = (uint16_t)(j * kThreads + tid);
 
-  // ---- E: victims in ascending (stamp, slot), assignment, copies --------
+  HS_PHASE_MARK(5);
+  // ---- E: victims in ascending (stamp, slot); assignment -----------------
   int A = 0;
+  uint16_t* vict = reinterpret_cast<uint16_t*>(keys);
   if (M > 0) {
-    uint16_t* vbuf0 = reinterpret_cast<uint16_t*>(keys);
-    uint16_t* vbuf1 = vbuf0 + C;
-    uint32_t mn = 0xffffffffu, mx = 0u;
+    bool predC[EC];
+    int posC[EC];
+    // the least-recent stamp among the usable non-hit slots, its group size,
+    // and the number of such slots; non-candidates carry stamp ~0 and are
+    // never taken (every candidate group is found before them)
+    uint32_t cst[EC];
+    uint32_t v = 0xffffffffu;
+    int c = 0, nv = 0;
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
+    for (int j = 0; j < EC; ++j) {
       const int q = j * kThreads + tid;
-      pred[j] = q < C && sflag[q] == 0;
-      if (pred[j]) {
-        mn = min(mn, sst[q]);
-        mx = max(mx, sst[q]);
-      }
-    }
-    const int nv = block_compact<E>(pred, pos, red);
-#pragma unroll
-    for (int j = 0; j < E; ++j)
-      if (pred[j]) vbuf0[pos[j]] = (uint16_t)(j * kThreads + tid);
-    block_minmax(mn, mx, red);  // barrier: vbuf0 complete
-    const int bits = (nv == 0 || mx == mn) ? 0 : 32 - __clz((int)(mx - mn));
-    uint16_t* src = vbuf0;
-    uint16_t* dst = vbuf1;
-    for (int bit = 0; bit < bits; ++bit) {
-      uint16_t qs[E];
-      bool one[E];
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        const int e = j * kThreads + tid;
-        qs[j] = 0;
-        one[j] = false;
-        if (e < nv) {
-          qs[j] = src[e];
-          one[j] = ((sst[qs[j]] - mn) >> bit) & 1u;
+      const bool cand = q < C && sflag[q] == 0;
+      cst[j] = cand ? sst[q] : 0xffffffffu;
+      nv += cand ? 1 : 0;
+      if (cand) {
+        if (cst[j] < v) {
+          v = cst[j];
+          c = 1;
+        } else if (cst[j] == v) {
+          c += 1;
         }
-        pred[j] = e < nv && !one[j];
       }
-      const int zeros = block_compact<E>(pred, pos, red);
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        const int e = j * kThreads + tid;
-        if (e < nv) dst[one[j] ? zeros + (e - pos[j]) : pos[j]] = qs[j];
-      }
-      __syncthreads();
-      uint16_t* tmp = src;
-      src = dst;
-      dst = tmp;
     }
+    block_mincount(v, c, nv, red);
     A = M < nv ? M : nv;
-    for (int j = tid; j < M; j += kThreads) {
-      const int k = mk[j];
-      if (j < A) {
-        const int q = src[j];
-        ures[k] = q;
-        stok[q] = unr[k];
-        sstp[q] = p.stamp;
-      } else {
-        ures[k] = kRowOverflow;
-      }
-    }
-    // one row per assigned miss: host row -> hot-slot row, 16 B per lane
-    const int pieces = PIECES > 0 ? PIECES : (p.row_bytes >> 4);
-    const int total = A * pieces;
-    const uint8_t* host_l = p.host + (int64_t)layer * p.host_stride;
-    uint8_t* pool_l = p.pool + (int64_t)layer * p.pool_stride;
-    constexpr int U = 4;
-    for (int base = tid; base < total; base += U * kThreads) {
-      u32x4 v[U];
-      uint8_t* dptr[U];
+    // take whole stamp groups, least recent first, each in slot order; the
+    // victims of a step normally span a few groups
+    int taken = 0, groups = 0;
+    bool fallback = false;
+#pragma unroll 1
+    while (taken < A) {
+      const int take = c < A - taken ? c : A - taken;
+      const uint32_t gv = v;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = base + u * kThreads;
-        dptr[u] = nullptr;
-        if (idx < total) {
-          const int jj = idx / pieces;
-          const int pc = idx - jj * pieces;
-          const int q = src[jj];
-          const int32_t tok = unr[mk[jj]];
-          const int64_t srow = ((int64_t)hbt[tok >> ps] << ps) | (tok & pm);
-          const int64_t drow = ((int64_t)hot[q >> ps] << ps) | (q & pm);
-          v[u] = *reinterpret_cast<const u32x4*>(host_l + srow * p.row_bytes + pc * 16);
-          dptr[u] = pool_l + drow * p.row_bytes + pc * 16;
+      for (int j = 0; j < EC; ++j) predC[j] = cst[j] == gv && (j * kThreads + tid) < C;
+      block_compact<EC>(predC, posC, red);
+#pragma unroll
+      for (int j = 0; j < EC; ++j)
+        if (predC[j] && posC[j] < take) vict[taken + posC[j]] = (uint16_t)(j * kThreads + tid);
+      taken += take;
+      if (taken >= A) break;
+      if (++groups >= kMaxGroups) {
+        fallback = true;
+        break;
+      }
+      uint32_t v2 = 0xffffffffu;
+      int c2 = 0, dummy = 0;
+#pragma unroll
+      for (int j = 0; j < EC; ++j) {
+        const uint32_t st = cst[j];
+        if (st > gv && st != 0xffffffffu) {
+          if (st < v2) {
+            v2 = st;
+            c2 = 1;
+          } else if (st == v2) {
+            c2 += 1;
+          }
         }
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (dptr[u]) *reinterpret_cast<u32x4*>(dptr[u]) = v[u];
+      block_mincount(v2, c2, dummy, red);
+      v = v2;
+      c = c2;
     }
+    __syncthreads();  // vict complete
+    if (fallback) {
+      // many stamp groups: stable radix sort of all candidates by stamp
+      uint16_t* vbuf0 = reinterpret_cast<uint16_t*>(keys);
+      uint16_t* vbuf1 = vbuf0 + C;
+      uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+      for (int j = 0; j < EC; ++j) {
+        const int q = j * kThreads + tid;
+        predC[j] = q < C && sflag[q] == 0;
+        if (predC[j]) {
+          mn = min(mn, sst[q]);
+          mx = max(mx, sst[q]);
+        }
+      }
+      block_minmax(mn, mx, red);
+      block_compact<EC>(predC, posC, red);
+#pragma unroll
+      for (int j = 0; j < EC; ++j)
+        if (predC[j]) vbuf0[posC[j]] = (uint16_t)(j * kThreads + tid);
+      __syncthreads();
+      const int bits = mx == mn ? 0 : 32 - __clz((int)(mx - mn));
+      uint16_t* srcb = vbuf0;
+      uint16_t* dstb = vbuf1;
+      for (int bit = 0; bit < bits; ++bit) {
+        uint16_t qs[EC];
+        bool one[EC];
+#pragma unroll
+        for (int j = 0; j < EC; ++j) {
+          const int e = j * kThreads + tid;
+          qs[j] = 0;
+          one[j] = false;
+          if (e < nv) {
+            qs[j] = srcb[e];
+            one[j] = ((sst[qs[j]] - mn) >> bit) & 1u;
+          }
+          predC[j] = e < nv && !one[j];
+        }
+        const int zeros = block_compact<EC>(predC, posC, red);
+#pragma unroll
+        for (int j = 0; j < EC; ++j) {
+          const int e = j * kThreads + tid;
+          if (e < nv) dstb[one[j] ? zeros + (e - posC[j]) : posC[j]] = qs[j];
+        }
+        __syncthreads();
+        uint16_t* tmp = srcb;
+        srcb = dstb;
+        dstb = tmp;
+      }
+      vict = srcb;
+    }
+    HS_PHASE_MARK(6);
+    for (int j = tid; j < M; j += kThreads)
+      ures[mk[j]] = j < A ? (kMissInit | (int32_t)vict[j]) : kRowOverflow;
     __syncthreads();  // ures final
   }
 
+  HS_PHASE_MARK(7);
   // ---- H: rows of the non-resident entries ------------------------------
+  int kk[ES];
+  lower_bound_multi<ES>(unr, n_u, tv, kk);
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    if (kind[j] != K_NONRES) continue;
-    const int e = j * kThreads + tid;
-    const int k = lower_bound(unr, n_u, t[j]);
+  for (int s = 0; s < ES; ++s) {
+    const bool nonres = ((kinds >> (2 * s)) & 3u) == K_NONRES;
     // every non-resident token is in the list by construction; the guard
-    // keeps a broken invariant from ever indexing past hot_blocks
-    const int32_t code = (k < n_u && unr[k] == t[j]) ? ures[k] : kRowInvalid;
-    rows[e] = (code >= 0 && code < C) ? ((hot[code >> ps] << ps) | (code & pm))
-                                      : (code >= 0 ? kRowInvalid : code);
+    // keeps a broken invariant from ever indexing past the slot arrays
+    if (!nonres || !(kk[s] < n_u && unr[kk[s]] == tv[s])) kk[s] = -1;
+    if (A > 0 && kk[s] >= 0) {
+      const int32_t code = ures[kk[s]];
+      if (code >= kMissBase && code != kNone)
+        atomicMin(&ures[kk[s]], kMissBase | ((sbase + 64 * s) << 13) | (code & 0x1fff));
+    }
+  }
+  if (A > 0) __syncthreads();
+#pragma unroll
+  for (int s = 0; s < ES; ++s) {
+    if (((kinds >> (2 * s)) & 3u) != K_NONRES) continue;
+    const int i = sbase + 64 * s;
+    int32_t row = kRowInvalid;
+    if (kk[s] >= 0) {
+      const int32_t code = ures[kk[s]];
+      if (code >= kMissBase && code != kNone) {
+        const int32_t q = code & 0x1fff;
+        row = -(8 + 2 * q + (((code >> 13) & 0x1fff) == i ? 1 : 0));
+      } else if (code >= 0 && code < C) {
+        row = (hot[code >> ps] << ps) | (code & pm);
+      } else if (code < 0) {
+        row = code;
+      }
+    }
+    rowA[s] = row;
   }
 
+  HS_PHASE_MARK(8);
+  // ---- stores: rows, the hit slots' stamps, the victims' token and stamp
+#pragma unroll
+  for (int s = 0; s < ES; ++s) {
+    const int i = sbase + 64 * s;
+    if (i < N) rows[i] = rowA[s];
+  }
+#pragma unroll
+  for (int j = 0; j < EC; ++j) {
+    const int q = j * kThreads + tid;
+    if (q < C && sflag[q] == 1) sstp[q] = p.stamp;
+  }
+  for (int j = tid; j < A; j += kThreads) {
+    const int q = vict[j];
+    stok[q] = unr[mk[j]];
+    sstp[q] = p.stamp;
+  }
   if (tid == 0) {
     int32_t* st = p.stats + (int64_t)rl * 8;
     st[0] = ucnt[1];
@@ -495,9 +776,9 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   }
 }
 
-template <int E, int PIECES>
-hipError_t launch_e(const KernelArgs& a, int grid, hipStream_t stream) {
-  auto fn = resolve_kernel<E, PIECES>;
+template <int ES, int EC>
+hipError_t launch_ec(const KernelArgs& a, int grid, hipStream_t stream) {
+  auto fn = resolve_kernel<ES, EC>;
   static bool attr = false;
   if (!attr) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -510,33 +791,44 @@ hipError_t launch_e(const KernelArgs& a, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int PIECES>
-hipError_t launch_pieces(const KernelArgs& a, int grid, int E, hipStream_t stream) {
-  switch (E) {
-    case 1: return launch_e<1, PIECES>(a, grid, stream);
-    case 2: return launch_e<2, PIECES>(a, grid, stream);
-    case 4: return launch_e<4, PIECES>(a, grid, stream);
-    default: return launch_e<8, PIECES>(a, grid, stream);
+template <int ES>
+hipError_t launch_es(const KernelArgs& a, int grid, int EC, hipStream_t stream) {
+  switch (EC) {
+    case 1: return launch_ec<ES, 1>(a, grid, stream);
+    case 2: return launch_ec<ES, 2>(a, grid, stream);
+    case 4: return launch_ec<ES, 4>(a, grid, stream);
+    case 8: return launch_ec<ES, 8>(a, grid, stream);
+    default: return launch_ec<ES, 16>(a, grid, stream);
   }
+}
+
+// Rounds of kThreads elements per thread covering n (a power of two, <= 16).
+int round_up_pow2_rounds(int n) {
+  const int e = (n + kThreads - 1) / kThreads;
+  return e <= 1 ? 1 : e <= 2 ? 2 : e <= 4 ? 4 : e <= 8 ? 8 : 16;
 }
 
 }  // namespace
 
 size_t resolve_lds_bytes(int32_t entries, int32_t hot_capacity) {
-  return make_plan(entries, hot_capacity).total;
+  return make_plan(entries, hot_capacity, round_up_pow2_rounds(entries)).total;
 }
 
 hipError_t launch_resolve(const ResolveParams& p, hipStream_t stream) {
+  const int ES = round_up_pow2_rounds(p.entries);
+  const int EC = round_up_pow2_rounds(p.hot_capacity);
   KernelArgs a;
   a.p = p;
-  a.plan = make_plan(p.entries, p.hot_capacity);
-  const int span = a.plan.sort_n > p.hot_capacity ? a.plan.sort_n : p.hot_capacity;
-  int E = (span + kThreads - 1) / kThreads;
-  E = E <= 1 ? 1 : E <= 2 ? 2 : E <= 4 ? 4 : 8;
+  a.plan = make_plan(p.entries, p.hot_capacity, ES);
   const int grid = p.num_reqs * p.num_layers;
   if (grid == 0) return hipSuccess;
-  if (p.row_bytes == 656) return launch_pieces<41>(a, grid, E, stream);
-  return launch_pieces<0>(a, grid, E, stream);
+  switch (ES) {
+    case 1: return launch_es<1>(a, grid, EC, stream);
+    case 2: return launch_es<2>(a, grid, EC, stream);
+    case 4: return launch_es<4>(a, grid, EC, stream);
+    case 8: return launch_es<8>(a, grid, EC, stream);
+    default: return launch_es<16>(a, grid, EC, stream);
+  }
 }
 
 }  // namespace hs

@@ -118,7 +118,7 @@ def test_gather_and_offload_reject(lib):
     assert g(0x1000, None, 1, 10, 0x1000) == 1
     assert g(0x1000, 0x1000, 1, 10, None) == 1
     assert g(0x1000, 0x1000, -1, 10, 0x1000) == 1
-    assert g(0x1000, 0x1000, 1, 200_000_000, 0x1000) == 2  # pieces per request-layer >= 2^32
+    assert g(0x1000, 0x1000, 1 << 20, 100_000, 0x1000) == 2  # more than 2^31 wave chunks
     assert g(0x1000, 0x1000, 0, 10, 0x1000) == 0            # nothing to do
     o = lambda pool, host, pairs, n: lib.hs_offload_prefix_pages(ctypes.byref(lay), pool, host,
                                                                 pairs, n, None)
