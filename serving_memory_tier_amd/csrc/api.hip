@@ -105,6 +105,8 @@ hs_status check_resolve(const hs_layout* lay, const hs_batch* b, const int32_t* 
   const int64_t n_rl = (int64_t)b->num_reqs * lay->num_layers;
   if (n_rl > INT32_MAX) return HS_ERR_UNSUPPORTED;
   if ((s = check_gather(lay, n_rl, (int64_t)num_pos * top_k)) != HS_OK) return s;
+  if (hs::resolve_lds_bytes(num_pos * top_k, lay->hot_capacity) > hs::kMaxLdsBytes)
+    return HS_ERR_UNSUPPORTED;
   if (b->num_reqs > 0) {
     if (!b->kv_pool || !b->block_table || !b->host_block_table || !b->ctx_len ||
         !b->hot_blocks || !b->slot_token || !b->slot_stamp)

@@ -7,9 +7,11 @@
 
 namespace hs {
 
-// Threads per resolver workgroup: 8 wave64s, one workgroup per request-layer
-// (with 256 VGPRs per lane available, every size variant runs without spills).
-constexpr int kResolveThreads = 512;
+// Threads per resolver workgroup (one workgroup per request-layer).
+#ifndef HS_RESOLVE_THREADS
+#define HS_RESOLVE_THREADS 1024
+#endif
+constexpr int kResolveThreads = HS_RESOLVE_THREADS;
 // Threads per copy workgroup (gather / offload) and 16-byte pieces per thread
 // per iteration.
 constexpr int kCopyThreads = 256;
@@ -43,6 +45,9 @@ struct ResolveParams {
 
 // Enqueue the resolver (no gather).  Returns a hipError_t from the launch.
 hipError_t launch_resolve(const ResolveParams& p, hipStream_t stream);
+
+// LDS of one gfx950 compute unit, all of which one workgroup may use.
+constexpr size_t kMaxLdsBytes = 160 * 1024;
 
 // Bytes of dynamic LDS the resolver needs for N entries and C slots.
 size_t resolve_lds_bytes(int32_t entries, int32_t hot_capacity);

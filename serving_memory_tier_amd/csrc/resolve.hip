@@ -44,7 +44,9 @@
 
 // Phase markers for timing builds; empty in the library.
 #ifndef HS_PHASE_MARK
+#define HS_PHASE_DECL
 #define HS_PHASE_MARK(i)
+#define HS_PHASE_FLUSH
 #endif
 
 namespace hs {
@@ -78,6 +80,8 @@ struct LdsPlan {
   uint32_t off_stp;    // uint32[C]: slot stamps
   uint32_t off_flag;   // uint8[C]: 0 free, 1 hit, 2 unusable
   uint32_t off_red;    // int32[kRed]: scan / reduction scratch
+  uint32_t off_bits;   // uint32[bits_words]: membership filter of the distinct list
+  int32_t bits_log2;   // log2 of the filter's size in bits
   uint32_t total;
 };
 
@@ -98,6 +102,12 @@ __host__ __device__ inline LdsPlan make_plan(int32_t N, int32_t C, int32_t ES) {
   p.off_stp = o;  o = align16(o + 4u * (uint32_t)C);
   p.off_flag = o; o = align16(o + (uint32_t)C);
   p.off_red = o;  o = align16(o + 4u * (uint32_t)kRed);
+  // 4 filter bits per possible distinct token (at least 4096): a slot whose
+  // token is not in the list almost always finds its bit clear
+  int32_t fb = 12;
+  while ((1 << fb) < 4 * N) ++fb;
+  p.bits_log2 = fb;
+  p.off_bits = o; o = align16(o + (uint32_t)(1u << fb) / 8u);
   p.total = o;
   return p;
 }
@@ -108,6 +118,55 @@ __device__ inline int wave_id() { return threadIdx.x >> 6; }
 __device__ inline int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// x ^ lane distance J within a wave64, for compile-time J: DPP moves for 1, 2,
+// 4 and 8 (quad permutes, half-row mirror + quad mirror, row rotate by 8),
+// a swizzle for 16, a permute through the LDS crossbar for 32.
+template <int J>
+__device__ __forceinline__ int32_t lane_xor(int32_t v) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const int32_t m = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // half mirror
+    return __builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false);   // quad_perm [3,2,1,0]
+  } else if constexpr (J == 8) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (J == 16) {
+    return __builtin_amdgcn_ds_swizzle(v, 0x401F);                     // xor 16 in 32 lanes
+  } else {
+    return __shfl_xor(v, J);
+  }
+}
+
+// Wave64 reductions by DPP/swizzle butterflies within each 32-lane half, the
+// halves joined through two lane reads; the result is wave-uniform.
+__device__ __forceinline__ int wave_sum(int v) {
+  v += lane_xor<1>(v);
+  v += lane_xor<2>(v);
+  v += lane_xor<4>(v);
+  v += lane_xor<8>(v);
+  v += lane_xor<16>(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 32);
+}
+
+// Inclusive prefix sum over the 64 lanes: row shifts within rows of 16, then
+// row broadcasts of lanes 15 and 31 into the rows above.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// Filter position of a token: a multiplicative hash (Knuth) on `log2` bits.
+__device__ inline uint32_t filter_bit(int32_t t, int log2) {
+  return ((uint32_t)t * 0x9E3779B1u) >> (32 - log2);
 }
 
 // Stable block-wide compaction over elements e = j * kThreads + tid, j < E:
@@ -129,12 +188,7 @@ __device__ int block_compact(const bool (&pred)[E], int (&pos)[E], int* red) {
     const int v0 = i0 < n ? red[i0] : 0;
     const int v1 = i1 < n ? red[i1] : 0;
     const int s = v0 + v1;
-    int inc = s;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int t = __shfl_up(inc, d);
-      if (l >= d) inc += t;
-    }
+    const int inc = wave_incl_scan(s);
     const int ex = inc - s;
     if (i0 < n) red[i0] = ex;
     if (i1 < n) red[i1] = ex + v0;
@@ -164,8 +218,7 @@ __device__ int block_compact_sum(const bool (&pred)[E], int (&pos)[E], int (&sum
   }
 #pragma unroll
   for (int c = 0; c < NS; ++c) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) sums[c] += __shfl_xor(sums[c], d);
+    sums[c] = wave_sum(sums[c]);
     if (l == 0) red[n + 1 + c * kWaves + w] = sums[c];
   }
   __syncthreads();
@@ -174,12 +227,7 @@ __device__ int block_compact_sum(const bool (&pred)[E], int (&pos)[E], int (&sum
     const int v0 = i0 < n ? red[i0] : 0;
     const int v1 = i1 < n ? red[i1] : 0;
     const int s = v0 + v1;
-    int inc = s;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int t = __shfl_up(inc, d);
-      if (l >= d) inc += t;
-    }
+    const int inc = wave_incl_scan(s);
     const int ex = inc - s;
     if (i0 < n) red[i0] = ex;
     if (i1 < n) red[i1] = ex + v0;
@@ -190,12 +238,7 @@ __device__ int block_compact_sum(const bool (&pred)[E], int (&pos)[E], int (&sum
   for (int j = 0; j < E; ++j) pos[j] = red[j * kWaves + w] + below[j];
   const int total = red[n];
 #pragma unroll
-  for (int c = 0; c < NS; ++c) {
-    int t = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) t += red[n + 1 + c * kWaves + i];
-    sums[c] = t;
-  }
+  for (int c = 0; c < NS; ++c) sums[c] = wave_sum(l < kWaves ? red[n + 1 + c * kWaves + l] : 0);
   __syncthreads();
   return total;
 }
@@ -204,39 +247,46 @@ __device__ int block_compact_sum(const bool (&pred)[E], int (&pos)[E], int (&sum
 // with c = 0 means "none".
 __device__ inline void block_mincount(uint32_t& v, int& c, int& s, int* red) {
   const int w = wave_id(), l = lane_id();
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t ov = (uint32_t)__shfl_xor((int)v, d);
-    const int oc = __shfl_xor(c, d);
-    s += __shfl_xor(s, d);
+  // (value, count) combine: keep the smaller value, add counts on ties
+  auto comb = [&](uint32_t ov, int oc) {
     if (ov < v) {
       v = ov;
       c = oc;
     } else if (ov == v) {
       c += oc;
     }
+  };
+  comb((uint32_t)lane_xor<1>((int)v), lane_xor<1>(c));
+  comb((uint32_t)lane_xor<2>((int)v), lane_xor<2>(c));
+  comb((uint32_t)lane_xor<4>((int)v), lane_xor<4>(c));
+  comb((uint32_t)lane_xor<8>((int)v), lane_xor<8>(c));
+  comb((uint32_t)lane_xor<16>((int)v), lane_xor<16>(c));
+  {
+    const uint32_t v0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const int c0 = __builtin_amdgcn_readlane(c, 0);
+    const uint32_t v1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const int c1 = __builtin_amdgcn_readlane(c, 32);
+    v = v0;
+    c = c0;
+    comb(v1, c1);
   }
+  s = wave_sum(s);
   if (l == 0) {
     red[w] = (int)v;
     red[kWaves + w] = c;
     red[2 * kWaves + w] = s;
   }
   __syncthreads();
-  v = 0xffffffffu;
-  c = 0;
-  s = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const uint32_t ov = (uint32_t)red[i];
-    const int oc = red[kWaves + i];
-    s += red[2 * kWaves + i];
-    if (ov < v) {
-      v = ov;
-      c = oc;
-    } else if (ov == v) {
-      c += oc;
-    }
-  }
+  v = l < kWaves ? (uint32_t)red[l] : 0xffffffffu;
+  c = l < kWaves ? red[kWaves + l] : 0;
+  s = wave_sum(l < kWaves ? red[2 * kWaves + l] : 0);
+  comb((uint32_t)lane_xor<1>((int)v), lane_xor<1>(c));
+  comb((uint32_t)lane_xor<2>((int)v), lane_xor<2>(c));
+  comb((uint32_t)lane_xor<4>((int)v), lane_xor<4>(c));
+  comb((uint32_t)lane_xor<8>((int)v), lane_xor<8>(c));
+  comb((uint32_t)lane_xor<16>((int)v), lane_xor<16>(c));
+  v = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  c = __builtin_amdgcn_readlane(c, 0);
   __syncthreads();
 }
 
@@ -261,62 +311,49 @@ __device__ inline void block_sum4(int (&v)[4], int* red) {
   const int w = wave_id(), l = lane_id();
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v[c] += __shfl_xor(v[c], d);
+    v[c] = wave_sum(v[c]);
     if (l == 0) red[c * kWaves + w] = v[c];
   }
   __syncthreads();
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    int t = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) t += red[c * kWaves + i];
-    v[c] = t;
-  }
+  for (int c = 0; c < 4; ++c) v[c] = wave_sum(l < kWaves ? red[c * kWaves + l] : 0);
   __syncthreads();
 }
 
 __device__ inline void block_minmax(uint32_t& mn, uint32_t& mx, int* red) {
   const int w = wave_id(), l = lane_id();
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, d));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d));
-  }
+  mn = min(mn, (uint32_t)lane_xor<1>((int)mn));
+  mx = max(mx, (uint32_t)lane_xor<1>((int)mx));
+  mn = min(mn, (uint32_t)lane_xor<2>((int)mn));
+  mx = max(mx, (uint32_t)lane_xor<2>((int)mx));
+  mn = min(mn, (uint32_t)lane_xor<4>((int)mn));
+  mx = max(mx, (uint32_t)lane_xor<4>((int)mx));
+  mn = min(mn, (uint32_t)lane_xor<8>((int)mn));
+  mx = max(mx, (uint32_t)lane_xor<8>((int)mx));
+  mn = min(mn, (uint32_t)lane_xor<16>((int)mn));
+  mx = max(mx, (uint32_t)lane_xor<16>((int)mx));
+  mn = min((uint32_t)__builtin_amdgcn_readlane((int)mn, 0),
+           (uint32_t)__builtin_amdgcn_readlane((int)mn, 32));
+  mx = max((uint32_t)__builtin_amdgcn_readlane((int)mx, 0),
+           (uint32_t)__builtin_amdgcn_readlane((int)mx, 32));
   if (l == 0) {
     red[w] = (int)mn;
     red[kWaves + w] = (int)mx;
   }
   __syncthreads();
-  mn = 0xffffffffu;
-  mx = 0u;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    mn = min(mn, (uint32_t)red[i]);
-    mx = max(mx, (uint32_t)red[kWaves + i]);
-  }
+  mn = l < kWaves ? (uint32_t)red[l] : 0xffffffffu;
+  mx = l < kWaves ? (uint32_t)red[kWaves + l] : 0u;
+  mn = min(mn, (uint32_t)lane_xor<1>((int)mn));
+  mx = max(mx, (uint32_t)lane_xor<1>((int)mx));
+  mn = min(mn, (uint32_t)lane_xor<2>((int)mn));
+  mx = max(mx, (uint32_t)lane_xor<2>((int)mx));
+  mn = min(mn, (uint32_t)lane_xor<4>((int)mn));
+  mx = max(mx, (uint32_t)lane_xor<4>((int)mx));
+  mn = min(mn, (uint32_t)lane_xor<8>((int)mn));
+  mx = max(mx, (uint32_t)lane_xor<8>((int)mx));
+  mn = (uint32_t)__builtin_amdgcn_readlane((int)min(mn, (uint32_t)lane_xor<16>((int)mn)), 0);
+  mx = (uint32_t)__builtin_amdgcn_readlane((int)max(mx, (uint32_t)lane_xor<16>((int)mx)), 0);
   __syncthreads();
-}
-
-// x ^ lane distance J within a wave64, for compile-time J: DPP moves for 1, 2,
-// 4 and 8 (quad permutes, half-row mirror + quad mirror, row rotate by 8),
-// a swizzle for 16, a permute through the LDS crossbar for 32.
-template <int J>
-__device__ __forceinline__ int32_t lane_xor(int32_t v) {
-  if constexpr (J == 1) {
-    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-  } else if constexpr (J == 2) {
-    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-  } else if constexpr (J == 4) {
-    const int32_t m = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // half mirror
-    return __builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false);   // quad_perm [3,2,1,0]
-  } else if constexpr (J == 8) {
-    return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
-  } else if constexpr (J == 16) {
-    return __builtin_amdgcn_ds_swizzle(v, 0x401F);                     // xor 16 in 32 lanes
-  } else {
-    return __shfl_xor(v, J);
-  }
 }
 
 // One stage (k = K, j = J) of an ascending bitonic network over kThreads * ES
@@ -416,6 +453,8 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   uint32_t* sst = reinterpret_cast<uint32_t*>(lds + plan.off_stp);
   uint8_t* sflag = reinterpret_cast<uint8_t*>(lds + plan.off_flag);
   int* red = reinterpret_cast<int*>(lds + plan.off_red);
+  uint32_t* fbits = reinterpret_cast<uint32_t*>(lds + plan.off_bits);
+  const int fb = plan.bits_log2;
 
   const int tid = threadIdx.x;
   const int l = lane_id(), w = wave_id();
@@ -436,6 +475,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   const int64_t host_blocks = p.host_rows >> ps;
   const int sbase = w * 64 * ES + l;  // element s of this thread: sbase + 64 * s
 
+  HS_PHASE_DECL;
   HS_PHASE_MARK(0);
   // ---- A: load in sort layout and classify; stage the slots ------------
   int32_t x[ES];     // sort keys
@@ -461,6 +501,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
     btv[s] = inrange ? bt[v >> ps] : -1;
     hbv[s] = inrange ? hbt[v >> ps] : -1;
   }
+  for (int wi = tid; wi < (1 << fb) / 32; wi += kThreads) fbits[wi] = 0u;
   int32_t tokq[EC];
 #pragma unroll
   for (int j = 0; j < EC; ++j) {
@@ -542,20 +583,25 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
     if (predS[j]) {
       unr[posS[j]] = sv[j];
       ures[posS[j]] = sinit[j];
+      const uint32_t fbit = filter_bit(sv[j], fb);
+      atomicOr(&fbits[fbit >> 5], 1u << (fbit & 31));
     }
-  __syncthreads();  // unr and ures complete
+  __syncthreads();  // unr, ures and the filter complete
 
   HS_PHASE_MARK(3);
   // ---- C: hot-map lookup (each slot searches its token) -----------------
   if (n_u > 0) {
-    int kq[EC];
-    lower_bound_multi<EC>(unr, n_u, tokq, kq);
 #pragma unroll
     for (int j = 0; j < EC; ++j) {
       const int q = j * kThreads + tid;
       const int32_t tk = tokq[j];
-      if (q < C && tk >= 0 && sflag[q] == 0 && kq[j] < n_u && unr[kq[j]] == tk)
-        atomicMin(&ures[kq[j]], q);
+      if (q < C && tk >= 0 && sflag[q] == 0) {
+        const uint32_t fbit = filter_bit(tk, fb);
+        if ((fbits[fbit >> 5] >> (fbit & 31)) & 1u) {
+          const int k = lower_bound(unr, n_u, tk);
+          if (k < n_u && unr[k] == tk) atomicMin(&ures[k], q);
+        }
+      }
     }
   }
   __syncthreads();
@@ -713,13 +759,14 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   HS_PHASE_MARK(7);
   // ---- H: rows of the non-resident entries ------------------------------
   int kk[ES];
-  lower_bound_multi<ES>(unr, n_u, tv, kk);
 #pragma unroll
   for (int s = 0; s < ES; ++s) {
-    const bool nonres = ((kinds >> (2 * s)) & 3u) == K_NONRES;
+    kk[s] = -1;
+    if (((kinds >> (2 * s)) & 3u) != K_NONRES) continue;
+    const int k = lower_bound(unr, n_u, tv[s]);
     // every non-resident token is in the list by construction; the guard
     // keeps a broken invariant from ever indexing past the slot arrays
-    if (!nonres || !(kk[s] < n_u && unr[kk[s]] == tv[s])) kk[s] = -1;
+    if (k < n_u && unr[k] == tv[s]) kk[s] = k;
     if (A > 0 && kk[s] >= 0) {
       const int32_t code = ures[kk[s]];
       if (code >= kMissBase && code != kNone)
@@ -774,6 +821,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
     st[6] = n_nonpad - ucnt[0];
     st[7] = 0;
   }
+  HS_PHASE_FLUSH;
 }
 
 template <int ES, int EC>
@@ -783,7 +831,7 @@ hipError_t launch_ec(const KernelArgs& a, int grid, hipStream_t stream) {
   if (!attr) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         160 * 1024);
+                                         (int)kMaxLdsBytes);
     if (err != hipSuccess) return err;
     attr = true;
   }
@@ -791,18 +839,26 @@ hipError_t launch_ec(const KernelArgs& a, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Largest rounds per thread needed: HS_MAX_ENTRIES and HS_MAX_HOT_CAPACITY
+// are 8192, i.e. 8192 / kThreads rounds.
+constexpr int kMaxRounds = 8192 / kThreads;
+
 template <int ES>
 hipError_t launch_es(const KernelArgs& a, int grid, int EC, hipStream_t stream) {
-  switch (EC) {
-    case 1: return launch_ec<ES, 1>(a, grid, stream);
-    case 2: return launch_ec<ES, 2>(a, grid, stream);
-    case 4: return launch_ec<ES, 4>(a, grid, stream);
-    case 8: return launch_ec<ES, 8>(a, grid, stream);
-    default: return launch_ec<ES, 16>(a, grid, stream);
+  if constexpr (ES > kMaxRounds) {
+    return hipErrorInvalidValue;
+  } else {
+    switch (EC) {
+      case 1: return launch_ec<ES, 1>(a, grid, stream);
+      case 2: return launch_ec<ES, 2>(a, grid, stream);
+      case 4: return launch_ec<ES, 4>(a, grid, stream);
+      case 8: return launch_ec<ES, (8 <= kMaxRounds ? 8 : kMaxRounds)>(a, grid, stream);
+      default: return launch_ec<ES, kMaxRounds>(a, grid, stream);
+    }
   }
 }
 
-// Rounds of kThreads elements per thread covering n (a power of two, <= 16).
+// Rounds of kThreads elements per thread covering n (a power of two).
 int round_up_pow2_rounds(int n) {
   const int e = (n + kThreads - 1) / kThreads;
   return e <= 1 ? 1 : e <= 2 ? 2 : e <= 4 ? 4 : e <= 8 ? 8 : 16;
