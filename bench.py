@@ -47,7 +47,103 @@ def parse():
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hit-replays", type=int, default=50)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed steps one by one instead of replaying a captured graph")
+    ap.add_argument("--event-steps", type=int, default=64,
+                    help="steps launched one by one with HIP events around every kernel "
+                         "(per-kernel durations), after the timed steps")
     return ap.parse_args()
+
+
+class HipEvents:
+    """Raw HIP timing events (ctypes on the HIP runtime): they can be recorded
+    inside a captured graph as external event nodes, so per-kernel times are
+    measured on the launch stream during a graph replay too."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        # the HIP runtime already mapped into this process (torch's, which the
+        # library binds to by soname): a second copy would not know torch's
+        # streams
+        paths = sorted({ln.split()[-1] for ln in open("/proc/self/maps")
+                        if "libamdhip64" in ln and ln.split()[-1].startswith("/")})
+        self.hip = ctypes.CDLL(paths[0] if paths else "libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        # the runtime exports several versions of this symbol; the external
+        # event node of stream capture needs the hip_6.4 one
+        libc = ctypes.CDLL("libc.so.6")
+        libc.dlvsym.restype = ctypes.c_void_p
+        libc.dlvsym.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_char_p]
+        addr = libc.dlvsym(self.hip._handle, b"hipEventRecordWithFlags", b"hip_6.4")
+        proto = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint)
+        self.record_fn = proto(addr) if addr else self.hip.hipEventRecordWithFlags
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def new(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.made.append(e)
+        return e
+
+    def record(self, e, stream, external):
+        if self.record_fn(e, self.ct.c_void_p(stream), 1 if external else 0) != 0:
+            raise RuntimeError("hipEventRecordWithFlags failed")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(e)
+        self.made = []
+
+    # -- stream capture into a HIP graph (relaxed mode), replay ----------
+    def begin_capture(self, stream):
+        ct = self.ct
+        self.hip.hipStreamBeginCapture.argtypes = [ct.c_void_p, ct.c_int]
+        if self.hip.hipStreamBeginCapture(ct.c_void_p(stream), 2) != 0:  # relaxed
+            raise RuntimeError("hipStreamBeginCapture failed")
+
+    def end_capture(self, stream):
+        ct = self.ct
+        g, ge = ct.c_void_p(), ct.c_void_p()
+        self.hip.hipStreamEndCapture.argtypes = [ct.c_void_p, ct.POINTER(ct.c_void_p)]
+        self.hip.hipGraphInstantiate.argtypes = [ct.POINTER(ct.c_void_p), ct.c_void_p,
+                                                 ct.c_void_p, ct.c_void_p, ct.c_size_t]
+        if self.hip.hipStreamEndCapture(ct.c_void_p(stream), ct.byref(g)) != 0:
+            raise RuntimeError("hipStreamEndCapture failed")
+        if self.hip.hipGraphInstantiate(ct.byref(ge), g, None, None, 0) != 0:
+            raise RuntimeError("hipGraphInstantiate failed")
+        self.graph, self.exec = g, ge
+
+    def launch(self, stream):
+        self.hip.hipGraphLaunch.argtypes = [self.ct.c_void_p, self.ct.c_void_p]
+        if self.hip.hipGraphLaunch(self.exec, self.ct.c_void_p(stream)) != 0:
+            raise RuntimeError("hipGraphLaunch failed")
+
+    def destroy_graph(self):
+        self.hip.hipGraphExecDestroy.argtypes = [self.ct.c_void_p]
+        self.hip.hipGraphDestroy.argtypes = [self.ct.c_void_p]
+        if getattr(self, "exec", None):
+            self.hip.hipGraphExecDestroy(self.exec)
+            self.hip.hipGraphDestroy(self.graph)
+            self.exec = None
+
+    def memcpy_h2d(self, dst, src, nbytes, stream):
+        ct = self.ct
+        self.hip.hipMemcpyAsync.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_size_t, ct.c_int,
+                                            ct.c_void_p]
+        if self.hip.hipMemcpyAsync(ct.c_void_p(dst), ct.c_void_p(src), nbytes, 1,
+                                   ct.c_void_p(stream)) != 0:
+            raise RuntimeError("hipMemcpyAsync failed")
 
 
 def build_workload(name: str, n_steps: int):
@@ -105,8 +201,9 @@ def main():
     torch.cuda.set_device(0)
 
     W, K = args.warmup, args.steps
+    KE = min(K, args.event_steps)  # eager steps timed with events, after the graph
     t_gen = time.time()
-    wl = build_workload(args.workload, W + K)
+    wl = build_workload(args.workload, W + K + KE)
     print(f"[bench] workload {wl.name}: R={wl.R} L={wl.L} P={wl.P} K={wl.K} C={wl.C} "
           f"steps={len(wl.steps)} generated in {time.time() - t_gen:.1f}s", file=sys.stderr,
           flush=True)
@@ -120,59 +217,98 @@ def main():
     stats_all = torch.zeros((n_steps, wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
     batches = [hs.batch_of(wl.R, wl.max_pages, dev.pool, dev.host_pool, dev.bt, dev.hbt,
                            ctx_all[i], dev.hot, dev.tok, dev.stp) for i in range(n_steps)]
+    # the scheduler's table updates between steps (nulled pages, new host
+    # copies) as (device address, pinned source) pairs: plain 4-byte copies
     table_sets = []
+    n_vals = sum(s.hbt_set.shape[0] + s.bt_set.shape[0] for s in wl.steps)
+    pinned_vals = torch.empty(max(1, n_vals), dtype=torch.int32, pin_memory=True)
+    k = 0
     for s in wl.steps:
         sets = []
         for arr, t in ((s.hbt_set, dev.hbt), (s.bt_set, dev.bt)):
-            if arr.shape[0]:
-                a = torch.from_numpy(arr).cuda()
-                sets.append((t, a[:, 0], a[:, 1], a[:, 2].to(torch.int32)))
+            for r, p, v in arr:
+                pinned_vals[k] = int(v)
+                sets.append((t.data_ptr() + 4 * (int(r) * wl.max_pages + int(p)),
+                             pinned_vals.data_ptr() + 4 * k))
+                k += 1
         table_sets.append(sets)
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
+    hev = HipEvents()
 
-    def step(i, ev=None):
-        for (t, r, p, v) in table_sets[i]:
-            t[r, p] = v
+    def step(i, sp, ev=None, external=False):
+        for dst, srcp in table_sets[i]:
+            hev.memcpy_h2d(dst, srcp, 4, sp)
         if ev is not None:
-            ev[0].record(stream)
+            hev.record(ev[0], sp, external)
         hs.hs_resolve_decide(dev.layout, batches[i], dev.topk[i], wl.P, wl.K, wl.steps[i].stamp,
                              dev.rows, stats_all[i], sp)
         if ev is not None:
-            ev[1].record(stream)
+            hev.record(ev[1], sp, external)
         hs.hs_resolve_move(dev.layout, batches[i], dev.topk[i], wl.P, wl.K, dev.rows, dev.out, sp)
         if ev is not None:
-            ev[2].record(stream)
+            hev.record(ev[2], sp, external)
         n_off = wl.steps[i].offload.shape[0]
         if n_off:
             hs.hs_offload_prefix_pages(dev.layout, dev.pool, dev.host_pool, dev.pairs[i], n_off,
                                        sp)
             if ev is not None:
-                ev[3].record(stream)
+                hev.record(ev[3], sp, external)
 
+    sp0 = torch.cuda.current_stream().cuda_stream
     for i in range(W):
-        step(i)
+        step(i, sp0)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    launch = "eager"
+    graph = False
+    cap = torch.cuda.Stream()
+    if not args.eager:
+        # the K timed steps, captured once and replayed as one graph: the
+        # decode path waits on nothing from the host, so it captures as is
+        try:
+            hev.begin_capture(cap.cuda_stream)
+            try:
+                for j in range(K):
+                    step(W + j, cap.cuda_stream)
+            finally:
+                hev.end_capture(cap.cuda_stream)
+            graph = True
+            launch = "hip_graph"
+        except Exception as exc:  # fall back to eager launches
+            print(f"[bench] graph capture failed ({exc}); timing eager launches",
+                  file=sys.stderr, flush=True)
+            graph = False
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for j in range(K):
-        step(W + j, events[j])
+    if graph:
+        hev.launch(cap.cuda_stream)
+    else:
+        for j in range(K):
+            step(W + j, sp0)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
 
-    dec_ms = [events[j][0].elapsed_time(events[j][1]) for j in range(K)]
-    mov_ms = [events[j][1].elapsed_time(events[j][2]) for j in range(K)]
-    off = [(j, events[j][2].elapsed_time(events[j][3])) for j in range(K)
-           if wl.steps[W + j].offload.shape[0]]
-    st = stats_all[W:].sum(dim=(0, 1, 2)).cpu().numpy().astype(np.int64)
+    # per-kernel durations: the next KE steps launched one by one, HIP events
+    # on the launch stream around every kernel
+    events = [[hev.new() for _ in range(4)] for _ in range(KE)]
+    for j in range(KE):
+        step(W + K + j, sp0, events[j])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    dec_ms = [hev.elapsed_ms(events[j][0], events[j][1]) for j in range(KE)]
+    mov_ms = [hev.elapsed_ms(events[j][1], events[j][2]) for j in range(KE)]
+    off = [(j, hev.elapsed_ms(events[j][2], events[j][3])) for j in range(KE)
+           if wl.steps[W + K + j].offload.shape[0]]
+    st = stats_all[W + K:W + K + KE].sum(dim=(0, 1, 2)).cpu().numpy().astype(np.int64)
+    st_all = stats_all[W:W + K].sum(dim=(0, 1, 2)).cpu().numpy().astype(np.int64)
     dec_us = 1e3 * float(np.mean(dec_ms))
     mov_us = 1e3 * float(np.mean(mov_ms))
     value = entries * K / wall
 
-    dec_bytes = decide_hbm_bytes(wl, st, K)
-    mov_bytes = move_hbm_bytes(wl, st, K)
-    host_bytes = st[2] * ROW / K
+    dec_bytes = decide_hbm_bytes(wl, st, KE)
+    mov_bytes = move_hbm_bytes(wl, st, KE)
+    host_bytes = st[2] * ROW / KE
     kernels = {
         "decide": {"us": round(dec_us, 2), "hbm_bytes": int(dec_bytes),
                    "hbm_gbps": round(dec_bytes / dec_us / 1e3, 1)},
@@ -182,7 +318,7 @@ def main():
                  "host_link_gbps": round(host_bytes / mov_us / 1e3, 2)},
     }
     if off:
-        page_layers = [wl.steps[W + j].offload.shape[0] * wl.L for j, _ in off]
+        page_layers = [wl.steps[W + K + j].offload.shape[0] * wl.L for j, _ in off]
         off_us = 1e3 * float(np.mean([ms for _, ms in off]))
         off_bytes = float(np.mean(page_layers)) * PAGE * ROW
         kernels["offload"] = {"us": round(off_us, 2), "launches": len(off),
@@ -191,7 +327,7 @@ def main():
 
     # the hit-replay path: the last step's lists again with the same stamp --
     # every non-resident token hits, no host traffic, HBM-bound
-    last = W + K - 1
+    last = W + K + KE - 1
     rep = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.hit_replays)]
     rep_stats = torch.zeros((wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
     for j in range(args.hit_replays):
@@ -235,28 +371,33 @@ def main():
         roofline = {"kernel": "decide", "bound": "hbm", "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                     "traffic": None}
-    step_hbm = dec_bytes + mov_bytes
+    # whole steps of the timed region: algorithmic bytes per step / step time
+    step_hbm_k = decide_hbm_bytes(wl, st_all, K) + move_hbm_bytes(wl, st_all, K)
+    host_k = st_all[2] * ROW / K
     line = {
         "metric": METRIC, "value": round(value), "unit": "rows/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(1e3 * wall / K, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": wl.name, "requests": wl.R, "layers": wl.L, "positions": wl.P,
                    "top_k": wl.K, "hot_capacity": wl.C, "context": int(wl.ctx0.max()),
-                   "row_bytes": ROW, "page_size": PAGE},
-        "hbm": {"achieved": round(step_hbm / (dec_us + mov_us) / 1e3, 1),
+                   "row_bytes": ROW, "page_size": PAGE, "launch": launch},
+        "hbm": {"achieved": round(step_hbm_k / (wall / K) / 1e9, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(step_hbm / (dec_us + mov_us) / 1e3 / HBM_PEAK_GBPS, 4)},
-        "host_link": {"achieved": round(host_bytes / (dec_us + mov_us) / 1e3, 2),
+                "frac": round(step_hbm_k / (wall / K) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "host_link": {"achieved": round(host_k / (wall / K) / 1e9, 2),
                       "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
-                      "frac": round(host_bytes / (dec_us + mov_us) / 1e3 / HOST_LINK_PEAK_GBPS,
-                                    4)},
-        "per_step": {"hits": round(st[1] / K, 1), "misses": round(st[2] / K, 1),
-                     "resident": round(st[0] / K, 1)},
+                      "frac": round(host_k / (wall / K) / 1e9 / HOST_LINK_PEAK_GBPS, 4)},
+        "per_step": {"hits": round(st_all[1] / K, 1), "misses": round(st_all[2] / K, 1),
+                     "resident": round(st_all[0] / K, 1)},
         "kernels": kernels,
+        "kernel_timing": f"HIP events around each kernel over {KE} eagerly launched steps "
+                         f"following the timed ones",
         "hit_replay": hit_replay,
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    hev.destroy_graph()
+    hev.close()
     dev.close()
 
     if not args.no_cpu_baseline:
