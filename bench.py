@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--hit-replays", type=int, default=50)
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a captured graph")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with one plain 256 MiB device copy (counter calibration runs)")
     ap.add_argument("--event-steps", type=int, default=64,
                     help="steps launched one by one with HIP events around every kernel "
                          "(per-kernel durations), after the timed steps")
@@ -155,6 +157,28 @@ def build_workload(name: str, n_steps: int):
     if name == "mixed_state":
         return hs_gen.mixed_state(steps=n_steps)
     return hs_gen.multi_layer(turns=n_steps)
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when it was taken on another workload or on other kernel sources."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "counters_decide_move_mixed_decode.md")
+    if workload != "mixed_decode" or not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in ("resolve.hip", "copy.hip", "hs_internal.h"):
+        with open(os.path.join(ROOT, "serving_memory_tier_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "|")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    v = fields.get(f"{kernel}_traffic_bytes_per_launch")
+    return int(v) if v else None
 
 
 def decide_hbm_bytes(wl, stats_sum, n_launches):
@@ -371,6 +395,7 @@ def main():
         roofline = {"kernel": "decide", "bound": "hbm", "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                     "traffic": None}
+    roofline["traffic"] = measured_traffic(roofline["kernel"], wl.name)
     # whole steps of the timed region: algorithmic bytes per step / step time
     step_hbm_k = decide_hbm_bytes(wl, st_all, K) + move_hbm_bytes(wl, st_all, K)
     host_k = st_all[2] * ROW / K
@@ -399,6 +424,15 @@ def main():
     hev.destroy_graph()
     hev.close()
     dev.close()
+    if args.calibrate_copy:
+        # a plain copy kernel of known size: 256 MiB read + 256 MiB written
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
