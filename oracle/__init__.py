@@ -19,7 +19,9 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "hisparse_oracle.cpp")
-LIB = os.path.join(HERE, "libhisparse_oracle.so")
+# HS_ORACLE_LIB points the wrapper at another build of the oracle source: the
+# mutation tests use it to check that the pins catch planted mistakes.
+LIB = os.environ.get("HS_ORACLE_LIB") or os.path.join(HERE, "libhisparse_oracle.so")
 
 PAGE = 64
 ROW_BYTES = 656
