@@ -57,97 +57,6 @@ def parse():
     return ap.parse_args()
 
 
-class HipEvents:
-    """Raw HIP timing events (ctypes on the HIP runtime): they can be recorded
-    inside a captured graph as external event nodes, so per-kernel times are
-    measured on the launch stream during a graph replay too."""
-
-    def __init__(self):
-        import ctypes
-        self.ct = ctypes
-        # the HIP runtime already mapped into this process (torch's, which the
-        # library binds to by soname): a second copy would not know torch's
-        # streams
-        paths = sorted({ln.split()[-1] for ln in open("/proc/self/maps")
-                        if "libamdhip64" in ln and ln.split()[-1].startswith("/")})
-        self.hip = ctypes.CDLL(paths[0] if paths else "libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        # the runtime exports several versions of this symbol; the external
-        # event node of stream capture needs the hip_6.4 one
-        libc = ctypes.CDLL("libc.so.6")
-        libc.dlvsym.restype = ctypes.c_void_p
-        libc.dlvsym.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_char_p]
-        addr = libc.dlvsym(self.hip._handle, b"hipEventRecordWithFlags", b"hip_6.4")
-        proto = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint)
-        self.record_fn = proto(addr) if addr else self.hip.hipEventRecordWithFlags
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
-                                                 ctypes.c_void_p, ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.made = []
-
-    def new(self):
-        e = self.ct.c_void_p()
-        if self.hip.hipEventCreate(self.ct.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
-        self.made.append(e)
-        return e
-
-    def record(self, e, stream, external):
-        if self.record_fn(e, self.ct.c_void_p(stream), 1 if external else 0) != 0:
-            raise RuntimeError("hipEventRecordWithFlags failed")
-
-    def elapsed_ms(self, a, b):
-        ms = self.ct.c_float()
-        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return ms.value
-
-    def close(self):
-        for e in self.made:
-            self.hip.hipEventDestroy(e)
-        self.made = []
-
-    # -- stream capture into a HIP graph (relaxed mode), replay ----------
-    def begin_capture(self, stream):
-        ct = self.ct
-        self.hip.hipStreamBeginCapture.argtypes = [ct.c_void_p, ct.c_int]
-        if self.hip.hipStreamBeginCapture(ct.c_void_p(stream), 2) != 0:  # relaxed
-            raise RuntimeError("hipStreamBeginCapture failed")
-
-    def end_capture(self, stream):
-        ct = self.ct
-        g, ge = ct.c_void_p(), ct.c_void_p()
-        self.hip.hipStreamEndCapture.argtypes = [ct.c_void_p, ct.POINTER(ct.c_void_p)]
-        self.hip.hipGraphInstantiate.argtypes = [ct.POINTER(ct.c_void_p), ct.c_void_p,
-                                                 ct.c_void_p, ct.c_void_p, ct.c_size_t]
-        if self.hip.hipStreamEndCapture(ct.c_void_p(stream), ct.byref(g)) != 0:
-            raise RuntimeError("hipStreamEndCapture failed")
-        if self.hip.hipGraphInstantiate(ct.byref(ge), g, None, None, 0) != 0:
-            raise RuntimeError("hipGraphInstantiate failed")
-        self.graph, self.exec = g, ge
-
-    def launch(self, stream):
-        self.hip.hipGraphLaunch.argtypes = [self.ct.c_void_p, self.ct.c_void_p]
-        if self.hip.hipGraphLaunch(self.exec, self.ct.c_void_p(stream)) != 0:
-            raise RuntimeError("hipGraphLaunch failed")
-
-    def destroy_graph(self):
-        self.hip.hipGraphExecDestroy.argtypes = [self.ct.c_void_p]
-        self.hip.hipGraphDestroy.argtypes = [self.ct.c_void_p]
-        if getattr(self, "exec", None):
-            self.hip.hipGraphExecDestroy(self.exec)
-            self.hip.hipGraphDestroy(self.graph)
-            self.exec = None
-
-    def memcpy_h2d(self, dst, src, nbytes, stream):
-        ct = self.ct
-        self.hip.hipMemcpyAsync.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_size_t, ct.c_int,
-                                            ct.c_void_p]
-        if self.hip.hipMemcpyAsync(ct.c_void_p(dst), ct.c_void_p(src), nbytes, 1,
-                                   ct.c_void_p(stream)) != 0:
-            raise RuntimeError("hipMemcpyAsync failed")
-
-
 def build_workload(name: str, n_steps: int):
     import hs_gen
     if name == "mixed_decode":
@@ -217,6 +126,7 @@ def main():
     import torch
 
     import serving_memory_tier_amd as hs
+    from serving_memory_tier_amd.hipgraph import HipRuntime
     from serving_memory_tier_amd.runner import DeviceRun
 
     if not os.path.exists(hs.LIB_PATH):
@@ -236,46 +146,12 @@ def main():
     n_steps = len(wl.steps)
     N = wl.P * wl.K
     entries = wl.R * wl.L * N
-    # per-step context lengths and stats records live in device memory up front
-    ctx_all = torch.from_numpy(np.stack([s.ctx for s in wl.steps]).astype(np.int32)).cuda()
+    dev.stage_steps()
     stats_all = torch.zeros((n_steps, wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
-    batches = [hs.batch_of(wl.R, wl.max_pages, dev.pool, dev.host_pool, dev.bt, dev.hbt,
-                           ctx_all[i], dev.hot, dev.tok, dev.stp) for i in range(n_steps)]
-    # the scheduler's table updates between steps (nulled pages, new host
-    # copies) as (device address, pinned source) pairs: plain 4-byte copies
-    table_sets = []
-    n_vals = sum(s.hbt_set.shape[0] + s.bt_set.shape[0] for s in wl.steps)
-    pinned_vals = torch.empty(max(1, n_vals), dtype=torch.int32, pin_memory=True)
-    k = 0
-    for s in wl.steps:
-        sets = []
-        for arr, t in ((s.hbt_set, dev.hbt), (s.bt_set, dev.bt)):
-            for r, p, v in arr:
-                pinned_vals[k] = int(v)
-                sets.append((t.data_ptr() + 4 * (int(r) * wl.max_pages + int(p)),
-                             pinned_vals.data_ptr() + 4 * k))
-                k += 1
-        table_sets.append(sets)
-    hev = HipEvents()
+    hev = HipRuntime()
 
-    def step(i, sp, ev=None, external=False):
-        for dst, srcp in table_sets[i]:
-            hev.memcpy_h2d(dst, srcp, 4, sp)
-        if ev is not None:
-            hev.record(ev[0], sp, external)
-        hs.hs_resolve_decide(dev.layout, batches[i], dev.topk[i], wl.P, wl.K, wl.steps[i].stamp,
-                             dev.rows, stats_all[i], sp)
-        if ev is not None:
-            hev.record(ev[1], sp, external)
-        hs.hs_resolve_move(dev.layout, batches[i], dev.topk[i], wl.P, wl.K, dev.rows, dev.out, sp)
-        if ev is not None:
-            hev.record(ev[2], sp, external)
-        n_off = wl.steps[i].offload.shape[0]
-        if n_off:
-            hs.hs_offload_prefix_pages(dev.layout, dev.pool, dev.host_pool, dev.pairs[i], n_off,
-                                       sp)
-            if ev is not None:
-                hev.record(ev[3], sp, external)
+    def step(i, sp, ev=None):
+        dev.launch_step(i, hev, sp, stats=stats_all[i], events=ev)
 
     sp0 = torch.cuda.current_stream().cuda_stream
     for i in range(W):
@@ -313,7 +189,7 @@ def main():
 
     # per-kernel durations: the next KE steps launched one by one, HIP events
     # on the launch stream around every kernel
-    events = [[hev.new() for _ in range(4)] for _ in range(KE)]
+    events = [[hev.new_event() for _ in range(4)] for _ in range(KE)]
     for j in range(KE):
         step(W + K + j, sp0, events[j])
     torch.cuda.synchronize()
@@ -356,10 +232,10 @@ def main():
     rep_stats = torch.zeros((wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
     for j in range(args.hit_replays):
         rep[j][0].record(stream)
-        hs.hs_resolve_decide(dev.layout, batches[last], dev.topk[last], wl.P, wl.K,
+        hs.hs_resolve_decide(dev.layout, dev.batches[last], dev.topk[last], wl.P, wl.K,
                              wl.steps[last].stamp, dev.rows, rep_stats, sp)
         rep[j][1].record(stream)
-        hs.hs_resolve_move(dev.layout, batches[last], dev.topk[last], wl.P, wl.K, dev.rows,
+        hs.hs_resolve_move(dev.layout, dev.batches[last], dev.topk[last], wl.P, wl.K, dev.rows,
                            dev.out, sp)
         rep[j][2].record(stream)
     torch.cuda.synchronize()

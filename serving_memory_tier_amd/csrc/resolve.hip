@@ -38,6 +38,8 @@
 // fixed by the sort and the scans, so repeated runs are bitwise identical.
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include "hs_internal.h"
@@ -827,13 +829,18 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
 template <int ES, int EC>
 hipError_t launch_ec(const KernelArgs& a, int grid, hipStream_t stream) {
   auto fn = resolve_kernel<ES, EC>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)kMaxLdsBytes);
+  // The dynamic-LDS limit is a per-device attribute of the function: raise
+  // it once on each device the kernel is launched on.
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_set.load(std::memory_order_acquire) & bit)) {
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
     if (err != hipSuccess) return err;
-    attr = true;
+    attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), a.plan.total, stream, a);
   return hipGetLastError();

@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 from .api import (HostPool, batch_of, hs_gather, hs_offload_prefix_pages, hs_plan_replay,
-                  hs_resolve, layout_of)
+                  hs_resolve, hs_resolve_decide, hs_resolve_move, layout_of)
 
 PAGE = 64
 ROW = 656
@@ -108,6 +108,58 @@ class DeviceRun:
         hs_plan_replay(self.layout, self.batch, self.topk[i], self.wl.P, self.wl.K, s.stamp,
                        self.rows, self.out if gather else None, self.stats,
                        self.pairs[i] if n else None, n, stream)
+
+    # -- steps with no host work between them ----------------------------------
+    def stage_steps(self) -> None:
+        """Stage every step's context lengths and table updates in device and
+        pinned memory, so that a run of steps (``launch_step``) needs no host
+        work between kernels and captures into a graph as it stands."""
+        wl = self.wl
+        n = len(wl.steps)
+        self.ctx_all = torch.from_numpy(
+            np.stack([s.ctx for s in wl.steps]).astype(np.int32)).to(self.device)
+        self.batches = [batch_of(wl.R, wl.max_pages, self.pool, self.host_pool, self.bt,
+                                 self.hbt, self.ctx_all[i], self.hot, self.tok, self.stp)
+                        for i in range(n)]
+        n_vals = sum(s.hbt_set.shape[0] + s.bt_set.shape[0] for s in wl.steps)
+        self.pinned_vals = torch.empty(max(1, n_vals), dtype=torch.int32, pin_memory=True)
+        self.table_sets = []
+        k = 0
+        for s in wl.steps:
+            sets = []
+            for arr, t in ((s.hbt_set, self.hbt), (s.bt_set, self.bt)):
+                for r, p, v in arr:
+                    self.pinned_vals[k] = int(v)
+                    sets.append((t.data_ptr() + 4 * (int(r) * wl.max_pages + int(p)),
+                                 self.pinned_vals.data_ptr() + 4 * k))
+                    k += 1
+            self.table_sets.append(sets)
+
+    def launch_step(self, i: int, hip, stream: int, stats=None, events=None) -> None:
+        """Step ``i`` on ``stream``: the scheduler's table updates as 4-byte
+        copies from pinned memory, the decide and move kernels, and the
+        offload of the pages the step completed.  ``hip`` is a HipRuntime;
+        ``events`` (optional) four events recorded around the kernels."""
+        wl = self.wl
+        s = wl.steps[i]
+        for dst, src in self.table_sets[i]:
+            hip.memcpy_h2d(dst, src, 4, stream)
+        if events is not None:
+            hip.record(events[0], stream)
+        hs_resolve_decide(self.layout, self.batches[i], self.topk[i], wl.P, wl.K, s.stamp,
+                          self.rows, self.stats if stats is None else stats, stream)
+        if events is not None:
+            hip.record(events[1], stream)
+        hs_resolve_move(self.layout, self.batches[i], self.topk[i], wl.P, wl.K, self.rows,
+                        self.out, stream)
+        if events is not None:
+            hip.record(events[2], stream)
+        n_off = s.offload.shape[0]
+        if n_off:
+            hs_offload_prefix_pages(self.layout, self.pool, self.host_pool, self.pairs[i], n_off,
+                                    stream)
+            if events is not None:
+                hip.record(events[3], stream)
 
     def close(self) -> None:
         self.host = None
