@@ -12,7 +12,7 @@ device / pinned host memory before the timed region.
 
 Prints one JSON line: resolved top-K rows/s for the whole job, plus the
 roofline of the dominant kernel (per-launch duration from HIP events on the
-launch stream, algorithmic bytes per launch), the achieved HBM and host-link
+kernel's own stream, algorithmic bytes per launch), the achieved HBM and host-link
 bandwidths, a hit-replay measurement of the HBM-bound path, and the CPU
 oracle timed on a bounded sample of the same workload.
 """
@@ -47,6 +47,9 @@ def parse():
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hit-replays", type=int, default=50)
+    ap.add_argument("--serial", action="store_true",
+                    help="time the serial stages (decide, then move with the host copies) "
+                         "instead of the overlapped hs_plan_replay")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a captured graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -68,23 +71,30 @@ def build_workload(name: str, n_steps: int):
     return hs_gen.multi_layer(turns=n_steps)
 
 
+def kernel_source_hash() -> str:
+    """First 16 hex digits of the SHA-256 over the kernel sources, in name order."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "serving_memory_tier_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
     None when it was taken on another workload or on other kernel sources."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "counters_decide_move_mixed_decode.md")
-    if workload != "mixed_decode" or not os.path.exists(path):
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
+    if not os.path.exists(path):
         return None
-    h = hashlib.sha256()
-    for f in ("resolve.hip", "copy.hip", "hs_internal.h"):
-        with open(os.path.join(ROOT, "serving_memory_tier_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
     fields = {}
     for line in open(path):
         if ":" in line and not line.startswith((" ", "#", "|")):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     v = fields.get(f"{kernel}_traffic_bytes_per_launch")
     return int(v) if v else None
@@ -103,15 +113,26 @@ def decide_hbm_bytes(wl, stats_sum, n_launches):
     return R * L * wl.C * 8 + R * L * N * 12 + (hits * 4 + misses * 12) / n_launches
 
 
-def move_hbm_bytes(wl, stats_sum, n_launches):
-    """Algorithmic HBM bytes of the row mover per launch: every entry reads its
-    row code (4 B) and writes its 656-B output row; every resident or hit entry
-    reads its 656-B row from the pool; every miss writes its row into the hot
-    slot (656 B) and its final row id (4 B) -- its read comes over the host link."""
+def fetch_bytes(wl, stats_sum, n_launches):
+    """(host-link bytes, HBM bytes) of the early fill's rows per launch: every
+    distinct miss (assigned or not) reads its 656-B row over the host link;
+    every resident or hit entry reads its 656-B row from the pool; every entry
+    writes its 656-B output row.  The fill's reads of the entries, tables and
+    slot tokens are the resolver's reads again (L2 hits in the fused launch)
+    and are counted once, in decide_hbm_bytes."""
     R, L, N = wl.R, wl.L, wl.P * wl.K
     entries = R * L * N
-    misses = stats_sum[2] / n_launches
-    return entries * (4 + ROW) + (entries - misses) * ROW + misses * (ROW + 4)
+    m = (stats_sum[2] + stats_sum[3]) / n_launches
+    return m * ROW, (entries - m) * ROW + entries * ROW
+
+
+def commit_bytes(wl, stats_sum, n_launches):
+    """HBM bytes of the commit per launch: every entry's code (4 B); per
+    assigned miss its row read from the output and written into the slot, the
+    slot's token and the final row id."""
+    R, L, N = wl.R, wl.L, wl.P * wl.K
+    a = stats_sum[2] / n_launches
+    return R * L * N * 4 + a * (2 * ROW + 8)
 
 
 def main():
@@ -150,8 +171,8 @@ def main():
     stats_all = torch.zeros((n_steps, wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
     hev = HipRuntime()
 
-    def step(i, sp, ev=None):
-        dev.launch_step(i, hev, sp, stats=stats_all[i], events=ev)
+    def step(i, sp):
+        dev.launch_step(i, hev, sp, stats=stats_all[i], serial=args.serial)
 
     sp0 = torch.cuda.current_stream().cuda_stream
     for i in range(W):
@@ -187,35 +208,34 @@ def main():
     t1 = time.perf_counter()
     wall = t1 - t0
 
-    # per-kernel durations: the next KE steps launched one by one, HIP events
-    # on the launch stream around every kernel
+    # per-kernel durations: the next KE steps launched as hs_plan_replay's
+    # stages on the launch stream (the fused resolve-and-fill launch, the
+    # commit, the offload), HIP events on that stream around every kernel
     events = [[hev.new_event() for _ in range(4)] for _ in range(KE)]
     for j in range(KE):
-        step(W + K + j, sp0, events[j])
+        dev.launch_step_timed(W + K + j, hev, sp0, events[j], stats=stats_all[W + K + j])
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
 
-    dec_ms = [hev.elapsed_ms(events[j][0], events[j][1]) for j in range(KE)]
-    mov_ms = [hev.elapsed_ms(events[j][1], events[j][2]) for j in range(KE)]
+    def mean_us(a, b, ev=events, n=KE):
+        return 1e3 * float(np.mean([hev.elapsed_ms(ev[j][a], ev[j][b]) for j in range(n)]))
+
+    fused_us, commit_us = mean_us(0, 1), mean_us(1, 2)
     off = [(j, hev.elapsed_ms(events[j][2], events[j][3])) for j in range(KE)
            if wl.steps[W + K + j].offload.shape[0]]
     st = stats_all[W + K:W + K + KE].sum(dim=(0, 1, 2)).cpu().numpy().astype(np.int64)
     st_all = stats_all[W:W + K].sum(dim=(0, 1, 2)).cpu().numpy().astype(np.int64)
-    dec_us = 1e3 * float(np.mean(dec_ms))
-    mov_us = 1e3 * float(np.mean(mov_ms))
     value = entries * K / wall
 
-    dec_bytes = decide_hbm_bytes(wl, st, KE)
-    mov_bytes = move_hbm_bytes(wl, st, KE)
-    host_bytes = st[2] * ROW / KE
+    f_host, f_hbm = fetch_bytes(wl, st, KE)
+    fused_hbm = decide_hbm_bytes(wl, st, KE) + f_hbm
+    com_bytes = commit_bytes(wl, st, KE)
     kernels = {
-        "decide": {"us": round(dec_us, 2), "hbm_bytes": int(dec_bytes),
-                   "hbm_gbps": round(dec_bytes / dec_us / 1e3, 1)},
-        "move": {"us": round(mov_us, 2), "hbm_bytes": int(mov_bytes),
-                 "hbm_gbps": round(mov_bytes / mov_us / 1e3, 1),
-                 "host_link_bytes": int(host_bytes),
-                 "host_link_gbps": round(host_bytes / mov_us / 1e3, 2)},
+        "resolve_fill": {"us": round(fused_us, 2), "host_link_bytes": int(f_host),
+                         "host_link_gbps": round(f_host / fused_us / 1e3, 2),
+                         "hbm_bytes": int(fused_hbm),
+                         "hbm_gbps": round(fused_hbm / fused_us / 1e3, 1)},
+        "commit": {"us": round(commit_us, 2), "hbm_bytes": int(com_bytes),
+                   "hbm_gbps": round(com_bytes / commit_us / 1e3, 1)},
     }
     if off:
         page_layers = [wl.steps[W + K + j].offload.shape[0] * wl.L for j, _ in off]
@@ -228,53 +248,44 @@ def main():
     # the hit-replay path: the last step's lists again with the same stamp --
     # every non-resident token hits, no host traffic, HBM-bound
     last = W + K + KE - 1
-    rep = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.hit_replays)]
+    NR = args.hit_replays
+    rep = [[hev.new_event() for _ in range(4)] for _ in range(NR)]
     rep_stats = torch.zeros((wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
-    for j in range(args.hit_replays):
-        rep[j][0].record(stream)
-        hs.hs_resolve_decide(dev.layout, dev.batches[last], dev.topk[last], wl.P, wl.K,
-                             wl.steps[last].stamp, dev.rows, rep_stats, sp)
-        rep[j][1].record(stream)
-        hs.hs_resolve_move(dev.layout, dev.batches[last], dev.topk[last], wl.P, wl.K, dev.rows,
-                           dev.out, sp)
-        rep[j][2].record(stream)
+    for j in range(NR):
+        dev.launch_step_timed(last, hev, sp0, rep[j], stats=rep_stats, offload=False)
     torch.cuda.synchronize()
     rs = rep_stats.sum(dim=(0, 1)).cpu().numpy()
-    rd_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in rep]))
-    rm_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in rep]))
-    rep_bytes = decide_hbm_bytes(wl, rs, 1) + move_hbm_bytes(wl, rs, 1)
-    hit_replay = {"decide_us": round(rd_us, 2), "move_us": round(rm_us, 2),
-                  "misses": int(rs[2]),
-                  "rows_per_s": round(entries / ((rd_us + rm_us) * 1e-6)),
-                  "hbm_gbps": round(rep_bytes / (rd_us + rm_us) / 1e3, 1),
-                  "hbm_frac": round(rep_bytes / (rd_us + rm_us) / 1e3 / HBM_PEAK_GBPS, 4),
-                  "move_hbm_gbps": round(move_hbm_bytes(wl, rs, 1) / rm_us / 1e3, 1)}
+    r_fused, r_commit = mean_us(0, 1, rep, NR), mean_us(1, 2, rep, NR)
+    r_step = mean_us(0, 2, rep, NR)
+    r_fused_bytes = decide_hbm_bytes(wl, rs, 1) + fetch_bytes(wl, rs, 1)[1]
+    rep_bytes = r_fused_bytes + commit_bytes(wl, rs, 1)
+    hit_replay = {"resolve_fill_us": round(r_fused, 2), "commit_us": round(r_commit, 2),
+                  "step_us": round(r_step, 2), "misses": int(rs[2]),
+                  "rows_per_s": round(entries / (r_step * 1e-6)),
+                  "hbm_gbps": round(rep_bytes / r_step / 1e3, 1),
+                  "hbm_frac": round(rep_bytes / r_step / 1e3 / HBM_PEAK_GBPS, 4),
+                  "resolve_fill_hbm_gbps": round(r_fused_bytes / r_fused / 1e3, 1)}
 
-    # the dominant kernel of a step and the resource that bounds it: the
-    # mover is bound by the host link when it carries misses (its HBM bytes
-    # would take a fraction of the time at HBM speed), by HBM otherwise
-    if mov_us >= dec_us:
-        host_t = host_bytes / (HOST_LINK_PEAK_GBPS * 1e3)
-        hbm_t = mov_bytes / (HBM_PEAK_GBPS * 1e3)
-        if host_t >= hbm_t:
-            ach = host_bytes / mov_us / 1e3
-            roofline = {"kernel": "move", "bound": "host_link", "achieved": round(ach, 2),
-                        "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(ach / HOST_LINK_PEAK_GBPS, 4), "traffic": None}
-        else:
-            ach = mov_bytes / mov_us / 1e3
-            roofline = {"kernel": "move", "bound": "hbm", "achieved": round(ach, 1),
-                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
+    # the dominant kernel of a step -- the fused resolve-and-fill launch -- and
+    # the resource that bounds it: the host link while it carries misses (its
+    # HBM bytes would take a fraction of the time at HBM speed), HBM otherwise
+    host_t = f_host / (HOST_LINK_PEAK_GBPS * 1e3)
+    hbm_t = fused_hbm / (HBM_PEAK_GBPS * 1e3)
+    if host_t >= hbm_t:
+        ach = f_host / fused_us / 1e3
+        roofline = {"kernel": "resolve_fill", "bound": "host_link", "achieved": round(ach, 2),
+                    "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / HOST_LINK_PEAK_GBPS, 4), "traffic": None}
     else:
-        ach = dec_bytes / dec_us / 1e3
-        roofline = {"kernel": "decide", "bound": "hbm", "achieved": round(ach, 1),
+        ach = fused_hbm / fused_us / 1e3
+        roofline = {"kernel": "resolve_fill", "bound": "hbm", "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                     "traffic": None}
     roofline["traffic"] = measured_traffic(roofline["kernel"], wl.name)
     # whole steps of the timed region: algorithmic bytes per step / step time
-    step_hbm_k = decide_hbm_bytes(wl, st_all, K) + move_hbm_bytes(wl, st_all, K)
-    host_k = st_all[2] * ROW / K
+    step_hbm_k = (decide_hbm_bytes(wl, st_all, K) + fetch_bytes(wl, st_all, K)[1] +
+                  commit_bytes(wl, st_all, K))
+    host_k = fetch_bytes(wl, st_all, K)[0]
     line = {
         "metric": METRIC, "value": round(value), "unit": "rows/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(1e3 * wall / K, 4), "higher_is_better": True,
@@ -291,8 +302,8 @@ def main():
         "per_step": {"hits": round(st_all[1] / K, 1), "misses": round(st_all[2] / K, 1),
                      "resident": round(st_all[0] / K, 1)},
         "kernels": kernels,
-        "kernel_timing": f"HIP events around each kernel over {KE} eagerly launched steps "
-                         f"following the timed ones",
+        "kernel_timing": f"HIP events on the launch stream around every kernel, over {KE} "
+                         f"steps launched as hs_plan_replay's stages after the timed ones",
         "hit_replay": hit_replay,
         "roofline": roofline,
         "cpu_baseline": None,

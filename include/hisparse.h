@@ -119,6 +119,11 @@ typedef struct {
  * counter (calling again with the same inputs and the same stamp leaves the
  * state unchanged); gather_out may be NULL, otherwise it receives the rows
  * gathered after every copy of this call (as hs_gather would).
+ * Execution: all on `stream`.  With a gather_out, one launch carries the
+ * resolver's workgroups and those of an early fill that writes every output
+ * row from the pre-call state (the misses' host rows included) while the
+ * resolver works; a short commit kernel then fills the assigned hot slots
+ * from the output.
  * Errors: HS_ERR_INVALID_ARGUMENT (null pointer, stamp 0, bad layout),
  * HS_ERR_UNSUPPORTED (K or C over the limits), HS_ERR_LAUNCH.
  */
@@ -173,30 +178,66 @@ hs_status hs_plan_replay(const hs_layout* layout, const hs_batch* batch, const i
                          int32_t n_offload, hipStream_t stream);
 
 /*
- * The two halves of hs_resolve / hs_plan_replay, for callers that time or
- * schedule them separately.  hs_resolve(...) is exactly
- *   hs_resolve_decide(layout, batch, topk, 1, top_k, stamp, row_ids, stats, s);
- *   hs_resolve_move(layout, batch, topk, 1, top_k, row_ids, gather_out, s);
- * and hs_plan_replay the same with num_pos positions followed by
- * hs_offload_prefix_pages.  decide runs one workgroup per request-layer:
- * it classifies, finds hits and victims and commits the hot-buffer state;
- * row_ids then hold final rows except for assigned misses, which hold the
- * code -(8 + 2 * slot + c) (c = 1 on exactly one entry per missed token).
+ * The stages of hs_resolve / hs_plan_replay, for callers that time or
+ * schedule them on their own streams.
+ *
+ * Serial form (what the calls do without a gather output):
+ *   hs_resolve_decide(layout, batch, topk, P, K, stamp, row_ids, NULL, stats, s);
+ *   hs_resolve_move(layout, batch, topk, P, K, row_ids, gather_out, s);
+ * Overlapped form (what the calls do with one):
+ *   hs_resolve_decide(layout, batch, topk, P, K, stamp, row_ids, gather_out, stats, s);
+ *   hs_resolve_commit(layout, batch, topk, P, K, row_ids, gather_out, s);
+ * or, scheduled by the caller on two streams:
+ *   s2: hs_resolve_decide(..., NULL, stats, s2);
+ *   s:  hs_resolve_fetch(layout, batch, topk, P, K, gather_out, s);
+ *       <wait for decide>  hs_resolve_commit(layout, batch, topk, P, K, row_ids,
+ *                                            gather_out, s);
+ * fetch and decide must start after every earlier change to the batch's
+ * state, tables and pools, and both finish before commit; they may overlap.
+ *
+ * decide runs one workgroup per request-layer: it classifies, finds hits and
+ * victims and writes the stamps; row_ids then hold final rows except for the
+ * misses: -(8 + 2 * slot + c) for a miss assigned to a slot (c = 1 on the
+ * token's first entry, which fills the slot) and -2 for a miss left without
+ * one.  The victims' new tokens are recorded by the entry that fills the
+ * slot, in move (serial) or commit (overlapped), so slot_token still holds
+ * the pre-call tokens until then.  With a gather_out, the same launch also
+ * carries fetch's workgroups.
  * move runs on the whole chip: it copies each missed row from the host pool
  * into its slot, gathers every row into gather_out (NULL: copies only) and
- * replaces the codes by the slots' row ids.  Until move has run on the same
- * stream, the hot slots of the misses do not yet hold their rows.
- * Errors: as hs_resolve.
+ * replaces the codes by the slots' row ids.
+ * fetch writes every entry's row of gather_out from the pre-call state, as
+ * decide classifies it: resident and hot rows from kv_pool, a miss's row from
+ * the host pool (read once per distinct token), zero rows otherwise -- a
+ * miss left without a slot included, until commit.  It writes nothing else.
+ * commit copies each assigned miss's row from gather_out into its slot,
+ * records the slot's token, replaces the codes by row ids, and zeroes the
+ * rows of misses left without a slot.
+ * Until the last stage has run, the hot slots of the misses do not hold
+ * their rows.  Errors: as hs_resolve; fetch and commit need a gather_out
+ * (HS_ERR_INVALID_ARGUMENT).
  */
 hs_status hs_resolve_decide(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
                             int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
-                            int32_t* stats, hipStream_t stream);
+                            uint8_t* gather_out, int32_t* stats, hipStream_t stream);
+hs_status hs_resolve_fetch(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                           int32_t num_pos, int32_t top_k, uint8_t* gather_out,
+                           hipStream_t stream);
 hs_status hs_resolve_move(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
                           int32_t num_pos, int32_t top_k, int32_t* row_ids, uint8_t* gather_out,
                           hipStream_t stream);
+hs_status hs_resolve_commit(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                            int32_t num_pos, int32_t top_k, int32_t* row_ids,
+                            uint8_t* gather_out, hipStream_t stream);
 
 /* A static English description of a status code. */
 const char* hs_status_string(hs_status status);
+
+/* The HIP runtime failure behind the last HS_ERR_LAUNCH or HS_ERR_HIP
+ * returned on the calling thread: "<what>: <hipError name> (<code>)", or ""
+ * if there was none.  The text is owned by the library and stays valid
+ * until the thread's next failing call. */
+const char* hs_last_error(void);
 
 /* Pinned host memory for the host pool, mapped into the device address space.
  * *host_ptr is the host address; hs_host_device_pointer gives the address

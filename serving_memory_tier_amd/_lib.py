@@ -17,8 +17,9 @@ HS_MAX_ENTRIES = 8192
 HS_MAX_HOT_CAPACITY = 8192
 
 EXPORTS = ("hs_resolve", "hs_gather", "hs_offload_prefix_pages", "hs_plan_replay",
-           "hs_resolve_decide", "hs_resolve_move", "hs_status_string", "hs_host_alloc",
-           "hs_host_free", "hs_host_device_pointer")
+           "hs_resolve_decide", "hs_resolve_fetch", "hs_resolve_move", "hs_resolve_commit",
+           "hs_status_string", "hs_last_error", "hs_host_alloc", "hs_host_free",
+           "hs_host_device_pointer")
 
 
 class HsError(RuntimeError):
@@ -59,16 +60,20 @@ def lib():
         L.hs_gather.argtypes = [lay, vp, vp, i32, i32, vp, vp]
         L.hs_offload_prefix_pages.argtypes = [lay, vp, vp, vp, i32, vp]
         L.hs_plan_replay.argtypes = [lay, bat, vp, i32, i32, u32, vp, vp, vp, vp, i32, vp]
-        L.hs_resolve_decide.argtypes = [lay, bat, vp, i32, i32, u32, vp, vp, vp]
+        L.hs_resolve_decide.argtypes = [lay, bat, vp, i32, i32, u32, vp, vp, vp, vp]
+        L.hs_resolve_fetch.argtypes = [lay, bat, vp, i32, i32, vp, vp]
         L.hs_resolve_move.argtypes = [lay, bat, vp, i32, i32, vp, vp, vp]
+        L.hs_resolve_commit.argtypes = [lay, bat, vp, i32, i32, vp, vp, vp]
         L.hs_status_string.argtypes = [i32]
         L.hs_status_string.restype = ctypes.c_char_p
+        L.hs_last_error.argtypes = []
+        L.hs_last_error.restype = ctypes.c_char_p
         L.hs_host_alloc.argtypes = [sz, ctypes.POINTER(vp)]
         L.hs_host_free.argtypes = [vp]
         L.hs_host_device_pointer.argtypes = [vp, ctypes.POINTER(vp)]
-        for name in ("hs_resolve", "hs_gather", "hs_offload_prefix_pages", "hs_plan_replay",
-                     "hs_resolve_decide", "hs_resolve_move", "hs_host_alloc", "hs_host_free",
-                     "hs_host_device_pointer"):
+        for name in EXPORTS:
+            if name in ("hs_status_string", "hs_last_error"):
+                continue
             getattr(L, name).restype = i32
         _lib = L
     return _lib

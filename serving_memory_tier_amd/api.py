@@ -37,7 +37,9 @@ def _stream(stream) -> int:
 
 def _check(status: int, what: str) -> None:
     if status != HS_OK:
-        raise HsError(status, f"{what} failed ({hs_status_string(status)})")
+        detail = lib().hs_last_error().decode() if status in (3, 4) else ""
+        raise HsError(status, f"{what} failed ({hs_status_string(status)}"
+                              f"{'; ' + detail if detail else ''})")
 
 
 def hs_status_string(status: int) -> str:
@@ -79,10 +81,16 @@ def hs_plan_replay(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: 
 
 
 def hs_resolve_decide(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: int,
-                      stamp: int, row_ids, stats, stream=None) -> None:
+                      stamp: int, row_ids, gather_out, stats, stream=None) -> None:
     _check(lib().hs_resolve_decide(ctypes.byref(layout), ctypes.byref(batch), _ptr(topk), num_pos,
-                                   top_k, ctypes.c_uint32(stamp), _ptr(row_ids), _ptr(stats),
-                                   _stream(stream)), "hs_resolve_decide")
+                                   top_k, ctypes.c_uint32(stamp), _ptr(row_ids), _ptr(gather_out),
+                                   _ptr(stats), _stream(stream)), "hs_resolve_decide")
+
+
+def hs_resolve_fetch(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: int,
+                     gather_out, stream=None) -> None:
+    _check(lib().hs_resolve_fetch(ctypes.byref(layout), ctypes.byref(batch), _ptr(topk), num_pos,
+                                  top_k, _ptr(gather_out), _stream(stream)), "hs_resolve_fetch")
 
 
 def hs_resolve_move(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: int, row_ids,
@@ -90,6 +98,13 @@ def hs_resolve_move(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k:
     _check(lib().hs_resolve_move(ctypes.byref(layout), ctypes.byref(batch), _ptr(topk), num_pos,
                                  top_k, _ptr(row_ids), _ptr(gather_out), _stream(stream)),
            "hs_resolve_move")
+
+
+def hs_resolve_commit(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: int, row_ids,
+                      gather_out, stream=None) -> None:
+    _check(lib().hs_resolve_commit(ctypes.byref(layout), ctypes.byref(batch), _ptr(topk),
+                                   num_pos, top_k, _ptr(row_ids), _ptr(gather_out),
+                                   _stream(stream)), "hs_resolve_commit")
 
 
 def hs_gather(layout: HsLayout, kv_pool, row_ids, num_reqs: int, rows_per_req_layer: int, out,

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdio>
+
 #include "hisparse.h"
 #include "hs_internal.h"
 
@@ -45,7 +47,25 @@ hs_status check_hot(const hs_layout* lay) {
   return HS_OK;
 }
 
-hs_status from_hip(hipError_t e) { return e == hipSuccess ? HS_OK : HS_ERR_LAUNCH; }
+// The last HIP failure on this thread, for hs_last_error.
+thread_local char g_last_error[160] = "";
+
+void note(const char* what, hipError_t e) {
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorName(e), (int)e);
+}
+
+hs_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return HS_OK;
+  note(what, e);
+  return HS_ERR_LAUNCH;
+}
+
+// A HIP runtime call other than a launch.
+bool hip_ok(hipError_t e, const char* what) {
+  if (e == hipSuccess) return true;
+  note(what, e);
+  return false;
+}
 
 hs_status check_gather(const hs_layout* lay, int64_t n_rl, int64_t rows_per_rl) {
   (void)lay;
@@ -116,9 +136,12 @@ hs_status check_resolve(const hs_layout* lay, const hs_batch* b, const int32_t* 
   return HS_OK;
 }
 
+hs::FetchParams fetch_params(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
+                             int32_t N, uint8_t* gather_out);
+
 hs_status launch_decide(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
                         int32_t N, uint32_t stamp, int32_t* row_ids, int32_t* stats,
-                        hipStream_t stream) {
+                        hipStream_t stream, uint8_t* fill_out = nullptr) {
   if ((int64_t)b->num_reqs * lay->num_layers == 0) return HS_OK;
   hs::ResolveParams p;
   p.page_shift = log2i(lay->page_size);
@@ -144,12 +167,16 @@ hs_status launch_decide(const hs_layout* lay, const hs_batch* b, const int32_t* 
   p.stamp = stamp;
   p.row_ids = row_ids;
   p.stats = stats;
-  return from_hip(hs::launch_resolve(p, stream));
+  if (fill_out) {
+    const hs::FetchParams f = fetch_params(lay, b, topk, N, fill_out);
+    return from_hip(hs::launch_resolve(p, &f, stream), "resolver launch");
+  }
+  return from_hip(hs::launch_resolve(p, nullptr, stream), "resolver launch");
 }
 
-hs_status launch_fused_move(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
-                            int32_t N, int32_t* row_ids, uint8_t* gather_out,
-                            hipStream_t stream) {
+hs_status launch_move_mode(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
+                           int32_t N, int32_t* row_ids, uint8_t* gather_out, hs::MoveMode mode,
+                           hipStream_t stream) {
   if ((int64_t)b->num_reqs * lay->num_layers == 0) return HS_OK;
   hs::MoveParams g = move_params(lay, b->kv_pool, row_ids, b->num_reqs, N, gather_out);
   g.pool_w = b->kv_pool;
@@ -160,12 +187,55 @@ hs_status launch_fused_move(const hs_layout* lay, const hs_batch* b, const int32
   g.topk = topk;
   g.host_block_table = b->host_block_table;
   g.hot_blocks = b->hot_blocks;
-  return from_hip(hs::launch_move(g, true, stream));
+  g.slot_token = b->slot_token;
+  return from_hip(hs::launch_move(g, mode, stream), "row mover launch");
 }
 
-// Shared body of hs_resolve and hs_plan_replay: decisions, then the misses'
-// host-link copies and the gather on the whole chip, then the offload -- all
-// on the caller's stream.
+hs::FetchParams fetch_params(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
+                             int32_t N, uint8_t* gather_out) {
+  hs::FetchParams f{};
+  f.page_shift = log2i(lay->page_size);
+  f.row_bytes = lay->row_bytes;
+  f.num_layers = lay->num_layers;
+  f.hot_capacity = lay->hot_capacity;
+  f.pool_rows = lay->pool_rows;
+  f.host_rows = lay->host_rows;
+  f.pool_stride = lay->pool_layer_stride;
+  f.host_stride = lay->host_layer_stride;
+  f.num_reqs = b->num_reqs;
+  f.max_pages = b->max_pages;
+  f.pool = b->kv_pool;
+  f.host = b->host_pool;
+  f.block_table = b->block_table;
+  f.host_block_table = b->host_block_table;
+  f.ctx_len = b->ctx_len;
+  f.hot_blocks = b->hot_blocks;
+  f.slot_token = b->slot_token;
+  f.topk = topk;
+  f.entries = N;
+  f.out = gather_out;
+  return f;
+}
+
+hs_status launch_fetch(const hs_layout* lay, const hs_batch* b, const int32_t* topk, int32_t N,
+                       uint8_t* gather_out, hipStream_t stream) {
+  if ((int64_t)b->num_reqs * lay->num_layers == 0) return HS_OK;
+  return from_hip(hs::launch_fetch(fetch_params(lay, b, topk, N, gather_out), stream),
+                  "prefetch launch");
+}
+
+bool fetch_fits(const hs_layout* lay, int32_t N) {
+  return hs::fetch_lds_bytes(N, lay->hot_capacity) <= hs::kMaxLdsBytes;
+}
+
+// Shared body of hs_resolve and hs_plan_replay, on the caller's stream.
+//
+// With a gather output: one launch holds the resolver's workgroups and the
+// early fill's (every output row, the misses' host-link reads included,
+// written from the pre-call state); then the commit fills the assigned hot
+// slots from the output.  Without one: the resolver, then the misses'
+// copies into their slots.  The offload of completed prefix pages comes
+// last.
 hs_status resolve_common(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
                          int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
                          uint8_t* gather_out, int32_t* stats, const int32_t* offload_pairs,
@@ -177,12 +247,20 @@ hs_status resolve_common(const hs_layout* lay, const hs_batch* b, const int32_t*
   if (n_offload > 0 && (!offload_pairs || !b->kv_pool || !b->host_pool))
     return HS_ERR_INVALID_ARGUMENT;
   const int32_t N = num_pos * top_k;
-  if ((s = launch_decide(lay, b, topk, N, stamp, row_ids, stats, stream)) != HS_OK) return s;
-  if ((s = launch_fused_move(lay, b, topk, N, row_ids, gather_out, stream)) != HS_OK) return s;
+  if (gather_out && fetch_fits(lay, N)) {
+    s = launch_decide(lay, b, topk, N, stamp, row_ids, stats, stream, gather_out);
+    if (s != HS_OK) return s;
+    s = launch_move_mode(lay, b, topk, N, row_ids, gather_out, hs::kMoveCommit, stream);
+    if (s != HS_OK) return s;
+  } else {
+    if ((s = launch_decide(lay, b, topk, N, stamp, row_ids, stats, stream)) != HS_OK) return s;
+    s = launch_move_mode(lay, b, topk, N, row_ids, gather_out, hs::kMoveFused, stream);
+    if (s != HS_OK) return s;
+  }
   if (n_offload > 0) {
     hs::OffloadParams o = offload_params(lay, b->kv_pool, const_cast<uint8_t*>(b->host_pool),
                                          offload_pairs, n_offload);
-    if ((s = from_hip(hs::launch_offload(o, stream))) != HS_OK) return s;
+    if ((s = from_hip(hs::launch_offload(o, stream), "offload launch")) != HS_OK) return s;
   }
   return HS_OK;
 }
@@ -208,11 +286,23 @@ hs_status hs_plan_replay(const hs_layout* layout, const hs_batch* batch, const i
 
 hs_status hs_resolve_decide(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
                             int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
-                            int32_t* stats, hipStream_t stream) {
+                            uint8_t* gather_out, int32_t* stats, hipStream_t stream) {
   hs_status s = check_resolve(layout, batch, topk, num_pos, top_k, row_ids);
   if (s != HS_OK) return s;
   if (!stats || stamp == 0) return HS_ERR_INVALID_ARGUMENT;
-  return launch_decide(layout, batch, topk, num_pos * top_k, stamp, row_ids, stats, stream);
+  const int32_t N = num_pos * top_k;
+  if (gather_out && !fetch_fits(layout, N)) return HS_ERR_UNSUPPORTED;
+  return launch_decide(layout, batch, topk, N, stamp, row_ids, stats, stream, gather_out);
+}
+
+hs_status hs_resolve_fetch(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                           int32_t num_pos, int32_t top_k, uint8_t* gather_out,
+                           hipStream_t stream) {
+  hs_status s = check_resolve(layout, batch, topk, num_pos, top_k, topk);
+  if (s != HS_OK) return s;
+  if (!gather_out) return HS_ERR_INVALID_ARGUMENT;
+  if (!fetch_fits(layout, num_pos * top_k)) return HS_ERR_UNSUPPORTED;
+  return launch_fetch(layout, batch, topk, num_pos * top_k, gather_out, stream);
 }
 
 hs_status hs_resolve_move(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
@@ -220,7 +310,18 @@ hs_status hs_resolve_move(const hs_layout* layout, const hs_batch* batch, const 
                           hipStream_t stream) {
   hs_status s = check_resolve(layout, batch, topk, num_pos, top_k, row_ids);
   if (s != HS_OK) return s;
-  return launch_fused_move(layout, batch, topk, num_pos * top_k, row_ids, gather_out, stream);
+  return launch_move_mode(layout, batch, topk, num_pos * top_k, row_ids, gather_out,
+                          hs::kMoveFused, stream);
+}
+
+hs_status hs_resolve_commit(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                            int32_t num_pos, int32_t top_k, int32_t* row_ids,
+                            uint8_t* gather_out, hipStream_t stream) {
+  hs_status s = check_resolve(layout, batch, topk, num_pos, top_k, row_ids);
+  if (s != HS_OK) return s;
+  if (!gather_out) return HS_ERR_INVALID_ARGUMENT;
+  return launch_move_mode(layout, batch, topk, num_pos * top_k, row_ids, gather_out,
+                          hs::kMoveCommit, stream);
 }
 
 hs_status hs_gather(const hs_layout* layout, const uint8_t* kv_pool, const int32_t* row_ids,
@@ -236,7 +337,7 @@ hs_status hs_gather(const hs_layout* layout, const uint8_t* kv_pool, const int32
   return from_hip(hs::launch_move(
       move_params(layout, kv_pool, const_cast<int32_t*>(row_ids), num_reqs, rows_per_req_layer,
                   out),
-      false, stream));
+      hs::kMoveGather, stream), "gather launch");
 }
 
 hs_status hs_offload_prefix_pages(const hs_layout* layout, const uint8_t* kv_pool,
@@ -247,8 +348,11 @@ hs_status hs_offload_prefix_pages(const hs_layout* layout, const uint8_t* kv_poo
   if ((s = check_offload(n)) != HS_OK) return s;
   if (n == 0) return HS_OK;
   if (!kv_pool || !host_pool || !pairs) return HS_ERR_INVALID_ARGUMENT;
-  return from_hip(hs::launch_offload(offload_params(layout, kv_pool, host_pool, pairs, n), stream));
+  return from_hip(hs::launch_offload(offload_params(layout, kv_pool, host_pool, pairs, n), stream),
+                  "offload launch");
 }
+
+const char* hs_last_error(void) { return g_last_error; }
 
 const char* hs_status_string(hs_status status) {
   switch (status) {

@@ -33,8 +33,9 @@ constexpr int kU = kCopyUnroll;
 constexpr int kWavesPerBlock = kT / 64;
 constexpr int kEPW = kMoveEntriesPerWave;
 
-// PIECES = row_bytes / 16 when known at compile time (0 = runtime).
-template <int PIECES, bool FUSED>
+// PIECES = row_bytes / 16 when known at compile time (0 = runtime); MODE is
+// a MoveMode.
+template <int PIECES, int MODE>
 __global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_per_rl,
                                                   int32_t total_chunks) {
   const int lane = threadIdx.x & 63;
@@ -53,39 +54,48 @@ __global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_p
   int32_t* rows = p.row_ids + (int64_t)rl * N + e0;
   const uint8_t* pool_l = p.pool + (int64_t)layer * p.pool_stride;
   uint8_t* out = p.out ? p.out + ((int64_t)rl * N + e0) * p.row_bytes : nullptr;
+  constexpr bool kSlots = MODE == kMoveFused;
 
   const int32_t* topk = nullptr;
   const int32_t* hbt = nullptr;
   const int32_t* hot = nullptr;
   const uint8_t* host_l = nullptr;
   uint8_t* slot_l = nullptr;
+  int32_t* stok = nullptr;
   int64_t host_blocks = 0;
-  if (FUSED) {
+  if (kSlots) {
     topk = p.topk + (int64_t)rl * N + e0;
-    hbt = p.host_block_table + (int64_t)r * p.max_pages;
     hot = p.hot_blocks + (int64_t)r * (p.hot_capacity >> ps);
-    host_l = p.host + (int64_t)layer * p.host_stride;
     slot_l = p.pool_w + (int64_t)layer * p.pool_stride;
+    stok = p.slot_token + (int64_t)rl * p.hot_capacity;
+  }
+  if (MODE == kMoveFused) {
+    hbt = p.host_block_table + (int64_t)r * p.max_pages;
+    host_l = p.host + (int64_t)layer * p.host_stride;
     host_blocks = p.host_rows >> ps;
   }
 
   for (int32_t base = 0; base < npieces; base += 64 * kU) {
     u32x4 v[kU];
     uint8_t* slot_dst[kU];
+    bool st[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int32_t g = base + u * 64 + lane;
       v[u] = u32x4{0u, 0u, 0u, 0u};
       slot_dst[u] = nullptr;
+      st[u] = false;
       if (g < npieces) {
         const int32_t el = g / pieces;
         const int32_t pc = g - el * pieces;
         const int32_t code = rows[el];
         if (code >= 0) {
+          st[u] = out != nullptr;
           if (out && code < p.pool_rows)
             v[u] = *reinterpret_cast<const u32x4*>(pool_l + (int64_t)code * p.row_bytes +
                                                    pc * 16);
-        } else if (FUSED && code <= -8) {
+        } else if (MODE == kMoveFused && code <= -8) {
+          st[u] = out != nullptr;
           const int32_t q = (-code - 8) >> 1;
           const bool copier = ((-code - 8) & 1) != 0;
           if (out || copier) {
@@ -103,27 +113,120 @@ __global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_p
               }
             }
           }
+        } else {
+          st[u] = out != nullptr;  // zero row
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int32_t g = base + u * 64 + lane;
-      if (g < npieces) {
-        if (out)
-          __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + (int64_t)g * 16));
-        if (FUSED && slot_dst[u]) *reinterpret_cast<u32x4*>(slot_dst[u]) = v[u];
-      }
+      if (st[u])
+        __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + (int64_t)g * 16));
+      if (kSlots && slot_dst[u]) *reinterpret_cast<u32x4*>(slot_dst[u]) = v[u];
     }
   }
-  if (FUSED && lane < ne) {
+  if (kSlots && lane < ne) {
     // only this wave reads these entries' codes, and all its reads are done
     const int32_t code = rows[lane];
     if (code <= -8) {
       const int32_t q = (-code - 8) >> 1;
-      rows[lane] = q < p.hot_capacity ? (int32_t)(((int64_t)hot[q >> ps] << ps) | (q & pm))
-                                      : -3;
+      if (q < p.hot_capacity) {
+        if ((-code - 8) & 1) stok[q] = topk[lane];
+        rows[lane] = (int32_t)(((int64_t)hot[q >> ps] << ps) | (q & pm));
+      } else {
+        rows[lane] = -3;
+      }
     }
+  }
+}
+
+// The commit after the early fill: one wave per 64 entries of a
+// request-layer.  Entries holding a first-entry code copy their output row
+// into the assigned slot and record the slot's token; every code becomes the
+// slot's row id; misses left without a slot get a zero row.  Only those rows
+// are touched, so the work is proportional to the misses.
+template <int PIECES>
+__global__ void __launch_bounds__(kT) commit_kernel(MoveParams p, int32_t chunks_per_rl,
+                                                    int32_t total_chunks) {
+  __shared__ int32_t work_e[kWavesPerBlock][64];    // entry; -1 - entry for a zero row
+  __shared__ int32_t work_row[kWavesPerBlock][64];  // the slot's pool row
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int32_t c = blockIdx.x * kWavesPerBlock + wv;
+  if (c >= total_chunks) return;  // the whole wave leaves together
+  const int32_t rl = c / chunks_per_rl;
+  const int32_t e0 = (c - rl * chunks_per_rl) * 64;
+  const int32_t N = p.rows_per_rl;
+  const int32_t ne = min(64, N - e0);
+  const int32_t r = rl / p.num_layers;
+  const int32_t layer = rl - r * p.num_layers;
+  const int32_t pieces = PIECES > 0 ? PIECES : (p.row_bytes >> 4);
+  const int ps = p.page_shift;
+  const int32_t pm = (1 << ps) - 1;
+  int32_t* rows = p.row_ids + (int64_t)rl * N + e0;
+  uint8_t* out = p.out + ((int64_t)rl * N + e0) * p.row_bytes;
+  const int32_t* topk = p.topk + (int64_t)rl * N + e0;
+  const int32_t* hot = p.hot_blocks + (int64_t)r * (p.hot_capacity >> ps);
+  uint8_t* slot_l = p.pool_w + (int64_t)layer * p.pool_stride;
+  int32_t* stok = p.slot_token + (int64_t)rl * p.hot_capacity;
+
+  const int32_t code = lane < ne ? rows[lane] : 0;
+  int32_t drow = -1;  // the slot's pool row, for a first entry
+  bool copier = false;
+  if (code <= -8) {
+    const int32_t q = (-code - 8) >> 1;
+    if (q < p.hot_capacity) {
+      const int32_t hblk = hot[q >> ps];
+      const int32_t row = (hblk << ps) | (q & pm);
+      copier = ((-code - 8) & 1) != 0 && hblk >= 0 && hblk < (p.pool_rows >> ps);
+      if (copier) {
+        drow = row;
+        stok[q] = topk[lane];
+      }
+      rows[lane] = row;
+    } else {
+      rows[lane] = -3;
+    }
+  }
+  const bool zero = code == -2;
+  const uint64_t m = __ballot(copier || zero);
+  if (m == 0) return;
+  if (copier || zero) {
+    const int32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    work_e[wv][rank] = zero ? -1 - lane : lane;
+    work_row[wv][rank] = drow;
+  }
+  // the work lists are written and read by this wave only
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const int32_t n = __popcll(m);
+  const int32_t total = n * pieces;
+  const int64_t dst_stride = p.row_bytes;
+  for (int32_t g0 = 0; g0 < total; g0 += 64 * kU) {
+    u32x4 v[kU];
+    uint8_t* dst[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t g = g0 + u * 64 + lane;
+      dst[u] = nullptr;
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (g < total) {
+        const int32_t j = g / pieces;
+        const int32_t pc = g - j * pieces;
+        const int32_t w = work_e[wv][j];
+        if (w < 0) {
+          dst[u] = out + (int64_t)(-1 - w) * dst_stride + pc * 16;
+        } else {
+          v[u] = *reinterpret_cast<const u32x4*>(out + (int64_t)w * dst_stride + pc * 16);
+          dst[u] = slot_l + (int64_t)work_row[wv][j] * dst_stride + pc * 16;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = v[u];
   }
 }
 
@@ -153,36 +256,42 @@ __global__ void __launch_bounds__(kT) offload_kernel(OffloadParams p) {
 }
 
 template <int PIECES>
-void launch_move_pieces(const MoveParams& p, bool fused, int32_t chunks_per_rl, int32_t total,
-                        uint32_t grid, hipStream_t stream) {
-  if (fused)
-    hipLaunchKernelGGL((move_kernel<PIECES, true>), dim3(grid), dim3(kT), 0, stream, p,
-                       chunks_per_rl, total);
-  else
-    hipLaunchKernelGGL((move_kernel<PIECES, false>), dim3(grid), dim3(kT), 0, stream, p,
-                       chunks_per_rl, total);
+hipError_t launch_move_pieces(const MoveParams& p, MoveMode mode, int32_t chunks_per_rl,
+                              int32_t total, uint32_t grid, hipStream_t stream) {
+  void (*fn)(MoveParams, int32_t, int32_t) = nullptr;
+  switch (mode) {
+    case kMoveGather: fn = move_kernel<PIECES, kMoveGather>; break;
+    case kMoveFused: fn = move_kernel<PIECES, kMoveFused>; break;
+    case kMoveCommit: break;  // commit_kernel
+  }
+  if (!fn) return hipErrorInvalidValue;
+  return launch_kernel(fn, dim3(grid), dim3(kT), 0, stream, p, chunks_per_rl, total);
 }
 
 }  // namespace
 
-hipError_t launch_move(const MoveParams& p, bool fused, hipStream_t stream) {
+hipError_t launch_move(const MoveParams& p, MoveMode mode, hipStream_t stream) {
   const int64_t n_rl = (int64_t)p.num_reqs * p.num_layers;
   if (n_rl == 0 || p.rows_per_rl == 0) return hipSuccess;
+  if (mode == kMoveCommit) {
+    const int32_t cpr = (p.rows_per_rl + 63) / 64;
+    const int64_t total = n_rl * cpr;
+    const uint32_t grid = (uint32_t)((total + kWavesPerBlock - 1) / kWavesPerBlock);
+    auto fn = p.row_bytes == 656 ? commit_kernel<41> : commit_kernel<0>;
+    return launch_kernel(fn, dim3(grid), dim3(kT), 0, stream, p, cpr, (int32_t)total);
+  }
   const int32_t chunks_per_rl = (p.rows_per_rl + kEPW - 1) / kEPW;
   const int64_t total = n_rl * chunks_per_rl;
   const uint32_t grid = (uint32_t)((total + kWavesPerBlock - 1) / kWavesPerBlock);
   if (p.row_bytes == 656)
-    launch_move_pieces<41>(p, fused, chunks_per_rl, (int32_t)total, grid, stream);
-  else
-    launch_move_pieces<0>(p, fused, chunks_per_rl, (int32_t)total, grid, stream);
-  return hipGetLastError();
+    return launch_move_pieces<41>(p, mode, chunks_per_rl, (int32_t)total, grid, stream);
+  return launch_move_pieces<0>(p, mode, chunks_per_rl, (int32_t)total, grid, stream);
 }
 
 hipError_t launch_offload(const OffloadParams& p, hipStream_t stream) {
   if (p.n == 0 || p.num_layers == 0) return hipSuccess;
-  hipLaunchKernelGGL(offload_kernel, dim3((uint32_t)p.n, (uint32_t)p.num_layers), dim3(kT), 0,
-                     stream, p);
-  return hipGetLastError();
+  return launch_kernel(offload_kernel, dim3((uint32_t)p.n, (uint32_t)p.num_layers), dim3(kT), 0,
+                       stream, p);
 }
 
 }  // namespace hs

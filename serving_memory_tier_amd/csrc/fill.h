@@ -1,0 +1,469 @@
+// Device code of the early fill (gfx950), shared by the fused resolve kernel
+// (resolve.hip: the fill's workgroups run in the same launch as the
+// resolver's) and the stand-alone fill kernel (fetch.hip).
+//
+// Method: "vLLM GLM 5.3 ... Hybrid HiSparse offloading, Part 1", section
+// "How it works": a resident token's row is read in place through the block
+// table, a hot token's from its slot, and a miss's row comes over the host
+// link from pinned host memory; the rows of a request are gathered at one
+// stride.  None of these rows depends on the LRU order: resident blocks and
+// the slots of hits are never written by the step (victims are non-hit
+// slots), and a miss's row is the host row whichever slot it gets.  So the
+// whole gather -- host-link reads included -- can start at once and run
+// while the resolver works; afterwards a short commit kernel copies each
+// assigned miss's row from the output into its slot, records the slot's
+// token, turns the codes into row ids and zeroes the rows of misses left
+// without a slot.
+//
+// Two kinds of fill workgroup classify entries the same way (an LDS map of
+// the non-resident entries' tokens that the hot buffer's slots probe gives
+// the hits; the block tables give the rest):
+//   * gather workgroups (several per request-layer, a range of entries each)
+//     write every row but the misses': resident and hot rows from the pool,
+//     zero rows for padded and invalid entries and tokens without a host copy;
+//   * miss workgroups (a fixed few for the whole launch) classify every entry
+//     of a request-layer, deduplicate the misses and read each distinct
+//     missed token's row once from the host into its first entry, then copy
+//     it to the token's later entries.  With several per request-layer,
+//     workgroup s owns the tokens t with t mod S == s.
+// Keeping the host reads to a few workgroups bounds how many are in flight:
+// the link saturates with a few tens of thousands of 16-byte reads
+// outstanding, and more only hold back the HBM reads of the rest of the
+// chip, which share the memory system's queues with them.
+//
+// Bound: the host link (PCIe 5.0 x16) while misses are in flight; HBM
+// otherwise.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hs_internal.h"
+
+// Timing hooks (per-workgroup timestamps), empty unless a profiling build
+// defines them.
+#ifndef HS_FILL_MARK
+#define HS_FILL_MARK(i)
+#endif
+
+namespace hs {
+namespace fill {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kT = kFillThreads;
+constexpr int kU = kCopyUnroll;
+
+// n / pieces for the piece counters of one row size: (n * magic) >> 32 with
+// magic = ceil(2^32 / pieces) is exact for n < 2^32 / pieces, far above any
+// piece count here (entries <= 8192, pieces <= 2^12).
+__device__ __forceinline__ int32_t pdiv(int32_t n, uint32_t magic) {
+  return (int32_t)(((uint64_t)(uint32_t)n * magic) >> 32);
+}
+
+// The token map: an open-addressing table (linear probing) over the tokens
+// of the non-resident entries.  A word holds (first entry << 16) | slot: the
+// smallest entry index holding the token -- its key is keys[entry] -- and the
+// smallest usable hot slot holding it, kNoSlot if none.  Entries are
+// inserted first (atomicMin over whole words of the same token keeps the
+// smallest entry, since the slot half is still kNoSlot); after a barrier the
+// hot buffer's slots probe the table and lower the slot half with atomicMin
+// (the entry half of a claimed word never changes).  The table holds at most
+// two thirds as many keys as words (a half or less but at the largest
+// sizes), and the slots' probes mostly end at an empty word at once.
+constexpr uint32_t kEmptyWord = 0xFFFFFFFFu;
+constexpr uint32_t kNoSlot = 0xFFFFu;
+
+__device__ __forceinline__ int32_t home(uint32_t key, int32_t n) {
+  return (int32_t)(((uint64_t)(key * 0x9E3779B1u) * (uint32_t)n) >> 32);
+}
+
+__device__ __forceinline__ int32_t next(int32_t h, int32_t n) { return h + 1 == n ? 0 : h + 1; }
+
+__device__ void map_insert(uint32_t* tab, int32_t n, const int32_t* keys, int32_t t, int32_t e) {
+  const uint32_t w = ((uint32_t)e << 16) | kNoSlot;
+  int32_t h = home((uint32_t)t, n);
+  while (true) {
+    const uint32_t old = atomicCAS(&tab[h], kEmptyWord, w);
+    if (old == kEmptyWord) return;
+    if (keys[old >> 16] == t) {
+      atomicMin(&tab[h], w);
+      return;
+    }
+    h = next(h, n);
+  }
+}
+
+// The table index holding token t, or -1.
+__device__ int32_t map_find(const uint32_t* tab, int32_t n, const int32_t* keys, int32_t t) {
+  int32_t h = home((uint32_t)t, n);
+  while (true) {
+    const uint32_t w = tab[h];
+    if (w == kEmptyWord) return -1;
+    if (keys[w >> 16] == t) return h;
+    h = next(h, n);
+  }
+}
+
+// The hot buffer's usable slots lower the slot half of their token's word.
+// Only the slot tokens are read up front (the first kT * kScanUnroll of them
+// already at the workgroup's start, `pre`); a slot's hot block is read only
+// when its token is in the table.  Ends with a barrier.
+constexpr int kScanUnroll = 4;
+
+__device__ __forceinline__ void prefetch_slots(const FetchParams& p, int32_t rl,
+                                               int32_t (&pre)[kScanUnroll]) {
+  const int32_t C = p.hot_capacity;
+  const int32_t* stok = p.slot_token + (int64_t)rl * C;
+#pragma unroll
+  for (int u = 0; u < kScanUnroll; ++u) {
+    const int32_t q = u * kT + (int32_t)threadIdx.x;
+    pre[u] = q < C ? stok[q] : -1;
+  }
+}
+
+__device__ void scan_slots(const FetchParams& p, int32_t rl, uint32_t* tab, int32_t n,
+                           const int32_t* keys, const int32_t (&pre)[kScanUnroll]) {
+  const int tid = threadIdx.x;
+  const int32_t C = p.hot_capacity;
+  const int ps = p.page_shift;
+  const int64_t pool_blocks = p.pool_rows >> ps;
+  const int32_t r = rl / p.num_layers;
+  const int32_t* stok = p.slot_token + (int64_t)rl * C;
+  const int32_t* hot = p.hot_blocks + (int64_t)r * (C >> ps);
+  for (int32_t q0 = 0; q0 < C; q0 += kT * kScanUnroll) {
+    int32_t tq[kScanUnroll], h[kScanUnroll];
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) {
+      const int32_t q = q0 + u * kT + tid;
+      tq[u] = q0 == 0 ? pre[u] : q < C ? stok[q] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) h[u] = tq[u] >= 0 ? map_find(tab, n, keys, tq[u]) : -1;
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) {
+      if (h[u] < 0) continue;
+      const int32_t q = q0 + u * kT + tid;
+      const int32_t hb = hot[q >> ps];
+      if (hb >= 0 && hb < pool_blocks) atomicMin(&tab[h[u]], (tab[h[u]] & 0xFFFF0000u) | (uint32_t)q);
+    }
+  }
+  __syncthreads();
+}
+
+// Appends `take` lanes' items to an LDS list, one LDS atomic per wave.
+__device__ __forceinline__ int32_t wave_append(int32_t* counter, bool take) {
+  const uint64_t m = __ballot(take);
+  if (m == 0) return -1;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)m) - 1;
+  int32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, __popcll(m));
+  base = __shfl(base, leader);
+  const int32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  return take ? base + rank : -1;
+}
+
+// Row sources in LDS: >= 0 a pool row, kZeroRow a zero row, kSkip a row
+// another workgroup writes, kNoHost (before the slot scan) a non-resident
+// entry without a host copy, otherwise a non-resident entry with one whose
+// host row r is stored as r | 0x80000000 (host rows are < 2^31 - 1, so it
+// never reads as one of the markers).
+constexpr int32_t kZeroRow = -1;
+constexpr int32_t kSkip = -2;
+constexpr int32_t kNoHost = -3;
+constexpr uint32_t kHostTag = 0x80000000u;
+
+__device__ __forceinline__ bool is_host_row(int32_t v) { return v < kNoHost; }
+__device__ __forceinline__ bool non_resident(int32_t v) { return v == kNoHost || is_host_row(v); }
+
+// The request-layer's pointers and sizes.
+struct Rl {
+  int32_t N, ps, pm, pieces, ctx;
+  uint32_t magic;
+  int64_t pool_blocks, host_blocks;
+  const int32_t *topk, *bt, *hbt, *hot;
+  const uint8_t *pool_l, *host_l;
+  uint8_t* out;
+};
+
+__device__ __forceinline__ Rl rl_view(const FetchParams& p, int32_t rl) {
+  Rl v;
+  const int32_t r = rl / p.num_layers;
+  const int32_t layer = rl - r * p.num_layers;
+  v.N = p.entries;
+  v.ps = p.page_shift;
+  v.pm = (1 << v.ps) - 1;
+  v.pieces = p.row_bytes >> 4;
+  v.magic = p.piece_magic;
+  v.pool_blocks = p.pool_rows >> v.ps;
+  v.host_blocks = p.host_rows >> v.ps;
+  v.topk = p.topk + (int64_t)rl * v.N;
+  v.bt = p.block_table + (int64_t)r * p.max_pages;
+  v.hbt = p.host_block_table + (int64_t)r * p.max_pages;
+  v.hot = p.hot_blocks + (int64_t)r * (p.hot_capacity >> v.ps);
+  v.pool_l = p.pool + (int64_t)layer * p.pool_stride;
+  v.host_l = p.host + (int64_t)layer * p.host_stride;
+  v.out = p.out + (int64_t)rl * v.N * p.row_bytes;
+  v.ctx = p.ctx_len[r];
+  return v;
+}
+
+// Entries e0 + u * kT + tid (< lim): the token (-1 for padded and invalid
+// entries) and the row source before the hot-buffer lookup: a resident row,
+// kZeroRow, kNoHost or a tagged host row.  The block-table and host-table
+// loads are issued together.
+__device__ __forceinline__ void load_entries(const FetchParams& p, const Rl& v, int32_t e0,
+                                             int32_t lim, int32_t (&t)[kU], int32_t (&src)[kU]) {
+  const int tid = threadIdx.x;
+  int32_t b[kU], hb[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int32_t e = e0 + u * kT + tid;
+    t[u] = e < lim ? v.topk[e] : -1;
+    if (t[u] >= v.ctx || (t[u] >> v.ps) >= p.max_pages) t[u] = -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    b[u] = t[u] >= 0 ? v.bt[t[u] >> v.ps] : 0;
+    hb[u] = t[u] >= 0 ? v.hbt[t[u] >> v.ps] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    src[u] = kZeroRow;
+    if (t[u] < 0) {
+      t[u] = -1;
+    } else if (b[u] >= 0) {
+      if (b[u] < v.pool_blocks) src[u] = (b[u] << v.ps) | (t[u] & v.pm);
+    } else if (hb[u] >= 0 && hb[u] < v.host_blocks) {
+      src[u] = (int32_t)(kHostTag | (uint32_t)((hb[u] << v.ps) | (t[u] & v.pm)));
+    } else {
+      src[u] = kNoHost;
+    }
+  }
+}
+
+// Gather workgroup: entries [lo, hi) of one request-layer, every row but the
+// misses': resident and hot rows from the pool, zero rows otherwise.
+__device__ void fill_gather(const FetchParams& p, int32_t* lds, int32_t rl, int32_t lo,
+                            int32_t hi) {
+  const int tid = threadIdx.x;
+  const Rl v = rl_view(p, rl);
+  const int32_t E = hi - lo;
+  // LDS: keys[E] | src[E] | tab[n] | flag
+  int32_t* keys = lds;
+  int32_t* src = keys + p.gather_e;
+  uint32_t* tab = reinterpret_cast<uint32_t*>(src + p.gather_e);
+  const int32_t n = p.gather_tab_n;
+  int32_t* flag = reinterpret_cast<int32_t*>(tab + n);
+  int32_t pre[kScanUnroll];
+  prefetch_slots(p, rl, pre);
+  for (int32_t h = tid; h < n; h += kT) tab[h] = kEmptyWord;
+  if (tid == 0) *flag = 0;
+  bool any = false;
+  for (int32_t e0 = lo; e0 < hi; e0 += kT * kU) {
+    int32_t t[kU], sv[kU];
+    load_entries(p, v, e0, hi, t, sv);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t el = e0 + u * kT + tid - lo;
+      if (el < E) {
+        keys[el] = t[u];
+        src[el] = sv[u];
+        any |= non_resident(sv[u]);
+      }
+    }
+  }
+  __syncthreads();
+  if (any) *flag = 1;
+  for (int32_t el = tid; el < E; el += kT)
+    if (non_resident(src[el])) map_insert(tab, n, keys, keys[el], el);
+  __syncthreads();
+  if (*flag) {
+    scan_slots(p, rl, tab, n, keys, pre);
+    for (int32_t el = tid; el < E; el += kT) {
+      const int32_t sv = src[el];
+      if (!non_resident(sv)) continue;
+      const uint32_t q = tab[map_find(tab, n, keys, keys[el])] & 0xFFFFu;
+      src[el] = q != kNoSlot ? (v.hot[q >> v.ps] << v.ps) | ((int32_t)q & v.pm)  // hot
+                             : sv == kNoHost ? kZeroRow : kSkip;                  // miss
+    }
+    __syncthreads();
+  }
+  HS_FILL_MARK(2);
+  const int32_t total = E * v.pieces;
+  for (int32_t g0 = 0; g0 < total; g0 += kT * kU) {
+    u32x4 val[kU];
+    uint8_t* dst[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t g = g0 + u * kT + tid;
+      dst[u] = nullptr;
+      val[u] = u32x4{0u, 0u, 0u, 0u};
+      if (g < total) {
+        const int32_t el = pdiv(g, v.magic);
+        const int32_t pc = g - el * v.pieces;
+        const int32_t code = src[el];
+        if (code != kSkip) dst[u] = v.out + (int64_t)(lo + el) * p.row_bytes + pc * 16;
+        if (code >= 0)
+          val[u] = *reinterpret_cast<const u32x4*>(v.pool_l + (int64_t)code * p.row_bytes +
+                                                   pc * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
+  }
+}
+
+// Miss workgroup s of S for one request-layer: the rows of the miss tokens t
+// with t mod S == s, each read once from the host into its first entry and
+// then copied to its later entries.
+__device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int32_t s,
+                            int32_t S) {
+  const int tid = threadIdx.x;
+  const Rl v = rl_view(p, rl);
+  const int32_t N = v.N;
+  // LDS: keys[N] | src[N] | list[N] | tab[n] | counters[4]
+  int32_t* keys = lds;
+  int32_t* src = keys + p.lds_n;
+  int32_t* list = src + p.lds_n;
+  uint32_t* tab = reinterpret_cast<uint32_t*>(list + p.lds_n);
+  const int32_t n = p.miss_tab_n;
+  int32_t* cnt = reinterpret_cast<int32_t*>(tab + n);
+  int32_t pre[kScanUnroll];
+  prefetch_slots(p, rl, pre);
+  for (int32_t h = tid; h < n; h += kT) tab[h] = kEmptyWord;
+  if (tid < 4) cnt[tid] = 0;
+  bool any = false;
+  for (int32_t e0 = 0; e0 < N; e0 += kT * kU) {
+    int32_t t[kU], sv[kU];
+    load_entries(p, v, e0, N, t, sv);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t e = e0 + u * kT + tid;
+      if (e < N) {
+        keys[e] = t[u];
+        src[e] = sv[u];
+        any |= is_host_row(sv[u]);
+      }
+    }
+  }
+  __syncthreads();
+  if (any) cnt[2] = 1;  // racing writes of the same value
+  HS_FILL_MARK(1);
+  for (int32_t e = tid; e < N; e += kT)
+    if (is_host_row(src[e])) map_insert(tab, n, keys, keys[e], e);
+  __syncthreads();
+  if (cnt[2] == 0) return;  // nothing to read from the host
+  scan_slots(p, rl, tab, n, keys, pre);
+  HS_FILL_MARK(2);
+
+  // ---- this workgroup's work lists: first entries of its miss tokens from
+  // the front of list[], their later entries from the back ----------------
+  for (int32_t e0 = 0; e0 < N; e0 += kT) {
+    const int32_t e = e0 + tid;
+    const int32_t sv = e < N ? src[e] : kZeroRow;
+    const int32_t t = e < N ? keys[e] : -1;
+    bool first = false, dup = false;
+    int32_t f = -1;
+    if (is_host_row(sv) && (t % S) == s) {
+      const uint32_t w = tab[map_find(tab, n, keys, t)];
+      if ((w & 0xFFFFu) == kNoSlot) {  // not in the hot buffer: a miss
+        f = (int32_t)(w >> 16);
+        first = f == e;
+        dup = !first;
+      }
+    }
+    const int32_t i = wave_append(&cnt[0], first);
+    if (first) list[i] = e;
+    const int32_t j = wave_append(&cnt[1], dup);
+    if (dup) {
+      list[p.lds_n - 1 - j] = e;
+      src[e] = f;  // a later entry copies the first entry's output row
+    }
+  }
+  __syncthreads();
+  const int32_t n_first = cnt[0];
+  const int32_t n_dup = cnt[1];
+  HS_FILL_MARK(3);
+
+  // ---- host rows of the first entries, kHostUnroll reads in flight a thread
+  const int32_t total = n_first * v.pieces;
+  for (int32_t g0 = 0; g0 < total; g0 += kT * kHostUnroll) {
+    u32x4 val[kHostUnroll];
+    uint8_t* dst[kHostUnroll];
+#pragma unroll
+    for (int u = 0; u < kHostUnroll; ++u) {
+      const int32_t g = g0 + u * kT + tid;
+      dst[u] = nullptr;
+      if (g < total) {
+        const int32_t j = pdiv(g, v.magic);
+        const int32_t pc = g - j * v.pieces;
+        const int32_t e = list[j];
+        const int64_t hrow = (int64_t)((uint32_t)src[e] & ~kHostTag);
+        val[u] = *reinterpret_cast<const u32x4*>(v.host_l + hrow * p.row_bytes + pc * 16);
+        dst[u] = v.out + (int64_t)e * p.row_bytes + pc * 16;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kHostUnroll; ++u)
+      if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
+  }
+  if (n_dup == 0) return;
+  __syncthreads();  // this workgroup's row writes are visible to it
+
+  // ---- later entries of the owned miss tokens copy the first entry's row
+  const int32_t total2 = n_dup * v.pieces;
+  const int32_t* dl = list + p.lds_n - n_dup;
+  for (int32_t g0 = 0; g0 < total2; g0 += kT * kU) {
+    u32x4 val[kU];
+    uint8_t* dst[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t g = g0 + u * kT + tid;
+      dst[u] = nullptr;
+      if (g < total2) {
+        const int32_t j = pdiv(g, v.magic);
+        const int32_t pc = g - j * v.pieces;
+        const int32_t e = dl[j];
+        val[u] = *reinterpret_cast<const u32x4*>(v.out + (int64_t)src[e] * p.row_bytes + pc * 16);
+        dst[u] = v.out + (int64_t)e * p.row_bytes + pc * 16;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
+  }
+}
+
+// Fill block b of the launch's fill blocks: [0, miss_groups) are miss
+// workgroups (group g handles the (request-layer, split) pairs g,
+// g + miss_groups, ...), the rest gather workgroups, gather_splits per
+// request-layer.
+__device__ void fill_block(const FetchParams& p, int32_t* lds, int32_t b) {
+  HS_FILL_MARK(0);
+  const int32_t n_rl = p.num_reqs * p.num_layers;
+  if (b < p.miss_groups) {
+    const int32_t S = p.miss_splits;
+    for (int32_t w = b; w < n_rl * S; w += p.miss_groups) {
+      if (w != b) __syncthreads();  // the previous pair's LDS reads are done
+      fill_misses(p, lds, w / S, w % S, S);
+    }
+    HS_FILL_MARK(5);
+    return;
+  }
+  const int32_t i = b - p.miss_groups;
+  const int32_t rl = i / p.gather_splits;
+  const int32_t s = i - rl * p.gather_splits;
+  const int32_t lo = min(p.entries, s * p.gather_e);
+  const int32_t hi = min(p.entries, lo + p.gather_e);
+  fill_gather(p, lds, rl, lo, hi);
+  HS_FILL_MARK(5);
+}
+
+}  // namespace
+}  // namespace fill
+}  // namespace hs

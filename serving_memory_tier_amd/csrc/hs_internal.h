@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace hs {
 
 // Threads per resolver workgroup (one workgroup per request-layer).
@@ -43,21 +45,60 @@ struct ResolveParams {
   int32_t* stats;
 };
 
-// Enqueue the resolver (no gather).  Returns a hipError_t from the launch.
-hipError_t launch_resolve(const ResolveParams& p, hipStream_t stream);
+struct FetchParams;
+
+// Enqueue the resolver (no gather); with `fill`, the early fill's
+// workgroups run in the same launch.  Returns the launch's hipError_t.
+hipError_t launch_resolve(const ResolveParams& p, const FetchParams* fill, hipStream_t stream);
 
 // LDS of one gfx950 compute unit, all of which one workgroup may use.
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 
+// Raises a kernel's dynamic-LDS limit to the whole CU less its static LDS.
+// The limit is a per-device attribute of the function, so it is set once on
+// each device (bit d of `done` records device d).
+inline hipError_t allow_full_lds(const void* fn, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  hipFuncAttributes attr{};
+  err = hipFuncGetAttributes(&attr, fn);
+  if (err != hipSuccess) return err;
+  err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(kMaxLdsBytes - attr.sharedSizeBytes));
+  if (err != hipSuccess) return err;
+  done.fetch_or(bit, std::memory_order_acq_rel);
+  return hipSuccess;
+}
+
+// Launches a kernel and returns that launch's own status (not whatever an
+// earlier runtime call left behind for hipGetLastError).
+template <typename... Args>
+inline hipError_t launch_kernel(void (*fn)(Args...), dim3 grid, dim3 block, size_t lds,
+                                hipStream_t stream, Args... args) {
+  void* ptrs[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, ptrs, lds, stream);
+}
+
 // Bytes of dynamic LDS the resolver needs for N entries and C slots.
 size_t resolve_lds_bytes(int32_t entries, int32_t hot_capacity);
 
-// The row mover: the single-stride gather, and (fused) the host-link copies
-// of the misses the resolver assigned.  Row ids in [0, pool_rows) are
-// gathered from the pool; in fused mode a code -(8 + 2 q + c) names a miss
-// assigned to hot slot q whose row is read from the host pool (and, when
-// c = 1, also written into the slot), after which the code is replaced by
-// the slot's row id; every other row id yields a zero row.
+// The row mover.  Row ids in [0, pool_rows) are gathered from the pool; a
+// code -(8 + 2 q + c) names a miss assigned to hot slot q (c = 1 on the
+// token's first entry, which fills the slot); -2 a miss left without a slot;
+// any other negative id yields a zero row.  Modes:
+//   kMoveGather  plain gather of row ids (no codes);
+//   kMoveFused   misses read from the host pool into the output and, on the
+//                first entry, into the slot; codes become the slot's row id
+//                and the first entry records the slot's new token;
+//   kMoveCommit  after the early fill (launch_fetch) wrote every output row:
+//                first entries copy their row from the output into the slot
+//                and record the slot's new token, codes become row ids, rows
+//                of misses without a slot become zero rows.
+enum MoveMode { kMoveGather = 0, kMoveFused = 1, kMoveCommit = 3 };
+
 struct MoveParams {
   const uint8_t* pool;
   uint8_t* pool_w;              // hot-slot writes (fused mode)
@@ -74,6 +115,7 @@ struct MoveParams {
   const int32_t* topk;              // fused mode
   const int32_t* host_block_table;  // fused mode
   const int32_t* hot_blocks;        // fused mode
+  int32_t* slot_token;              // fused / commit mode
   int32_t* row_ids;
   int32_t num_reqs;
   int32_t rows_per_rl;
@@ -84,7 +126,50 @@ struct MoveParams {
 // it reads are rewritten only by itself.
 constexpr int kMoveEntriesPerWave = 16;
 
-hipError_t launch_move(const MoveParams& p, bool fused, hipStream_t stream);
+hipError_t launch_move(const MoveParams& p, MoveMode mode, hipStream_t stream);
+
+// The early fill (fill.h; fetch.hip, and fused into the resolver's launch
+// in resolve.hip): every entry's row of the gather output written from the
+// state before the step -- resident and hot rows from the pool, misses from
+// the host pool once per distinct token, zero rows otherwise -- while the
+// resolver runs.
+constexpr int kFillThreads = kResolveThreads;
+constexpr int kHostUnroll = 1;             // host reads in flight per miss-workgroup thread
+constexpr int kFetchHostGroups = 32;       // miss workgroups per launch, at most
+constexpr int kFetchMaxSplits = 16;        // miss workgroups per request-layer, at most
+constexpr int kFetchGatherEntries = 512;   // entries per gather workgroup
+
+struct FetchParams {
+  int32_t page_shift;
+  int32_t row_bytes;
+  int32_t num_layers;
+  int32_t hot_capacity;
+  int64_t pool_rows, host_rows;
+  int64_t pool_stride, host_stride;
+  int32_t num_reqs, max_pages;
+  const uint8_t* pool;
+  const uint8_t* host;
+  const int32_t* block_table;
+  const int32_t* host_block_table;
+  const int32_t* ctx_len;
+  const int32_t* hot_blocks;
+  const int32_t* slot_token;
+  const int32_t* topk;
+  int32_t entries;
+  uint8_t* out;
+  // set by prepare_fetch
+  int32_t miss_groups, miss_splits, gather_splits;
+  int32_t lds_n, miss_tab_n, gather_e, gather_tab_n;
+  uint32_t piece_magic;
+};
+
+// Bytes of dynamic LDS a fill workgroup needs for N entries.
+size_t fetch_lds_bytes(int32_t entries, int32_t hot_capacity);
+// Completes p's launch shape; returns the number of fill workgroups and sets
+// *lds_bytes.
+int64_t prepare_fetch(FetchParams& p, size_t* lds_bytes);
+// The fill as a kernel of its own.
+hipError_t launch_fetch(FetchParams p, hipStream_t stream);
 
 struct OffloadParams {
   const uint8_t* pool;

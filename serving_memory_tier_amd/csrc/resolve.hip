@@ -42,6 +42,7 @@
 #include <atomic>
 #include <stdint.h>
 
+#include "fill.h"
 #include "hs_internal.h"
 
 // Phase markers for timing builds; empty in the library.
@@ -437,15 +438,33 @@ __device__ inline int lower_bound(const int32_t* a, int n, int32_t v) {
 struct KernelArgs {
   ResolveParams p;
   LdsPlan plan;
+  FetchParams fill;  // the fused fill's workgroups (FILL launches)
+  int32_t n_rl;
+  uint32_t lds_bytes;
 };
 
 // ES: sort elements per thread (kThreads * ES >= N); EC: slots per thread
 // (kThreads * EC >= C).
 // All global stores happen after the last barrier, so no barrier ever waits
 // for store acknowledgements.
-template <int ES, int EC>
+// FILL: the launch also carries the early fill's workgroups (fill.h) -- its
+// miss workgroups first, so that the host-link reads start at once, then one
+// resolver workgroup per request-layer, then the fill's gather workgroups.
+// The two kinds never wait on each other; they share the launch so that the
+// step needs no second stream and no cross-queue join.
+template <int ES, int EC, bool FILL>
 __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  int rl = blockIdx.x;
+  if constexpr (FILL) {
+    const int32_t b = blockIdx.x;
+    const int32_t mg = args.fill.miss_groups;
+    if (b < mg || b >= mg + args.n_rl) {
+      fill::fill_block(args.fill, reinterpret_cast<int32_t*>(lds), b < mg ? b : b - args.n_rl);
+      return;
+    }
+    rl = b - mg;
+  }
   const ResolveParams& p = args.p;
   const LdsPlan& plan = args.plan;
   int32_t* keys = reinterpret_cast<int32_t*>(lds + plan.off_keys);
@@ -460,7 +479,6 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
 
   const int tid = threadIdx.x;
   const int l = lane_id(), w = wave_id();
-  const int rl = blockIdx.x;
   const int r = rl / p.num_layers;
   const int ps = p.page_shift;
   const int32_t pm = (1 << ps) - 1;
@@ -471,7 +489,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   const int32_t* hot = p.hot_blocks + (int64_t)r * (C >> ps);
   const int32_t* topk = p.topk + (int64_t)rl * N;
   int32_t* rows = p.row_ids + (int64_t)rl * N;
-  int32_t* stok = p.slot_token + (int64_t)rl * C;
+  const int32_t* stok = p.slot_token + (int64_t)rl * C;
   uint32_t* sstp = p.slot_stamp + (int64_t)rl * C;
   const int64_t pool_blocks = p.pool_rows >> ps;
   const int64_t host_blocks = p.host_rows >> ps;
@@ -807,11 +825,9 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
     const int q = j * kThreads + tid;
     if (q < C && sflag[q] == 1) sstp[q] = p.stamp;
   }
-  for (int j = tid; j < A; j += kThreads) {
-    const int q = vict[j];
-    stok[q] = unr[mk[j]];
-    sstp[q] = p.stamp;
-  }
+  // (a victim's new token is recorded by the row mover, on the entry that
+  // fills the slot)
+  for (int j = tid; j < A; j += kThreads) sstp[vict[j]] = p.stamp;
   if (tid == 0) {
     int32_t* st = p.stats + (int64_t)rl * 8;
     st[0] = ucnt[1];
@@ -826,42 +842,42 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   HS_PHASE_FLUSH;
 }
 
-template <int ES, int EC>
+template <int ES, int EC, bool FILL>
 hipError_t launch_ec(const KernelArgs& a, int grid, hipStream_t stream) {
-  auto fn = resolve_kernel<ES, EC>;
-  // The dynamic-LDS limit is a per-device attribute of the function: raise
-  // it once on each device the kernel is launched on.
-  static std::atomic<uint64_t> attr_set{0};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
+  auto fn = resolve_kernel<ES, EC, FILL>;
+  static std::atomic<uint64_t> raised{0};
+  hipError_t err = allow_full_lds(reinterpret_cast<const void*>(fn), raised);
   if (err != hipSuccess) return err;
-  const uint64_t bit = 1ull << (dev & 63);
-  if (!(attr_set.load(std::memory_order_acquire) & bit)) {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
-    if (err != hipSuccess) return err;
-    attr_set.fetch_or(bit, std::memory_order_acq_rel);
-  }
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), a.plan.total, stream, a);
-  return hipGetLastError();
+  return launch_kernel(fn, dim3(grid), dim3(kThreads), a.lds_bytes, stream, a);
 }
 
 // Largest rounds per thread needed: HS_MAX_ENTRIES and HS_MAX_HOT_CAPACITY
 // are 8192, i.e. 8192 / kThreads rounds.
 constexpr int kMaxRounds = 8192 / kThreads;
 
-template <int ES>
+template <int ES, bool FILL>
 hipError_t launch_es(const KernelArgs& a, int grid, int EC, hipStream_t stream) {
   if constexpr (ES > kMaxRounds) {
     return hipErrorInvalidValue;
   } else {
     switch (EC) {
-      case 1: return launch_ec<ES, 1>(a, grid, stream);
-      case 2: return launch_ec<ES, 2>(a, grid, stream);
-      case 4: return launch_ec<ES, 4>(a, grid, stream);
-      case 8: return launch_ec<ES, (8 <= kMaxRounds ? 8 : kMaxRounds)>(a, grid, stream);
-      default: return launch_ec<ES, kMaxRounds>(a, grid, stream);
+      case 1: return launch_ec<ES, 1, FILL>(a, grid, stream);
+      case 2: return launch_ec<ES, 2, FILL>(a, grid, stream);
+      case 4: return launch_ec<ES, 4, FILL>(a, grid, stream);
+      case 8: return launch_ec<ES, (8 <= kMaxRounds ? 8 : kMaxRounds), FILL>(a, grid, stream);
+      default: return launch_ec<ES, kMaxRounds, FILL>(a, grid, stream);
     }
+  }
+}
+
+template <bool FILL>
+hipError_t launch_rounds(const KernelArgs& a, int grid, int ES, int EC, hipStream_t stream) {
+  switch (ES) {
+    case 1: return launch_es<1, FILL>(a, grid, EC, stream);
+    case 2: return launch_es<2, FILL>(a, grid, EC, stream);
+    case 4: return launch_es<4, FILL>(a, grid, EC, stream);
+    case 8: return launch_es<8, FILL>(a, grid, EC, stream);
+    default: return launch_es<16, FILL>(a, grid, EC, stream);
   }
 }
 
@@ -877,21 +893,23 @@ size_t resolve_lds_bytes(int32_t entries, int32_t hot_capacity) {
   return make_plan(entries, hot_capacity, round_up_pow2_rounds(entries)).total;
 }
 
-hipError_t launch_resolve(const ResolveParams& p, hipStream_t stream) {
+hipError_t launch_resolve(const ResolveParams& p, const FetchParams* fill, hipStream_t stream) {
   const int ES = round_up_pow2_rounds(p.entries);
   const int EC = round_up_pow2_rounds(p.hot_capacity);
   KernelArgs a;
   a.p = p;
   a.plan = make_plan(p.entries, p.hot_capacity, ES);
-  const int grid = p.num_reqs * p.num_layers;
-  if (grid == 0) return hipSuccess;
-  switch (ES) {
-    case 1: return launch_es<1>(a, grid, EC, stream);
-    case 2: return launch_es<2>(a, grid, EC, stream);
-    case 4: return launch_es<4>(a, grid, EC, stream);
-    case 8: return launch_es<8>(a, grid, EC, stream);
-    default: return launch_es<16>(a, grid, EC, stream);
-  }
+  a.n_rl = p.num_reqs * p.num_layers;
+  a.lds_bytes = a.plan.total;
+  if (a.n_rl == 0) return hipSuccess;
+  if (!fill) return launch_rounds<false>(a, a.n_rl, ES, EC, stream);
+  a.fill = *fill;
+  size_t flds = 0;
+  const int64_t fill_groups = prepare_fetch(a.fill, &flds);
+  const int64_t grid = a.n_rl + fill_groups;
+  if (grid > INT32_MAX || flds > kMaxLdsBytes) return hipErrorInvalidValue;
+  if (flds > a.lds_bytes) a.lds_bytes = (uint32_t)flds;
+  return launch_rounds<true>(a, (int)grid, ES, EC, stream);
 }
 
 }  // namespace hs

@@ -31,6 +31,7 @@ class HipRuntime:
         self.hip = hip = _runtime()
         hip.hipEventCreate.argtypes = [ct.POINTER(ct.c_void_p)]
         hip.hipEventRecord.argtypes = [ct.c_void_p, ct.c_void_p]
+        hip.hipStreamWaitEvent.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_uint]
         hip.hipEventElapsedTime.argtypes = [ct.POINTER(ct.c_float), ct.c_void_p, ct.c_void_p]
         hip.hipEventDestroy.argtypes = [ct.c_void_p]
         hip.hipStreamBeginCapture.argtypes = [ct.c_void_p, ct.c_int]
@@ -56,6 +57,11 @@ class HipRuntime:
     def record(self, e, stream: int) -> None:
         if self.hip.hipEventRecord(e, self.ct.c_void_p(stream)) != 0:
             raise RuntimeError("hipEventRecord failed")
+
+    def wait(self, stream: int, e) -> None:
+        """Work enqueued on ``stream`` after this waits for event ``e``."""
+        if self.hip.hipStreamWaitEvent(self.ct.c_void_p(stream), e, 0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
 
     def elapsed_ms(self, a, b) -> float:
         ms = self.ct.c_float()

@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 from .api import (HostPool, batch_of, hs_gather, hs_offload_prefix_pages, hs_plan_replay,
-                  hs_resolve, hs_resolve_decide, hs_resolve_move, layout_of)
+                  hs_resolve, hs_resolve_commit, hs_resolve_decide, hs_resolve_move, layout_of)
 
 PAGE = 64
 ROW = 656
@@ -135,31 +135,52 @@ class DeviceRun:
                     k += 1
             self.table_sets.append(sets)
 
-    def launch_step(self, i: int, hip, stream: int, stats=None, events=None) -> None:
-        """Step ``i`` on ``stream``: the scheduler's table updates as 4-byte
-        copies from pinned memory, the decide and move kernels, and the
-        offload of the pages the step completed.  ``hip`` is a HipRuntime;
-        ``events`` (optional) four events recorded around the kernels."""
+    def launch_step(self, i: int, hip, stream: int, stats=None, serial: bool = False) -> None:
+        """Step ``i`` on ``stream`` with no host work: the scheduler's table
+        updates as 4-byte copies from pinned memory, then one hs_plan_replay
+        call (resolve, gather, offload of the pages the step completed).
+        ``serial``: the decide and move stages one after the other instead
+        (the path the library takes without a gather output, with one)."""
         wl = self.wl
         s = wl.steps[i]
         for dst, src in self.table_sets[i]:
             hip.memcpy_h2d(dst, src, 4, stream)
-        if events is not None:
-            hip.record(events[0], stream)
-        hs_resolve_decide(self.layout, self.batches[i], self.topk[i], wl.P, wl.K, s.stamp,
-                          self.rows, self.stats if stats is None else stats, stream)
-        if events is not None:
-            hip.record(events[1], stream)
-        hs_resolve_move(self.layout, self.batches[i], self.topk[i], wl.P, wl.K, self.rows,
-                        self.out, stream)
-        if events is not None:
-            hip.record(events[2], stream)
+        st = self.stats if stats is None else stats
         n_off = s.offload.shape[0]
+        if serial:
+            hs_resolve_decide(self.layout, self.batches[i], self.topk[i], wl.P, wl.K, s.stamp,
+                              self.rows, None, st, stream)
+            hs_resolve_move(self.layout, self.batches[i], self.topk[i], wl.P, wl.K, self.rows,
+                            self.out, stream)
+            if n_off:
+                hs_offload_prefix_pages(self.layout, self.pool, self.host_pool, self.pairs[i],
+                                        n_off, stream)
+        else:
+            hs_plan_replay(self.layout, self.batches[i], self.topk[i], wl.P, wl.K, s.stamp,
+                           self.rows, self.out, st, self.pairs[i] if n_off else None, n_off,
+                           stream)
+
+    def launch_step_timed(self, i: int, hip, stream: int, ev, stats=None,
+                          offload: bool = True) -> None:
+        """Step ``i`` as the stages of hs_plan_replay on ``stream`` -- the fused
+        resolve-and-fill launch, the commit, the offload -- with events around
+        each kernel: ``ev`` holds four events, recorded before the fused
+        launch, after it, after the commit and after the offload."""
+        wl = self.wl
+        s = wl.steps[i]
+        for dst, src in self.table_sets[i]:
+            hip.memcpy_h2d(dst, src, 4, stream)
+        st = self.stats if stats is None else stats
+        L, B, T = self.layout, self.batches[i], self.topk[i]
+        hip.record(ev[0], stream)
+        hs_resolve_decide(L, B, T, wl.P, wl.K, s.stamp, self.rows, self.out, st, stream)
+        hip.record(ev[1], stream)
+        hs_resolve_commit(L, B, T, wl.P, wl.K, self.rows, self.out, stream)
+        hip.record(ev[2], stream)
+        n_off = s.offload.shape[0] if offload else 0
         if n_off:
-            hs_offload_prefix_pages(self.layout, self.pool, self.host_pool, self.pairs[i], n_off,
-                                    stream)
-            if events is not None:
-                hip.record(events[3], stream)
+            hs_offload_prefix_pages(L, self.pool, self.host_pool, self.pairs[i], n_off, stream)
+        hip.record(ev[3], stream)
 
     def close(self) -> None:
         self.host = None

@@ -42,6 +42,7 @@ def test_status_strings(lib):
     assert "unsupported" in hs.hs_status_string(2)
     assert "launch" in hs.hs_status_string(3)
     assert "unknown" in hs.hs_status_string(99)
+    assert lib.hs_last_error() == b""           # no HIP failure on this thread yet
 
 
 def _layout(**kw):
@@ -109,6 +110,29 @@ def test_plan_rejects_bad_call(lib):
     assert f(5, 2048, None, 0) == 2      # 10240 entries > 8192
     assert f(4, 2048, None, -1) == 1
     assert f(4, 2048, None, 3) == 1      # pairs missing
+
+
+def test_stages_reject_bad_call(lib):
+    lay, bat = _layout(), _batch()
+    L, B = ctypes.byref(lay), ctypes.byref(bat)
+    fetch = lambda topk, P, K, out: lib.hs_resolve_fetch(L, B, topk, P, K, out, None)
+    assert fetch(0x1000, 1, 2048, None) == 1          # the prefetch writes into gather_out
+    assert fetch(None, 1, 2048, 0x1000) == 1
+    assert fetch(0x1000, 0, 2048, 0x1000) == 1
+    assert fetch(0x1000, 5, 2048, 0x1000) == 2
+    move = lambda rows: lib.hs_resolve_move(L, B, 0x1000, 1, 2048, rows, None, None)
+    assert move(None) == 1
+    commit = lambda rows, out: lib.hs_resolve_commit(L, B, 0x1000, 1, 2048, rows, out, None)
+    assert commit(0x1000, None) == 1
+    assert commit(None, 0x1000) == 1
+    dec = lambda stamp, stats: lib.hs_resolve_decide(L, B, 0x1000, 1, 2048, ctypes.c_uint32(stamp),
+                                                     0x1000, None, stats, None)
+    assert dec(0, 0x1000) == 1
+    assert dec(1, None) == 1
+    empty = _batch(R=0)
+    E = ctypes.byref(empty)
+    assert lib.hs_resolve_fetch(L, E, 0x1000, 1, 2048, 0x1000, None) == 0   # nothing to do
+    assert lib.hs_resolve_commit(L, E, 0x1000, 1, 2048, 0x1000, 0x1000, None) == 0
 
 
 def test_gather_and_offload_reject(lib):

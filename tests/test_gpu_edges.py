@@ -5,18 +5,22 @@ pages, 8 slots), padding, duplicates, out-of-range tokens, null pages without
 host copies, table entries pointing outside the pools, unusable hot blocks,
 non-monotone stamps, ragged and maximal list sizes, maximal hot capacity,
 other page sizes and row sizes, an empty batch, and the gather and offload
-entry points on their own.
+entry points on their own.  The randomised cases run each path of the
+library: the one-call form, the serial stages and the caller-scheduled
+overlapped stages.
 """
 
 from __future__ import annotations
 
 import os
+import zlib
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
+import stages
 from harness import run_tiny, tiny_instance
 
 pytestmark = pytest.mark.gpu
@@ -59,7 +63,7 @@ class GpuCase:
         self.batch = hs.batch_of(bt.shape[0], bt.shape[1], self.pool, self.host_pool, self.bt,
                                  self.hbt, self.ctx, self.hot, self.tok, self.stp)
 
-    def resolve(self, topk: np.ndarray, stamp: int, gather=True, pairs=None):
+    def resolve(self, topk: np.ndarray, stamp: int, gather=True, pairs=None, mode="call"):
         R, L = topk.shape[:2]
         P, K = (1, topk.shape[2]) if topk.ndim == 3 else topk.shape[2:]
         t = torch.from_numpy(np.ascontiguousarray(topk)).cuda()
@@ -69,11 +73,8 @@ class GpuCase:
                if gather else None)
         pr = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda() \
             if pairs is not None else None
-        if topk.ndim == 3 and pairs is None:
-            self.hs.hs_resolve(self.layout, self.batch, t, K, stamp, rows, out, stats)
-        else:
-            self.hs.hs_plan_replay(self.layout, self.batch, t, P, K, stamp, rows, out, stats,
-                                   pr, 0 if pairs is None else len(pairs))
+        stages.run(mode, self.layout, self.batch, t, P, K, stamp, rows, out, stats, pr,
+                   0 if pairs is None else len(pairs))
         torch.cuda.synchronize()
         return (rows.cpu().numpy(), stats.cpu().numpy(),
                 None if out is None else out.cpu().numpy())
@@ -87,9 +88,9 @@ class GpuCase:
         self.host_pool.close()
 
 
-def _compare(case, inst_or_arrays, topk, stamp, pairs=None, page=None):
+def _compare(case, inst_or_arrays, topk, stamp, pairs=None, page=None, mode="call"):
     a = inst_or_arrays
-    g_rows, g_stats, g_out = case.resolve(topk, stamp, pairs=pairs)
+    g_rows, g_stats, g_out = case.resolve(topk, stamp, pairs=pairs, mode=mode)
     o_rows, o_stats, o_out = oracle.resolve(a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"],
                                             a["hot"], a["tok"], a["stp"],
                                             np.ascontiguousarray(topk), stamp, True,
@@ -113,31 +114,36 @@ def _case_from_tiny(inst):
                    inst["tok"].shape[2])
 
 
-def test_worked_example_on_gpu():
+@pytest.mark.parametrize("mode", stages.MODES)
+def test_worked_example_on_gpu(mode):
     inst = tiny_instance()
     case = _case_from_tiny(inst)
     try:
         lists = [[21, 5, 13, 2, 17, 9], [9, 1, 22, 13, 6, 14]]
-        rows, _ = _compare(case, inst, np.array([[lists[0]]], np.int32), 1)
+        rows, _ = _compare(case, inst, np.array([[lists[0]]], np.int32), 1, mode=mode)
         assert rows.ravel().tolist() == [9, 37, 39, 36, 29, 38]
-        rows, _ = _compare(case, inst, np.array([[lists[1]]], np.int32), 2)
+        rows, _ = _compare(case, inst, np.array([[lists[1]]], np.int32), 2, mode=mode)
         assert rows.ravel().tolist() == [38, 24, 10, 39, 25, 26]
         inst["bt"][0, 4] = -1
         case.bt[0, 4] = -1
-        rows, _ = _compare(case, inst, np.array([[[17, 2, 10, 6, 20, 3]]], np.int32), 3)
+        rows, _ = _compare(case, inst, np.array([[[17, 2, 10, 6, 20, 3]]], np.int32), 3,
+                           mode=mode)
         assert rows.ravel().tolist() == [38, 36, 37, 25, 8, 27]
-        rows, stats = _compare(case, inst, np.array([[[17, 2, 10, 6, 20, 3]]], np.int32), 4)
+        rows, stats = _compare(case, inst, np.array([[[17, 2, 10, 6, 20, 3]]], np.int32), 4,
+                               mode=mode)
         assert stats.ravel()[:3].tolist() == [1, 5, 0]
     finally:
         case.close()
 
 
-def test_worked_example_plan_and_overflow_on_gpu():
+@pytest.mark.parametrize("mode", stages.MODES)
+def test_worked_example_plan_and_overflow_on_gpu(mode):
     inst = tiny_instance(C=4, hot_blocks=(9,))
     case = _case_from_tiny(inst)
     try:
-        _compare(case, inst, np.array([[[21, 5, 13, 2, 17, 9]]], np.int32), 1)
-        rows, stats = _compare(case, inst, np.array([[[[9, 1, 22], [13, 6, 14]]]], np.int32), 2)
+        _compare(case, inst, np.array([[[21, 5, 13, 2, 17, 9]]], np.int32), 1, mode=mode)
+        rows, stats = _compare(case, inst, np.array([[[[9, 1, 22], [13, 6, 14]]]], np.int32), 2,
+                               mode=mode)
         assert rows.tolist() == [[[[38, 36, 10], [39, 37, -2]]]]
         assert stats.ravel().tolist() == [1, 2, 2, 1, 0, 0, 0, 0]
     finally:
@@ -211,17 +217,18 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("mode", stages.MODES)
 @pytest.mark.parametrize("name,R,L,P,K,C,page,rb,n_pages,hostile", CASES,
                          ids=[c[0] for c in CASES])
-def test_random_cases(name, R, L, P, K, C, page, rb, n_pages, hostile):
-    rs = np.random.default_rng(abs(hash(name)) % (1 << 31))
+def test_random_cases(name, R, L, P, K, C, page, rb, n_pages, hostile, mode):
+    rs = np.random.default_rng(zlib.crc32(name.encode()))
     n_blocks = R * (C // page) + n_pages * R // 2 + 8
     a = random_arrays(rs, R, L, C, page, rb, n_pages, n_blocks, n_pages, hostile)
     case = GpuCase(page, a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"], a["hot"],
                    a["tok"].copy(), a["stp"].copy(), C)
     try:
         for step in range(4):
-            _say(f"[edges] {name} step {step}")
+            _say(f"[edges] {name} {mode} step {step}")
             lists = random_lists(rs, R, L, P, K, a["ctx"])
             topk = lists[:, :, 0] if P == 1 else lists
             pairs = None
@@ -231,7 +238,7 @@ def test_random_cases(name, R, L, P, K, C, page, rb, n_pages, hostile):
                 if hostile:
                     pairs[0, 0] = n_blocks + 1
                     pairs[1, 1] = -2
-            _compare(case, a, topk, 10 + 3 * step - (step == 3) * 7, pairs=pairs)
+            _compare(case, a, topk, 10 + 3 * step - (step == 3) * 7, pairs=pairs, mode=mode)
     finally:
         case.close()
 

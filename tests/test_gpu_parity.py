@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import hs_gen
+import stages
 from harness import OracleRun, expected_content
 
 pytestmark = pytest.mark.gpu
@@ -43,7 +44,7 @@ def _say(msg: str) -> None:
 
 
 def run_parity(wl, requests=None, n_steps=None, hit_replay=False, fused_plan=False,
-               check_content=True):
+               check_content=True, mode="call"):
     from serving_memory_tier_amd.runner import DeviceRun
 
     dev = DeviceRun(wl)
@@ -60,8 +61,11 @@ def run_parity(wl, requests=None, n_steps=None, hit_replay=False, fused_plan=Fal
             ora.pre(step)
             if fused_plan:
                 dev.plan_step(i)
-            else:
+            elif mode == "call":
                 dev.resolve(i)
+            else:
+                stages.run(mode, dev.layout, dev.batch, dev.topk[i], wl.P, wl.K, step.stamp,
+                           dev.rows, dev.out, dev.stats)
             torch.cuda.synchronize()
             rows, stats, out = ora.resolve(step)
             totals += stats.sum(axis=(0, 1))
@@ -119,6 +123,12 @@ def test_mixed_decode_full():
     assert totals[1] > 0 and totals[2] > 0 and totals[0] > 0
 
 
+@pytest.mark.parametrize("mode", ["serial", "staged"])
+def test_mixed_decode_stages(mode):
+    totals = run_parity(hs_gen.mixed_decode(steps=6), mode=mode)
+    assert totals[2] > 0
+
+
 def test_no_residency_full():
     totals = run_parity(hs_gen.no_residency())
     _say(f"[parity] no_residency totals {totals.tolist()}")
@@ -139,6 +149,12 @@ def test_mixed_state_full_sampled():
 def test_multi_layer_full_sampled():
     wl = hs_gen.multi_layer(turns=4)
     run_parity(wl, requests=[0, 17, 63], fused_plan=False)
+
+
+@pytest.mark.parametrize("mode", ["serial", "staged"])
+def test_mixed_state_stages_sampled(mode):
+    wl = hs_gen.mixed_state(steps=4)
+    run_parity(wl, requests=[0, 1, 64, 127], mode=mode)
 
 
 def test_determinism_repeat():
