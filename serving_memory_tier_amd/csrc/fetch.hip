@@ -21,8 +21,17 @@ __global__ void __launch_bounds__(kFillThreads) fetch_kernel(FetchParams p) {
 
 }  // namespace
 
-size_t fetch_lds_words(int32_t entries, int32_t* miss_tab_n, int32_t* gather_e,
-                       int32_t* gather_tab_n) {
+// Entries per gather workgroup: about kFetchGatherTarget workgroups in all,
+// kFetchGatherMin..kFetchGatherEntries entries each (a multiple of 4).
+int32_t gather_entries(int32_t entries, int64_t n_rl) {
+  int64_t per = (entries * n_rl + kFetchGatherTarget - 1) / kFetchGatherTarget;
+  if (per < kFetchGatherMin) per = kFetchGatherMin;
+  if (per > kFetchGatherEntries) per = kFetchGatherEntries;
+  if (per > entries) per = entries;
+  return (int32_t)((per + 3) / 4 * 4);
+}
+
+size_t fetch_lds_words(int32_t entries, int32_t ge, int32_t* miss_tab_n, int32_t* gather_tab_n) {
   const int32_t ln = ((entries + 3) / 4) * 4;
   // miss workgroups: keys, src and list of N entries, the table, 4 counters;
   // the table takes 2N + 64 words where that fits, at least 1.5N + 1
@@ -32,11 +41,8 @@ size_t fetch_lds_words(int32_t entries, int32_t* miss_tab_n, int32_t* gather_e,
   const int32_t lo_bound = entries + entries / 2 + 1;
   if (mt < lo_bound) mt = lo_bound;
   // gather workgroups: keys and src of their range, a table 4x its size, a flag
-  const int32_t ge =
-      entries < kFetchGatherEntries ? ((entries + 3) / 4) * 4 : kFetchGatherEntries;
   const int32_t gt = ((4 * ge) / 64 + 1) * 64;
   if (miss_tab_n) *miss_tab_n = mt;
-  if (gather_e) *gather_e = ge;
   if (gather_tab_n) *gather_tab_n = gt;
   const size_t miss_words = 3 * (size_t)ln + mt + 4;
   const size_t gather_words = 2 * (size_t)ge + gt + 4;
@@ -45,13 +51,16 @@ size_t fetch_lds_words(int32_t entries, int32_t* miss_tab_n, int32_t* gather_e,
 
 size_t fetch_lds_bytes(int32_t entries, int32_t hot_capacity) {
   (void)hot_capacity;
-  return 4 * fetch_lds_words(entries, nullptr, nullptr, nullptr);
+  // the largest gather range any launch uses
+  const int32_t ge = entries < kFetchGatherEntries ? (entries + 3) / 4 * 4 : kFetchGatherEntries;
+  return 4 * fetch_lds_words(entries, ge, nullptr, nullptr);
 }
 
 int64_t prepare_fetch(FetchParams& p, size_t* lds_bytes) {
   const int64_t n_rl = (int64_t)p.num_reqs * p.num_layers;
   p.lds_n = ((p.entries + 3) / 4) * 4;
-  *lds_bytes = 4 * fetch_lds_words(p.entries, &p.miss_tab_n, &p.gather_e, &p.gather_tab_n);
+  p.gather_e = gather_entries(p.entries, n_rl);
+  *lds_bytes = 4 * fetch_lds_words(p.entries, p.gather_e, &p.miss_tab_n, &p.gather_tab_n);
   const uint32_t pieces = (uint32_t)(p.row_bytes >> 4);
   p.piece_magic = (uint32_t)(((1ull << 32) + pieces - 1) / pieces);
   // miss workgroups: kFetchHostGroups in all (the host reads in flight that

@@ -137,7 +137,9 @@ constexpr int kFillThreads = kResolveThreads;
 constexpr int kHostUnroll = 1;             // host reads in flight per miss-workgroup thread
 constexpr int kFetchHostGroups = 32;       // miss workgroups per launch, at most
 constexpr int kFetchMaxSplits = 16;        // miss workgroups per request-layer, at most
-constexpr int kFetchGatherEntries = 512;   // entries per gather workgroup
+constexpr int kFetchGatherTarget = 256;    // gather workgroups per launch to aim for
+constexpr int kFetchGatherMin = 64;        // entries per gather workgroup, at least
+constexpr int kFetchGatherEntries = 512;   // entries per gather workgroup, at most
 
 struct FetchParams {
   int32_t page_shift;
