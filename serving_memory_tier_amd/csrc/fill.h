@@ -107,20 +107,31 @@ __device__ int32_t map_find(const uint32_t* tab, int32_t n, const int32_t* keys,
 }
 
 // The hot buffer's usable slots lower the slot half of their token's word.
-// Only the slot tokens are read up front (the first kT * kScanUnroll of them
-// already at the workgroup's start, `pre`); a slot's hot block is read only
-// when its token is in the table.  Ends with a barrier.
+// The first kT * kScanUnroll slots come prefetched from the workgroup's
+// start (`pre`); for the others a slot's hot block is read only when its
+// token is in the table.  Ends with a barrier.
 constexpr int kScanUnroll = 4;
 
+// The first kT * kScanUnroll slots' tokens, already masked to -1 where the
+// slot's hot block is not a usable pool block.
 __device__ __forceinline__ void prefetch_slots(const FetchParams& p, int32_t rl,
                                                int32_t (&pre)[kScanUnroll]) {
   const int32_t C = p.hot_capacity;
+  const int ps = p.page_shift;
+  const int64_t pool_blocks = p.pool_rows >> ps;
+  const int32_t r = rl / p.num_layers;
   const int32_t* stok = p.slot_token + (int64_t)rl * C;
+  const int32_t* hot = p.hot_blocks + (int64_t)r * (C >> ps);
+  int32_t hb[kScanUnroll];
 #pragma unroll
   for (int u = 0; u < kScanUnroll; ++u) {
     const int32_t q = u * kT + (int32_t)threadIdx.x;
     pre[u] = q < C ? stok[q] : -1;
+    hb[u] = q < C ? hot[q >> ps] : -1;
   }
+#pragma unroll
+  for (int u = 0; u < kScanUnroll; ++u)
+    if (hb[u] < 0 || hb[u] >= pool_blocks) pre[u] = -1;
 }
 
 __device__ void scan_slots(const FetchParams& p, int32_t rl, uint32_t* tab, int32_t n,
@@ -134,10 +145,11 @@ __device__ void scan_slots(const FetchParams& p, int32_t rl, uint32_t* tab, int3
   const int32_t* hot = p.hot_blocks + (int64_t)r * (C >> ps);
   for (int32_t q0 = 0; q0 < C; q0 += kT * kScanUnroll) {
     int32_t tq[kScanUnroll], h[kScanUnroll];
+    const bool first = q0 == 0;  // the prefetched slots, already masked
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
       const int32_t q = q0 + u * kT + tid;
-      tq[u] = q0 == 0 ? pre[u] : q < C ? stok[q] : -1;
+      tq[u] = first ? pre[u] : q < C ? stok[q] : -1;
     }
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) h[u] = tq[u] >= 0 ? map_find(tab, n, keys, tq[u]) : -1;
@@ -145,8 +157,11 @@ __device__ void scan_slots(const FetchParams& p, int32_t rl, uint32_t* tab, int3
     for (int u = 0; u < kScanUnroll; ++u) {
       if (h[u] < 0) continue;
       const int32_t q = q0 + u * kT + tid;
-      const int32_t hb = hot[q >> ps];
-      if (hb >= 0 && hb < pool_blocks) atomicMin(&tab[h[u]], (tab[h[u]] & 0xFFFF0000u) | (uint32_t)q);
+      if (!first) {
+        const int32_t hb = hot[q >> ps];
+        if (hb < 0 || hb >= pool_blocks) continue;
+      }
+      atomicMin(&tab[h[u]], (tab[h[u]] & 0xFFFF0000u) | (uint32_t)q);
     }
   }
   __syncthreads();
@@ -211,31 +226,36 @@ __device__ __forceinline__ Rl rl_view(const FetchParams& p, int32_t rl) {
   return v;
 }
 
-// Entries e0 + u * kT + tid (< lim): the token (-1 for padded and invalid
-// entries) and the row source before the hot-buffer lookup: a resident row,
-// kZeroRow, kNoHost or a tagged host row.  The block-table and host-table
-// loads are issued together.
-__device__ __forceinline__ void load_entries(const FetchParams& p, const Rl& v, int32_t e0,
-                                             int32_t lim, int32_t (&t)[kU], int32_t (&src)[kU]) {
+// Entries e0 + u * kT + tid (< lim): the tokens, -1 for padded and invalid
+// entries.
+__device__ __forceinline__ void load_tokens(const FetchParams& p, const Rl& v, int32_t e0,
+                                            int32_t lim, int32_t (&t)[kU]) {
   const int tid = threadIdx.x;
-  int32_t b[kU], hb[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int32_t e = e0 + u * kT + tid;
     t[u] = e < lim ? v.topk[e] : -1;
     if (t[u] >= v.ctx || (t[u] >> v.ps) >= p.max_pages) t[u] = -1;
   }
+}
+
+// The row source of each token before the hot-buffer lookup: a resident row,
+// kZeroRow, kNoHost or a tagged host row.  The block-table and host-table
+// loads are issued together.
+__device__ __forceinline__ void classify_tokens(const Rl& v, const int32_t* bt,
+                                                const int32_t* hbt, const int32_t (&t)[kU],
+                                                int32_t (&src)[kU]) {
+  int32_t b[kU], hb[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    b[u] = t[u] >= 0 ? v.bt[t[u] >> v.ps] : 0;
-    hb[u] = t[u] >= 0 ? v.hbt[t[u] >> v.ps] : -1;
+    b[u] = t[u] >= 0 ? bt[t[u] >> v.ps] : 0;
+    hb[u] = t[u] >= 0 ? hbt[t[u] >> v.ps] : -1;
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     src[u] = kZeroRow;
-    if (t[u] < 0) {
-      t[u] = -1;
-    } else if (b[u] >= 0) {
+    if (t[u] < 0) continue;
+    if (b[u] >= 0) {
       if (b[u] < v.pool_blocks) src[u] = (b[u] << v.ps) | (t[u] & v.pm);
     } else if (hb[u] >= 0 && hb[u] < v.host_blocks) {
       src[u] = (int32_t)(kHostTag | (uint32_t)((hb[u] << v.ps) | (t[u] & v.pm)));
@@ -243,6 +263,33 @@ __device__ __forceinline__ void load_entries(const FetchParams& p, const Rl& v, 
       src[u] = kNoHost;
     }
   }
+}
+
+// Classifies entries [lo, hi) into keys[e - lo] (the token) and src[e - lo];
+// returns whether this thread saw an entry for which `want` holds.  Ends
+// with a barrier.
+template <typename Want>
+__device__ __forceinline__ bool classify_range(const FetchParams& p, const Rl& v, int32_t lo,
+                                               int32_t hi, int32_t* keys, int32_t* src,
+                                               Want want) {
+  const int tid = threadIdx.x;
+  bool any = false;
+  for (int32_t e0 = lo; e0 < hi; e0 += kT * kU) {
+    int32_t t[kU], sv[kU];
+    load_tokens(p, v, e0, hi, t);
+    classify_tokens(v, v.bt, v.hbt, t, sv);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int32_t el = e0 + u * kT + tid - lo;
+      if (el < hi - lo) {
+        keys[el] = t[u];
+        src[el] = sv[u];
+        any |= want(sv[u]);
+      }
+    }
+  }
+  __syncthreads();
+  return any;
 }
 
 // Gather workgroup: entries [lo, hi) of one request-layer, every row but the
@@ -262,21 +309,8 @@ __device__ void fill_gather(const FetchParams& p, int32_t* lds, int32_t rl, int3
   prefetch_slots(p, rl, pre);
   for (int32_t h = tid; h < n; h += kT) tab[h] = kEmptyWord;
   if (tid == 0) *flag = 0;
-  bool any = false;
-  for (int32_t e0 = lo; e0 < hi; e0 += kT * kU) {
-    int32_t t[kU], sv[kU];
-    load_entries(p, v, e0, hi, t, sv);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int32_t el = e0 + u * kT + tid - lo;
-      if (el < E) {
-        keys[el] = t[u];
-        src[el] = sv[u];
-        any |= non_resident(sv[u]);
-      }
-    }
-  }
-  __syncthreads();
+  const bool any = classify_range(p, v, lo, hi, keys, src,
+                                  [](int32_t s) { return non_resident(s); });
   if (any) *flag = 1;
   for (int32_t el = tid; el < E; el += kT)
     if (non_resident(src[el])) map_insert(tab, n, keys, keys[el], el);
@@ -337,21 +371,8 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   prefetch_slots(p, rl, pre);
   for (int32_t h = tid; h < n; h += kT) tab[h] = kEmptyWord;
   if (tid < 4) cnt[tid] = 0;
-  bool any = false;
-  for (int32_t e0 = 0; e0 < N; e0 += kT * kU) {
-    int32_t t[kU], sv[kU];
-    load_entries(p, v, e0, N, t, sv);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int32_t e = e0 + u * kT + tid;
-      if (e < N) {
-        keys[e] = t[u];
-        src[e] = sv[u];
-        any |= is_host_row(sv[u]);
-      }
-    }
-  }
-  __syncthreads();
+  const bool any = classify_range(p, v, 0, N, keys, src,
+                                  [](int32_t s) { return is_host_row(s); });
   if (any) cnt[2] = 1;  // racing writes of the same value
   HS_FILL_MARK(1);
   for (int32_t e = tid; e < N; e += kT)

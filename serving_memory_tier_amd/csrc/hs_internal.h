@@ -134,8 +134,16 @@ hipError_t launch_move(const MoveParams& p, MoveMode mode, hipStream_t stream);
 // the host pool once per distinct token, zero rows otherwise -- while the
 // resolver runs.
 constexpr int kFillThreads = kResolveThreads;
-constexpr int kHostUnroll = 1;             // host reads in flight per miss-workgroup thread
-constexpr int kFetchHostGroups = 32;       // miss workgroups per launch, at most
+// Host reads in flight per miss-workgroup thread, and miss workgroups per
+// launch (at most): together they bound the host reads in flight.
+#ifndef HS_HOST_UNROLL
+#define HS_HOST_UNROLL 1
+#endif
+#ifndef HS_HOST_GROUPS
+#define HS_HOST_GROUPS 32
+#endif
+constexpr int kHostUnroll = HS_HOST_UNROLL;
+constexpr int kFetchHostGroups = HS_HOST_GROUPS;
 constexpr int kFetchMaxSplits = 16;        // miss workgroups per request-layer, at most
 constexpr int kFetchGatherTarget = 256;    // gather workgroups per launch to aim for
 constexpr int kFetchGatherMin = 64;        // entries per gather workgroup, at least
