@@ -41,7 +41,7 @@ from .content import PAGE, ROW_BYTES, fill_rows
 class Step:
     stamp: int
     ctx: np.ndarray            # int32 [R], context length during this step
-    topk: np.ndarray           # int32 [R, L, P, K]
+    topk: np.ndarray           # int32 [R, L // G, P, K]: one list per layer group
     bt_set: np.ndarray         # int64 [n, 3] (r, page, value) applied before the step
     hbt_set: np.ndarray        # int64 [n, 3] (r, page, value) applied before the step
     offload: np.ndarray        # int32 [n, 2] (device block, host block) copied after the step
@@ -69,6 +69,12 @@ class Workload:
     host_src: np.ndarray            # int64 [n] content source of each initial host page
     steps: list = field(default_factory=list)
     classes: np.ndarray | None = None   # int8 [R]: 0 full, 1 mixed, 2 none (informational)
+    G: int = 1                          # layers per group sharing one top-K list (IndexShare)
+
+    @property
+    def NG(self) -> int:
+        """Layer groups: top-K lists and hot-buffer states per request."""
+        return self.L // self.G
 
     @property
     def page(self) -> int:
@@ -205,6 +211,7 @@ class Spec:
     pos_keep: int = 1536             # positions 1.. : tokens kept from position 0
     shared_src: bool = False         # all requests read one source sequence (shared host pages)
     move_tail: bool = False          # null pages that leave the tail as the context grows
+    group: int = 1                   # layers per group sharing one top-K list (IndexShare)
 
 
 def _tail_first_page(ctx: int, frac: float) -> int:
@@ -216,6 +223,10 @@ def build(spec: Spec) -> Workload:
     R, L, P, K, C = spec.R, spec.L, spec.P, spec.K, spec.C
     if C % PAGE:
         raise ValueError("hot capacity must be a whole number of pages")
+    G = spec.group
+    if G < 1 or L % G:
+        raise ValueError("the layer group must divide the layers")
+    NG = L // G
     seed = spec.seed
     ctx0 = spec.ctx0.astype(np.int64)
     d = 1 if spec.append_first else 0
@@ -301,11 +312,11 @@ def build(spec: Spec) -> Workload:
                   ctx0=ctx0.astype(np.int32), block_table=bt.copy(),
                   host_block_table=hbt.copy(), hot_blocks=hot, src=src,
                   dev_pages=dev_pages, host_pages=host_pages.astype(np.int64),
-                  host_src=host_src, classes=classes)
+                  host_src=host_src, classes=classes, G=G)
 
     # steps
     ov_n, rc_n, un_n = _split_counts(K, spec.mix)
-    prev = [[None] * L for _ in range(R)]
+    prev = [[None] * NG for _ in range(R)]
     cur_bt = bt.copy()
     cur_hbt = hbt.copy()
     pend_hbt = []     # host-table entries that become valid after the previous step's offload
@@ -324,10 +335,10 @@ def build(spec: Spec) -> Workload:
             if cur_hbt[r, p] == -1:
                 raise AssertionError("a page is nulled before its host copy exists")
             cur_bt[r, p] = v
-        topk = np.full((R, L, P, K), -1, dtype=np.int32)
+        topk = np.full((R, NG, P, K), -1, dtype=np.int32)
         for r in range(R):
             c = int(ctx[r])
-            for layer in range(L):
+            for layer in range(NG):  # a layer group's list (one group per layer if G = 1)
                 kk = rng.key(seed, 0x70C, s, r, layer)
                 p0 = _mix(kk, prev[r][layer], c, K, ov_n, rc_n, spec.recent_window,
                           spec.first_recent_share)
@@ -418,10 +429,22 @@ def mixed_state(seed: int = 1004, steps: int = 16, R: int = 128) -> Workload:
                       ctx0=ctx0, classes=cls, tail_frac=0.25, P=4, shared_src=True))
 
 
+def grouped_decode(seed: int = 1005, steps: int = 16, R: int = 32, L: int = 4,
+                   G: int = 4) -> Workload:
+    """mixed_decode with IndexShare ("Use sparsity when needed": one indexer
+    layer per 4 sparse-MLA layers): 32 requests x 4 layers forming one group
+    that shares each step's top-K list and one hot buffer; 74,160 tokens, 25 %
+    resident tail, top-K 2048, hot buffer 4096, +1 token per step."""
+    return build(Spec(name="grouped_decode", seed=seed, R=R, L=L, K=2048, C=4096, steps=steps,
+                      ctx0=np.full(R, 74160), classes=np.ones(R, np.int8), tail_frac=0.25,
+                      group=G))
+
+
 CONFIGS = {
     "tiny": tiny,
     "mixed_decode": mixed_decode,
     "multi_layer": multi_layer,
     "no_residency": no_residency,
     "mixed_state": mixed_state,
+    "grouped_decode": grouped_decode,
 }

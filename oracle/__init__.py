@@ -49,7 +49,11 @@ def _load():
         lib.oracle_offload.argtypes = [i32, i32, i32, i64, i64, i64, i64, vp, vp, vp, i32]
         lib.oracle_resolve.argtypes = [i32, i32, i32, i32, i64, i64, i64, i64, i32, i32, vp, vp,
                                        vp, vp, vp, vp, vp, vp, vp, i32, u32, vp, vp, vp]
-        for f in (lib.oracle_gather, lib.oracle_offload, lib.oracle_resolve):
+        lib.oracle_resolve_grouped.argtypes = [i32, i32, i32, i32, i32, i64, i64, i64, i64, i32,
+                                               i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, u32,
+                                               vp, vp, vp]
+        for f in (lib.oracle_gather, lib.oracle_offload, lib.oracle_resolve,
+                  lib.oracle_resolve_grouped):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -145,3 +149,48 @@ def plan_replay(pool, host, block_table, host_block_table, ctx_len, hot_blocks, 
     if offload_pairs is not None and len(offload_pairs):
         offload(pool, host, offload_pairs, page)
     return res
+
+
+def resolve_grouped(pool: np.ndarray, host: np.ndarray, block_table: np.ndarray,
+                    host_block_table: np.ndarray, ctx_len: np.ndarray, hot_blocks: np.ndarray,
+                    slot_token: np.ndarray, slot_stamp: np.ndarray, topk: np.ndarray, stamp: int,
+                    group: int, gather_out: bool = True, page: int = PAGE):
+    """Grouped resolve ("Use sparsity when needed": IndexShare, one indexer
+    layer per group of sparse-MLA layers): the pool's L layers form L / group
+    groups that share one top-K list and one hot-buffer state.  Decisions are
+    made once per group; each copy is made in every layer of the group; every
+    layer gets the group's row ids.
+
+    slot_token / slot_stamp [R, L/group, C] (updated); topk [R, L/group, N] or
+    [R, L/group, P, K]; rows / stats per group; out [R, L, ...topk dims, 656].
+    Returns (rows, stats, out-or-None).
+    """
+    for a, t, n in ((pool, np.uint8, "pool"), (host, np.uint8, "host"),
+                    (block_table, np.int32, "block_table"),
+                    (host_block_table, np.int32, "host_block_table"),
+                    (ctx_len, np.int32, "ctx_len"), (hot_blocks, np.int32, "hot_blocks"),
+                    (slot_token, np.int32, "slot_token"), (slot_stamp, np.uint32, "slot_stamp"),
+                    (topk, np.int32, "topk")):
+        _check(a, t, n)
+    L, pool_rows, rb = pool.shape
+    assert group >= 1 and L % group == 0
+    NG = L // group
+    host_rows = host.shape[1]
+    R, max_pages = block_table.shape
+    C = slot_token.shape[2]
+    assert slot_token.shape == slot_stamp.shape == (R, NG, C)
+    assert hot_blocks.shape == (R, C // page)
+    assert topk.shape[:2] == (R, NG)
+    N = int(np.prod(topk.shape[2:]))
+    rows = np.empty(topk.shape, dtype=np.int32)
+    stats = np.zeros((R, NG, 8), dtype=np.int32)
+    out = (np.empty((R, L) + topk.shape[2:] + (rb,), dtype=np.uint8) if gather_out else None)
+    topk_c = np.ascontiguousarray(topk)
+    rc = _load().oracle_resolve_grouped(page, rb, L, group, C, pool_rows, pool_rows * rb,
+                                        host_rows, host_rows * rb, R, max_pages, _ptr(pool),
+                                        _ptr(host), _ptr(block_table), _ptr(host_block_table),
+                                        _ptr(ctx_len), _ptr(hot_blocks), _ptr(slot_token),
+                                        _ptr(slot_stamp), _ptr(topk_c), N, ctypes.c_uint32(stamp),
+                                        _ptr(rows), _ptr(stats), _ptr(out))
+    assert rc == 0
+    return rows, stats, out

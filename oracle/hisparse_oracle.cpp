@@ -23,6 +23,9 @@
 //   [INTEG] "Integration with the rest of vLLM": speculative decoding uses a
 //           per-step replayable resolve plan sharing the request's hot state;
 //           the hot buffer defaults to 2 x top-K rows per request.
+//   [SHARE] "Use sparsity when needed": GLM 5.3's IndexShare places one
+//           indexer layer per 4 sparse-MLA layers, so a group of layers
+//           attends to one top-K list.
 //
 // Where the pages leave a choice open the plainest reading is taken:
 //   * null placeholder / no host copy / empty slot = a negative entry;
@@ -66,10 +69,13 @@ struct Layout {
 inline bool row_in(int64_t row, int64_t rows) { return row >= 0 && row < rows; }
 
 // Resolve the N entries of one request-layer ([HOW], [FIG2], [HMA], [INTEG]).
+// `copies`, when given, receives the (host row, pool row) of every row copy
+// made into pool_l.
 void resolve_one(const Layout& lay, int32_t N, int32_t C, int32_t max_pages, int32_t ctx,
                  const int32_t* bt, const int32_t* hbt, const int32_t* hot_blocks,
                  int32_t* tok, uint32_t* stp, uint32_t stamp, const int32_t* topk,
-                 int32_t* rows, int32_t* stats, uint8_t* pool_l, const uint8_t* host_l) {
+                 int32_t* rows, int32_t* stats, uint8_t* pool_l, const uint8_t* host_l,
+                 std::vector<std::pair<int64_t, int64_t>>* copies = nullptr) {
   const int32_t page = lay.page;
   const int64_t pool_blocks = lay.pool_rows / page;
   const int64_t host_blocks = lay.host_rows / page;
@@ -160,6 +166,7 @@ void resolve_one(const Layout& lay, int32_t N, int32_t C, int32_t max_pages, int
     const int64_t dst_row = hot_row(q);
     std::memcpy(pool_l + dst_row * lay.row_bytes, host_l + src_row * lay.row_bytes,
                 (size_t)lay.row_bytes);
+    if (copies) copies->emplace_back(src_row, dst_row);
     tok[q] = u;
     stp[q] = stamp;
     uslot[miss_uidx[j]] = q;
@@ -282,6 +289,55 @@ int oracle_resolve(int32_t page, int32_t row_bytes, int32_t L, int32_t C, int64_
     }
   // Step 8: the gather reads the pool after every copy of the call.
   if (gather_out) gather_rows(lay, R, L, N, pool, rows, gather_out);
+  return 0;
+}
+
+// Grouped resolve ([SHARE]): the L layers form L / G groups of G layers that
+// share one top-K list and one hot-buffer state (slot tokens and stamps per
+// group).  A group's decisions are those of a resolve on its lists and state;
+// every copy it makes is made in each of its G layers (the layer's own host
+// row into the layer's own slot row), and every layer of the group gets the
+// group's row ids.  Arrays as oracle_resolve, but: slot_token, slot_stamp
+// [R][L/G][C]; topk, rows [R][L/G][N]; stats [R][L/G][8]; gather_out
+// [R][L][N][row_bytes] or null (out[r][l][i] = pool[l][rows[r][l/G][i]]).
+int oracle_resolve_grouped(int32_t page, int32_t row_bytes, int32_t L, int32_t G, int32_t C,
+                           int64_t pool_rows, int64_t pool_layer_stride, int64_t host_rows,
+                           int64_t host_layer_stride, int32_t R, int32_t max_pages, uint8_t* pool,
+                           const uint8_t* host, const int32_t* block_table,
+                           const int32_t* host_block_table, const int32_t* ctx_len,
+                           const int32_t* hot_blocks, int32_t* slot_token, uint32_t* slot_stamp,
+                           const int32_t* topk, int32_t N, uint32_t stamp, int32_t* rows,
+                           int32_t* stats, uint8_t* gather_out) {
+  if (G < 1 || L % G != 0) return 1;
+  Layout lay{page, row_bytes, pool_rows, host_rows, pool_layer_stride, host_layer_stride};
+  const int32_t NG = L / G;
+  for (int32_t r = 0; r < R; ++r)
+    for (int32_t g = 0; g < NG; ++g) {
+      const int64_t rg = (int64_t)r * NG + g;
+      const int32_t l0 = g * G;
+      std::vector<std::pair<int64_t, int64_t>> copies;
+      resolve_one(lay, N, C, max_pages, ctx_len[r], block_table + (int64_t)r * max_pages,
+                  host_block_table + (int64_t)r * max_pages, hot_blocks + (int64_t)r * (C / page),
+                  slot_token + rg * C, slot_stamp + rg * C, stamp, topk + rg * N, rows + rg * N,
+                  stats + rg * 8, pool + l0 * pool_layer_stride, host + l0 * host_layer_stride,
+                  &copies);
+      for (int32_t l = l0 + 1; l < l0 + G; ++l)
+        for (const auto& c : copies)
+          std::memcpy(pool + l * pool_layer_stride + c.second * row_bytes,
+                      host + l * host_layer_stride + c.first * row_bytes, (size_t)row_bytes);
+    }
+  if (gather_out) {
+    for (int32_t r = 0; r < R; ++r)
+      for (int32_t l = 0; l < L; ++l)
+        for (int32_t i = 0; i < N; ++i) {
+          const int64_t row = rows[((int64_t)r * NG + l / G) * N + i];
+          uint8_t* dst = gather_out + (((int64_t)r * L + l) * N + i) * row_bytes;
+          if (row_in(row, pool_rows))
+            std::memcpy(dst, pool + l * pool_layer_stride + row * row_bytes, (size_t)row_bytes);
+          else
+            std::memset(dst, 0, (size_t)row_bytes);
+        }
+  }
   return 0;
 }
 

@@ -36,8 +36,10 @@ class OracleRun:
         self.hbt = np.ascontiguousarray(wl.host_block_table[self.req])
         self.hot = np.ascontiguousarray(wl.hot_blocks[self.req])
         self.ctx = np.ascontiguousarray(wl.ctx0[self.req])
-        self.tok = np.full((R, wl.L, wl.C), -1, dtype=np.int32)
-        self.stp = np.zeros((R, wl.L, wl.C), dtype=np.uint32)
+        # hot-buffer state per layer group (one group per layer unless the
+        # workload's layers share top-K lists)
+        self.tok = np.full((R, wl.NG, wl.C), -1, dtype=np.int32)
+        self.stp = np.zeros((R, wl.NG, wl.C), dtype=np.uint32)
         blocks = wl.dev_pages[np.isin(wl.dev_pages[:, 0], self.req), 2]
         self.own_blocks = set(blocks.tolist())
         self.pos = {int(r): i for i, r in enumerate(self.req)}
@@ -58,6 +60,10 @@ class OracleRun:
     def resolve(self, step: hs_gen.Step, gather: bool = True, topk=None, stamp=None):
         topk = step.topk[self.req] if topk is None else topk
         stamp = step.stamp if stamp is None else stamp
+        if self.wl.G > 1:
+            return oracle.resolve_grouped(self.pool, self.host, self.bt, self.hbt, self.ctx,
+                                          self.hot, self.tok, self.stp, np.ascontiguousarray(topk),
+                                          stamp, self.wl.G, gather)
         return oracle.resolve(self.pool, self.host, self.bt, self.hbt, self.ctx, self.hot,
                               self.tok, self.stp, np.ascontiguousarray(topk), stamp, gather)
 
@@ -74,7 +80,11 @@ class OracleRun:
 def expected_content(wl: hs_gen.Workload, topk: np.ndarray, rows: np.ndarray,
                      requests=None) -> np.ndarray:
     """What every gathered row must hold, from the token alone: its synthetic
-    content where a row was resolved (row id >= 0), zeros elsewhere."""
+    content where a row was resolved (row id >= 0), zeros elsewhere.  With
+    layer groups, topk and rows are per group and the result per layer."""
+    if wl.G > 1:
+        topk = np.repeat(topk, wl.G, axis=1)
+        rows = np.repeat(rows, wl.G, axis=1)
     R, L = topk.shape[:2]
     t = topk.reshape(R, L, -1).astype(np.int64)
     lay = np.broadcast_to(np.arange(L)[None, :, None], t.shape)

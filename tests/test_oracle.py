@@ -396,3 +396,70 @@ def test_plan_equals_resolve_of_concatenation():
         assert np.array_equal(sa, sb)
         assert np.array_equal(a.tok, b.tok) and np.array_equal(a.stp, b.stp)
         assert np.array_equal(oa, expected_content(wl, step.topk, ra))
+
+
+# --------------------------------------------------------------------------
+# grouped resolve (IndexShare: layers of a group share one top-K list)
+
+def _grouped_spec(G, seed=77, L=4):
+    return hs_gen.Spec(name="grouped_small", seed=seed, R=3, L=L, K=256, C=512, steps=4,
+                       ctx0=np.array([4096, 3000, 5000]), classes=np.array([1, 1, 2], np.int8),
+                       tail_frac=0.25, mix=(0.5, 0.2, 0.3), group=G)
+
+
+@pytest.mark.parametrize("G", [2, 4])
+def test_grouped_equals_per_layer_resolve(G):
+    """A grouped resolve is the per-layer resolve of every layer of the group on
+    the group's list, from the group's state: same rows, stats, final states
+    (every layer ends with the group's state), pools and gathered rows."""
+    wl = hs_gen.build(_grouped_spec(G))
+    grp = OracleRun(wl)
+    flat = OracleRun(wl)
+    flat.tok = np.repeat(grp.tok, G, axis=1)
+    flat.stp = np.repeat(grp.stp, G, axis=1)
+    moved = 0
+    for step in wl.steps:
+        grp.pre(step)
+        flat.pre(step)
+        g_rows, g_stats, g_out = grp.resolve(step)
+        rep = np.ascontiguousarray(np.repeat(step.topk, G, axis=1))
+        f_rows, f_stats, f_out = oracle.resolve(flat.pool, flat.host, flat.bt, flat.hbt,
+                                                flat.ctx, flat.hot, flat.tok, flat.stp, rep,
+                                                step.stamp, True)
+        assert np.array_equal(f_rows, np.repeat(g_rows, G, axis=1))
+        assert np.array_equal(f_stats, np.repeat(g_stats, G, axis=1))
+        assert np.array_equal(flat.tok, np.repeat(grp.tok, G, axis=1))
+        assert np.array_equal(flat.stp, np.repeat(grp.stp, G, axis=1))
+        assert np.array_equal(flat.pool, grp.pool)
+        assert np.array_equal(f_out, g_out)
+        moved += int(g_stats[..., 2].sum())
+        grp.post(step)
+        flat.post(step)
+        assert np.array_equal(flat.host, grp.host)
+    assert moved > 0
+
+
+def test_grouped_rows_hold_each_layers_content():
+    """Every gathered row of every layer holds that layer's content of the token."""
+    wl = hs_gen.build(_grouped_spec(4))
+    run = OracleRun(wl)
+    for step in wl.steps:
+        run.pre(step)
+        rows, stats, out = run.resolve(step)
+        assert out.shape[1] == wl.L
+        assert np.array_equal(out, expected_content(wl, step.topk, rows))
+        run.post(step)
+
+
+def test_grouped_with_one_layer_per_group_is_resolve():
+    wl = hs_gen.build(_grouped_spec(1))
+    a, b = OracleRun(wl), OracleRun(wl)
+    for step in wl.steps[:2]:
+        a.pre(step)
+        b.pre(step)
+        ra = a.resolve(step)
+        rb = oracle.resolve_grouped(b.pool, b.host, b.bt, b.hbt, b.ctx, b.hot, b.tok, b.stp,
+                                    np.ascontiguousarray(step.topk), step.stamp, 1, True)
+        for x, y in zip(ra, rb):
+            assert np.array_equal(x, y)
+        assert np.array_equal(a.pool, b.pool) and np.array_equal(a.tok, b.tok)

@@ -40,6 +40,10 @@ MUTANTS = {
     "offload_skips_last_layer": ("for (int32_t l = 0; l < L; ++l)\n      std::memcpy(host",
                                  "for (int32_t l = 0; l + 1 < L; ++l)\n      std::memcpy(host"),
     "dup_count_wrong": ("stats[6] = n_nonpad - (int32_t)nonpad.size();", "stats[6] = 0;"),
+    "grouped_copies_skip_last_layer": ("for (int32_t l = l0 + 1; l < l0 + G; ++l)",
+                                       "for (int32_t l = l0 + 1; l < l0 + G - 1; ++l)"),
+    "grouped_gather_wrong_group": ("const int64_t row = rows[((int64_t)r * NG + l / G) * N + i];",
+                                   "const int64_t row = rows[((int64_t)r * NG + l % NG) * N + i];"),
 }
 
 FAST_PINS = ["tests/test_oracle.py::test_worked_example_steps",
@@ -49,7 +53,9 @@ FAST_PINS = ["tests/test_oracle.py::test_worked_example_steps",
              "tests/test_oracle.py::test_matches_sequential_restatement",
              "tests/test_oracle.py::test_empty_buffer_fills_slots_in_token_order",
              "tests/test_oracle.py::test_offload_copies_every_layer_and_leaves_pool",
-             "tests/test_oracle.py::test_tiny_workload_invariants"]
+             "tests/test_oracle.py::test_tiny_workload_invariants",
+             "tests/test_oracle.py::test_grouped_equals_per_layer_resolve",
+             "tests/test_oracle.py::test_grouped_rows_hold_each_layers_content"]
 
 
 def test_unmutated_source_passes_the_pins():
