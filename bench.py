@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="mixed_decode",
-                    choices=["mixed_decode", "no_residency", "mixed_state", "multi_layer"])
+                    choices=["mixed_decode", "no_residency", "mixed_state", "multi_layer", "grouped_decode"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -68,6 +68,8 @@ def build_workload(name: str, n_steps: int):
         return hs_gen.no_residency(steps=n_steps)
     if name == "mixed_state":
         return hs_gen.mixed_state(steps=n_steps)
+    if name == "grouped_decode":
+        return hs_gen.grouped_decode(steps=n_steps)
     return hs_gen.multi_layer(turns=n_steps)
 
 
@@ -103,14 +105,15 @@ def measured_traffic(kernel: str, workload: str):
 def decide_hbm_bytes(wl, stats_sum, n_launches):
     """Algorithmic HBM bytes of the decision kernel per launch.
 
-    Per request-layer: the slot tokens and stamps are read once (8 B/slot).
-    Per entry: the index (4 B), its block-table entry (4 B), its row (4 B).
-    Per hit: the refreshed stamp (4 B).  Per miss: the host-table entry (4 B)
-    and the slot's new token and stamp (8 B).
+    Per request-layer (per layer group when layers share lists): the slot
+    tokens and stamps are read once (8 B/slot).  Per entry: the index (4 B),
+    its block-table entry (4 B), its row (4 B).  Per hit: the refreshed stamp
+    (4 B).  Per miss: the host-table entry (4 B) and the slot's new token and
+    stamp (8 B).
     """
-    R, L, N = wl.R, wl.L, wl.P * wl.K
+    R, NG, N = wl.R, wl.NG, wl.P * wl.K
     hits, misses = stats_sum[1], stats_sum[2]
-    return R * L * wl.C * 8 + R * L * N * 12 + (hits * 4 + misses * 12) / n_launches
+    return R * NG * wl.C * 8 + R * NG * N * 12 + (hits * 4 + misses * 12) / n_launches
 
 
 def fetch_bytes(wl, stats_sum, n_launches):
@@ -119,20 +122,21 @@ def fetch_bytes(wl, stats_sum, n_launches):
     every resident or hit entry reads its 656-B row from the pool; every entry
     writes its 656-B output row.  The fill's reads of the entries, tables and
     slot tokens are the resolver's reads again (L2 hits in the fused launch)
-    and are counted once, in decide_hbm_bytes."""
+    and are counted once, in decide_hbm_bytes.  With layer groups every miss
+    and every row is moved once per layer of the group."""
     R, L, N = wl.R, wl.L, wl.P * wl.K
     entries = R * L * N
-    m = (stats_sum[2] + stats_sum[3]) / n_launches
+    m = (stats_sum[2] + stats_sum[3]) / n_launches * wl.G
     return m * ROW, (entries - m) * ROW + entries * ROW
 
 
 def commit_bytes(wl, stats_sum, n_launches):
     """HBM bytes of the commit per launch: every entry's code (4 B); per
     assigned miss its row read from the output and written into the slot, the
-    slot's token and the final row id."""
-    R, L, N = wl.R, wl.L, wl.P * wl.K
+    slot's token and the final row id (the rows once per layer of a group)."""
+    R, NG, N = wl.R, wl.NG, wl.P * wl.K
     a = stats_sum[2] / n_launches
-    return R * L * N * 4 + a * (2 * ROW + 8)
+    return R * NG * N * 4 + a * (2 * ROW * wl.G + 8)
 
 
 def main():
@@ -168,7 +172,7 @@ def main():
     N = wl.P * wl.K
     entries = wl.R * wl.L * N
     dev.stage_steps()
-    stats_all = torch.zeros((n_steps, wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
+    stats_all = torch.zeros((n_steps, wl.R, wl.NG, 8), dtype=torch.int32, device="cuda")
     hev = HipRuntime()
 
     def step(i, sp):
@@ -235,8 +239,11 @@ def main():
                          "hbm_bytes": int(fused_hbm),
                          "hbm_gbps": round(fused_hbm / fused_us / 1e3, 1)},
         "commit": {"us": round(commit_us, 2), "hbm_bytes": int(com_bytes),
-                   "hbm_gbps": round(com_bytes / commit_us / 1e3, 1)},
+                   "hbm_gbps": round(com_bytes / max(commit_us, 1e-3) / 1e3, 1)},
     }
+    if wl.G > 1:
+        kernels["resolve_fill"]["note"] = ("layer groups of %d: the whole hs_resolve_grouped call "
+                                           "(fused launch, commit, offload)" % wl.G)
     if off:
         page_layers = [wl.steps[W + K + j].offload.shape[0] * wl.L for j, _ in off]
         off_us = 1e3 * float(np.mean([ms for _, ms in off]))
@@ -250,7 +257,7 @@ def main():
     last = W + K + KE - 1
     NR = args.hit_replays
     rep = [[hev.new_event() for _ in range(4)] for _ in range(NR)]
-    rep_stats = torch.zeros((wl.R, wl.L, 8), dtype=torch.int32, device="cuda")
+    rep_stats = torch.zeros((wl.R, wl.NG, 8), dtype=torch.int32, device="cuda")
     for j in range(NR):
         dev.launch_step_timed(last, hev, sp0, rep[j], stats=rep_stats, offload=False)
     torch.cuda.synchronize()
@@ -292,7 +299,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": wl.name, "requests": wl.R, "layers": wl.L, "positions": wl.P,
                    "top_k": wl.K, "hot_capacity": wl.C, "context": int(wl.ctx0.max()),
-                   "row_bytes": ROW, "page_size": PAGE, "launch": launch},
+                   "row_bytes": ROW, "page_size": PAGE, "layer_group": wl.G, "launch": launch},
         "hbm": {"achieved": round(step_hbm_k / (wall / K) / 1e9, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(step_hbm_k / (wall / K) / 1e9 / HBM_PEAK_GBPS, 4)},

@@ -178,6 +178,29 @@ hs_status hs_plan_replay(const hs_layout* layout, const hs_batch* batch, const i
                          int32_t n_offload, hipStream_t stream);
 
 /*
+ * hs_resolve_grouped -- the resolve for layers that share a top-K list
+ * ("Use sparsity when needed": GLM 5.3's IndexShare places one indexer layer
+ * per 4 sparse-MLA layers, so those layers attend to the same tokens).  The
+ * layout's L layers form L / G groups of G consecutive layers; each group of
+ * a request has one top-K list and one hot-buffer state.  The decisions are
+ * made once per group, exactly as hs_plan_replay makes them for one layer;
+ * every copy into a slot is made in each of the group's layers (each layer's
+ * own host row into its own slot row), and every layer of a group receives
+ * the group's rows.  G = 1 is hs_plan_replay.
+ * Arguments: group_layers = G >= 1, dividing layout->num_layers; the batch's
+ * slot_token and slot_stamp are [R][L/G][C]; topk and row_ids are
+ * [R][L/G][P*K]; stats [R][L/G][8]; gather_out (may be NULL)
+ * [R][L][P*K][row_bytes], gather_out[r][l][i] from layer l's pool plane at
+ * row_ids[r][l/G][i]; the offload pairs copy every layer, as in
+ * hs_plan_replay.
+ * Errors: as hs_plan_replay; G not dividing L is HS_ERR_INVALID_ARGUMENT.
+ */
+hs_status hs_resolve_grouped(const hs_layout* layout, const hs_batch* batch, int32_t group_layers,
+                             const int32_t* topk, int32_t num_pos, int32_t top_k, uint32_t stamp,
+                             int32_t* row_ids, uint8_t* gather_out, int32_t* stats,
+                             const int32_t* offload_pairs, int32_t n_offload, hipStream_t stream);
+
+/*
  * The stages of hs_resolve / hs_plan_replay, for callers that time or
  * schedule them on their own streams.
  *

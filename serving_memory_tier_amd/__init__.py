@@ -4,6 +4,7 @@ Argument marshalling only: every step of the path runs in the HIP kernels of
 ``libhisparse.so`` (built from ``csrc/`` for gfx950).  PyTorch supplies device
 memory and streams.  The names mirror the C ABI in ``include/hisparse.h``:
 ``hs_resolve``, ``hs_gather``, ``hs_offload_prefix_pages``, ``hs_plan_replay``,
+``hs_resolve_grouped`` (layers sharing a top-K list),
 the resolver's stages (``hs_resolve_decide``, ``hs_resolve_fetch``,
 ``hs_resolve_move``, ``hs_resolve_commit``), plus pinned host-pool helpers.  There is no fallback: if the library is
 missing or fails to load, every call raises.
@@ -14,7 +15,8 @@ from ._lib import (EXPORTS, HS_ERR_HIP, HS_ERR_INVALID_ARGUMENT, HS_ERR_LAUNCH,
                    LIB_PATH, HsBatch, HsError, HsLayout, lib)
 from .api import (HostPool, batch_of, hs_gather, hs_host_alloc, hs_host_device_pointer,
                   hs_host_free, hs_offload_prefix_pages, hs_plan_replay, hs_resolve,
-                  hs_resolve_commit, hs_resolve_decide, hs_resolve_fetch, hs_resolve_move,
+                  hs_resolve_commit, hs_resolve_decide, hs_resolve_fetch, hs_resolve_grouped,
+                  hs_resolve_move,
                   hs_status_string, layout_of)
 
 __all__ = [
@@ -22,7 +24,8 @@ __all__ = [
     "HS_ERR_HIP", "HS_MAX_ENTRIES", "HS_MAX_HOT_CAPACITY", "LIB_PATH",
     "HsLayout", "HsBatch",
     "HsError", "HostPool", "lib", "layout_of", "batch_of", "hs_resolve", "hs_gather",
-    "hs_offload_prefix_pages", "hs_plan_replay", "hs_resolve_decide", "hs_resolve_fetch",
+    "hs_offload_prefix_pages", "hs_plan_replay", "hs_resolve_grouped", "hs_resolve_decide",
+    "hs_resolve_fetch",
     "hs_resolve_move", "hs_resolve_commit",
     "hs_status_string", "hs_host_alloc",
     "hs_host_free", "hs_host_device_pointer",

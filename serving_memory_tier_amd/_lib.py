@@ -17,6 +17,7 @@ HS_MAX_ENTRIES = 8192
 HS_MAX_HOT_CAPACITY = 8192
 
 EXPORTS = ("hs_resolve", "hs_gather", "hs_offload_prefix_pages", "hs_plan_replay",
+           "hs_resolve_grouped",
            "hs_resolve_decide", "hs_resolve_fetch", "hs_resolve_move", "hs_resolve_commit",
            "hs_status_string", "hs_last_error", "hs_host_alloc", "hs_host_free",
            "hs_host_device_pointer")
@@ -60,6 +61,7 @@ def lib():
         L.hs_gather.argtypes = [lay, vp, vp, i32, i32, vp, vp]
         L.hs_offload_prefix_pages.argtypes = [lay, vp, vp, vp, i32, vp]
         L.hs_plan_replay.argtypes = [lay, bat, vp, i32, i32, u32, vp, vp, vp, vp, i32, vp]
+        L.hs_resolve_grouped.argtypes = [lay, bat, i32, vp, i32, i32, u32, vp, vp, vp, vp, i32, vp]
         L.hs_resolve_decide.argtypes = [lay, bat, vp, i32, i32, u32, vp, vp, vp, vp]
         L.hs_resolve_fetch.argtypes = [lay, bat, vp, i32, i32, vp, vp]
         L.hs_resolve_move.argtypes = [lay, bat, vp, i32, i32, vp, vp, vp]

@@ -80,6 +80,16 @@ def hs_plan_replay(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: 
            "hs_plan_replay")
 
 
+def hs_resolve_grouped(layout: HsLayout, batch: HsBatch, group_layers: int, topk, num_pos: int,
+                       top_k: int, stamp: int, row_ids, gather_out, stats, offload_pairs=None,
+                       n_offload: int = 0, stream=None) -> None:
+    _check(lib().hs_resolve_grouped(ctypes.byref(layout), ctypes.byref(batch), group_layers,
+                                    _ptr(topk), num_pos, top_k, ctypes.c_uint32(stamp),
+                                    _ptr(row_ids), _ptr(gather_out), _ptr(stats),
+                                    _ptr(offload_pairs), n_offload, _stream(stream)),
+           "hs_resolve_grouped")
+
+
 def hs_resolve_decide(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: int,
                       stamp: int, row_ids, gather_out, stats, stream=None) -> None:
     _check(lib().hs_resolve_decide(ctypes.byref(layout), ctypes.byref(batch), _ptr(topk), num_pos,

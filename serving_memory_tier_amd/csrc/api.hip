@@ -141,12 +141,16 @@ hs::FetchParams fetch_params(const hs_layout* lay, const hs_batch* b, const int3
 
 hs_status launch_decide(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
                         int32_t N, uint32_t stamp, int32_t* row_ids, int32_t* stats,
-                        hipStream_t stream, uint8_t* fill_out = nullptr) {
+                        hipStream_t stream, uint8_t* fill_out = nullptr, int32_t group = 1) {
   if ((int64_t)b->num_reqs * lay->num_layers == 0) return HS_OK;
+  // with layer groups the resolver runs once per (request, group): the state,
+  // lists and row ids are per group
+  hs_layout glay = *lay;
+  glay.num_layers = lay->num_layers / group;
   hs::ResolveParams p;
   p.page_shift = log2i(lay->page_size);
   p.row_bytes = lay->row_bytes;
-  p.num_layers = lay->num_layers;
+  p.num_layers = glay.num_layers;
   p.hot_capacity = lay->hot_capacity;
   p.pool_rows = lay->pool_rows;
   p.host_rows = lay->host_rows;
@@ -168,7 +172,9 @@ hs_status launch_decide(const hs_layout* lay, const hs_batch* b, const int32_t* 
   p.row_ids = row_ids;
   p.stats = stats;
   if (fill_out) {
-    const hs::FetchParams f = fetch_params(lay, b, topk, N, fill_out);
+    hs::FetchParams f = fetch_params(&glay, b, topk, N, fill_out);
+    f.group = group;
+    f.layers = lay->num_layers;
     return from_hip(hs::launch_resolve(p, &f, stream), "resolver launch");
   }
   return from_hip(hs::launch_resolve(p, nullptr, stream), "resolver launch");
@@ -176,9 +182,12 @@ hs_status launch_decide(const hs_layout* lay, const hs_batch* b, const int32_t* 
 
 hs_status launch_move_mode(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
                            int32_t N, int32_t* row_ids, uint8_t* gather_out, hs::MoveMode mode,
-                           hipStream_t stream) {
+                           hipStream_t stream, int32_t group = 1) {
   if ((int64_t)b->num_reqs * lay->num_layers == 0) return HS_OK;
   hs::MoveParams g = move_params(lay, b->kv_pool, row_ids, b->num_reqs, N, gather_out);
+  g.num_layers = lay->num_layers / group;  // codes and row ids per (request, group)
+  g.group = group;
+  g.layers = lay->num_layers;
   g.pool_w = b->kv_pool;
   g.host = b->host_pool;
   g.host_rows = lay->host_rows;
@@ -214,6 +223,8 @@ hs::FetchParams fetch_params(const hs_layout* lay, const hs_batch* b, const int3
   f.topk = topk;
   f.entries = N;
   f.out = gather_out;
+  f.group = 1;
+  f.layers = lay->num_layers;
   return f;
 }
 
@@ -239,22 +250,24 @@ bool fetch_fits(const hs_layout* lay, int32_t N) {
 hs_status resolve_common(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
                          int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
                          uint8_t* gather_out, int32_t* stats, const int32_t* offload_pairs,
-                         int32_t n_offload, hipStream_t stream) {
+                         int32_t n_offload, hipStream_t stream, int32_t group = 1) {
   hs_status s = check_resolve(lay, b, topk, num_pos, top_k, row_ids);
   if (s != HS_OK) return s;
+  if (group < 1 || lay->num_layers % group != 0) return HS_ERR_INVALID_ARGUMENT;
   if (!stats || stamp == 0) return HS_ERR_INVALID_ARGUMENT;
   if ((s = check_offload(n_offload)) != HS_OK) return s;
   if (n_offload > 0 && (!offload_pairs || !b->kv_pool || !b->host_pool))
     return HS_ERR_INVALID_ARGUMENT;
   const int32_t N = num_pos * top_k;
   if (gather_out && fetch_fits(lay, N)) {
-    s = launch_decide(lay, b, topk, N, stamp, row_ids, stats, stream, gather_out);
+    s = launch_decide(lay, b, topk, N, stamp, row_ids, stats, stream, gather_out, group);
     if (s != HS_OK) return s;
-    s = launch_move_mode(lay, b, topk, N, row_ids, gather_out, hs::kMoveCommit, stream);
+    s = launch_move_mode(lay, b, topk, N, row_ids, gather_out, hs::kMoveCommit, stream, group);
     if (s != HS_OK) return s;
   } else {
-    if ((s = launch_decide(lay, b, topk, N, stamp, row_ids, stats, stream)) != HS_OK) return s;
-    s = launch_move_mode(lay, b, topk, N, row_ids, gather_out, hs::kMoveFused, stream);
+    s = launch_decide(lay, b, topk, N, stamp, row_ids, stats, stream, nullptr, group);
+    if (s != HS_OK) return s;
+    s = launch_move_mode(lay, b, topk, N, row_ids, gather_out, hs::kMoveFused, stream, group);
     if (s != HS_OK) return s;
   }
   if (n_offload > 0) {
@@ -282,6 +295,15 @@ hs_status hs_plan_replay(const hs_layout* layout, const hs_batch* batch, const i
                          int32_t n_offload, hipStream_t stream) {
   return resolve_common(layout, batch, topk, num_pos, top_k, stamp, row_ids, gather_out, stats,
                         offload_pairs, n_offload, stream);
+}
+
+hs_status hs_resolve_grouped(const hs_layout* layout, const hs_batch* batch, int32_t group_layers,
+                             const int32_t* topk, int32_t num_pos, int32_t top_k, uint32_t stamp,
+                             int32_t* row_ids, uint8_t* gather_out, int32_t* stats,
+                             const int32_t* offload_pairs, int32_t n_offload,
+                             hipStream_t stream) {
+  return resolve_common(layout, batch, topk, num_pos, top_k, stamp, row_ids, gather_out, stats,
+                        offload_pairs, n_offload, stream, group_layers);
 }
 
 hs_status hs_resolve_decide(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,

@@ -46,14 +46,15 @@ __global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_p
   const int32_t N = p.rows_per_rl;
   const int32_t ne = min(kEPW, N - e0);
   const int32_t r = rl / p.num_layers;
-  const int32_t layer = rl - r * p.num_layers;
+  const int32_t group = MODE == kMoveFused ? p.group : 1;
+  const int32_t l0 = (rl - r * p.num_layers) * group;  // first layer of the group
+  const int32_t layers = p.layers > 0 ? p.layers : p.num_layers;
   const int32_t pieces = PIECES > 0 ? PIECES : (p.row_bytes >> 4);
   const int32_t npieces = ne * pieces;
   const int ps = p.page_shift;
   const int32_t pm = (1 << ps) - 1;
   int32_t* rows = p.row_ids + (int64_t)rl * N + e0;
-  const uint8_t* pool_l = p.pool + (int64_t)layer * p.pool_stride;
-  uint8_t* out = p.out ? p.out + ((int64_t)rl * N + e0) * p.row_bytes : nullptr;
+  const int64_t out_stride = (int64_t)N * p.row_bytes;  // between layers of the output
   constexpr bool kSlots = MODE == kMoveFused;
 
   const int32_t* topk = nullptr;
@@ -66,15 +67,21 @@ __global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_p
   if (kSlots) {
     topk = p.topk + (int64_t)rl * N + e0;
     hot = p.hot_blocks + (int64_t)r * (p.hot_capacity >> ps);
-    slot_l = p.pool_w + (int64_t)layer * p.pool_stride;
     stok = p.slot_token + (int64_t)rl * p.hot_capacity;
   }
   if (MODE == kMoveFused) {
     hbt = p.host_block_table + (int64_t)r * p.max_pages;
-    host_l = p.host + (int64_t)layer * p.host_stride;
     host_blocks = p.host_rows >> ps;
   }
 
+  for (int32_t lj = 0; lj < group; ++lj) {  // each layer of the group
+  const int32_t layer = l0 + lj;
+  const uint8_t* pool_l = p.pool + (int64_t)layer * p.pool_stride;
+  uint8_t* out = p.out ? p.out + ((int64_t)r * layers + layer) * out_stride +
+                             (int64_t)e0 * p.row_bytes
+                       : nullptr;
+  if (kSlots) slot_l = p.pool_w + (int64_t)layer * p.pool_stride;
+  if (MODE == kMoveFused) host_l = p.host + (int64_t)layer * p.host_stride;
   for (int32_t base = 0; base < npieces; base += 64 * kU) {
     u32x4 v[kU];
     uint8_t* slot_dst[kU];
@@ -126,6 +133,7 @@ __global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_p
       if (kSlots && slot_dst[u]) *reinterpret_cast<u32x4*>(slot_dst[u]) = v[u];
     }
   }
+  }  // layers of the group
   if (kSlots && lane < ne) {
     // only this wave reads these entries' codes, and all its reads are done
     const int32_t code = rows[lane];
@@ -160,15 +168,17 @@ __global__ void __launch_bounds__(kT) commit_kernel(MoveParams p, int32_t chunks
   const int32_t N = p.rows_per_rl;
   const int32_t ne = min(64, N - e0);
   const int32_t r = rl / p.num_layers;
-  const int32_t layer = rl - r * p.num_layers;
+  const int32_t l0 = (rl - r * p.num_layers) * p.group;  // first layer of the group
+  const int32_t layers = p.layers > 0 ? p.layers : p.num_layers;
   const int32_t pieces = PIECES > 0 ? PIECES : (p.row_bytes >> 4);
   const int ps = p.page_shift;
   const int32_t pm = (1 << ps) - 1;
   int32_t* rows = p.row_ids + (int64_t)rl * N + e0;
-  uint8_t* out = p.out + ((int64_t)rl * N + e0) * p.row_bytes;
+  const int64_t out_stride = (int64_t)N * p.row_bytes;  // between layers of the output
+  uint8_t* out0 = p.out + ((int64_t)r * layers + l0) * out_stride + (int64_t)e0 * p.row_bytes;
   const int32_t* topk = p.topk + (int64_t)rl * N + e0;
   const int32_t* hot = p.hot_blocks + (int64_t)r * (p.hot_capacity >> ps);
-  uint8_t* slot_l = p.pool_w + (int64_t)layer * p.pool_stride;
+  uint8_t* slot0 = p.pool_w + (int64_t)l0 * p.pool_stride;
   int32_t* stok = p.slot_token + (int64_t)rl * p.hot_capacity;
 
   const int32_t code = lane < ne ? rows[lane] : 0;
@@ -204,29 +214,33 @@ __global__ void __launch_bounds__(kT) commit_kernel(MoveParams p, int32_t chunks
   const int32_t n = __popcll(m);
   const int32_t total = n * pieces;
   const int64_t dst_stride = p.row_bytes;
-  for (int32_t g0 = 0; g0 < total; g0 += 64 * kU) {
-    u32x4 v[kU];
-    uint8_t* dst[kU];
+  for (int32_t l = 0; l < p.group; ++l) {  // each layer of the group
+    uint8_t* out = out0 + l * out_stride;
+    uint8_t* slot_l = slot0 + l * p.pool_stride;
+    for (int32_t g0 = 0; g0 < total; g0 += 64 * kU) {
+      u32x4 v[kU];
+      uint8_t* dst[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int32_t g = g0 + u * 64 + lane;
-      dst[u] = nullptr;
-      v[u] = u32x4{0u, 0u, 0u, 0u};
-      if (g < total) {
-        const int32_t j = g / pieces;
-        const int32_t pc = g - j * pieces;
-        const int32_t w = work_e[wv][j];
-        if (w < 0) {
-          dst[u] = out + (int64_t)(-1 - w) * dst_stride + pc * 16;
-        } else {
-          v[u] = *reinterpret_cast<const u32x4*>(out + (int64_t)w * dst_stride + pc * 16);
-          dst[u] = slot_l + (int64_t)work_row[wv][j] * dst_stride + pc * 16;
+      for (int u = 0; u < kU; ++u) {
+        const int32_t g = g0 + u * 64 + lane;
+        dst[u] = nullptr;
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        if (g < total) {
+          const int32_t j = g / pieces;
+          const int32_t pc = g - j * pieces;
+          const int32_t w = work_e[wv][j];
+          if (w < 0) {
+            dst[u] = out + (int64_t)(-1 - w) * dst_stride + pc * 16;
+          } else {
+            v[u] = *reinterpret_cast<const u32x4*>(out + (int64_t)w * dst_stride + pc * 16);
+            dst[u] = slot_l + (int64_t)work_row[wv][j] * dst_stride + pc * 16;
+          }
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
-      if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = v[u];
+      for (int u = 0; u < kU; ++u)
+        if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = v[u];
+    }
   }
 }
 

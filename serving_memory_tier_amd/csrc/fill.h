@@ -194,11 +194,14 @@ constexpr uint32_t kHostTag = 0x80000000u;
 __device__ __forceinline__ bool is_host_row(int32_t v) { return v < kNoHost; }
 __device__ __forceinline__ bool non_resident(int32_t v) { return v == kNoHost || is_host_row(v); }
 
-// The request-layer's pointers and sizes.
+// A request-layer's (or a layer group's) pointers and sizes.  With layer
+// groups, rl counts (request, group) pairs; pool_l, host_l and out address
+// the group's first layer, the next layers follow at the strides.
 struct Rl {
-  int32_t N, ps, pm, pieces, ctx;
+  int32_t N, ps, pm, pieces, ctx, group;
   uint32_t magic;
   int64_t pool_blocks, host_blocks;
+  int64_t pool_stride, host_stride, out_stride;
   const int32_t *topk, *bt, *hbt, *hot;
   const uint8_t *pool_l, *host_l;
   uint8_t* out;
@@ -207,21 +210,25 @@ struct Rl {
 __device__ __forceinline__ Rl rl_view(const FetchParams& p, int32_t rl) {
   Rl v;
   const int32_t r = rl / p.num_layers;
-  const int32_t layer = rl - r * p.num_layers;
+  const int32_t l0 = (rl - r * p.num_layers) * p.group;
   v.N = p.entries;
   v.ps = p.page_shift;
   v.pm = (1 << v.ps) - 1;
   v.pieces = p.row_bytes >> 4;
+  v.group = p.group;
   v.magic = p.piece_magic;
   v.pool_blocks = p.pool_rows >> v.ps;
   v.host_blocks = p.host_rows >> v.ps;
+  v.pool_stride = p.pool_stride;
+  v.host_stride = p.host_stride;
+  v.out_stride = (int64_t)v.N * p.row_bytes;
   v.topk = p.topk + (int64_t)rl * v.N;
   v.bt = p.block_table + (int64_t)r * p.max_pages;
   v.hbt = p.host_block_table + (int64_t)r * p.max_pages;
   v.hot = p.hot_blocks + (int64_t)r * (p.hot_capacity >> v.ps);
-  v.pool_l = p.pool + (int64_t)layer * p.pool_stride;
-  v.host_l = p.host + (int64_t)layer * p.host_stride;
-  v.out = p.out + (int64_t)rl * v.N * p.row_bytes;
+  v.pool_l = p.pool + (int64_t)l0 * p.pool_stride;
+  v.host_l = p.host + (int64_t)l0 * p.host_stride;
+  v.out = p.out + ((int64_t)r * p.layers + l0) * v.out_stride;
   v.ctx = p.ctx_len[r];
   return v;
 }
@@ -328,27 +335,31 @@ __device__ void fill_gather(const FetchParams& p, int32_t* lds, int32_t rl, int3
   }
   HS_FILL_MARK(2);
   const int32_t total = E * v.pieces;
-  for (int32_t g0 = 0; g0 < total; g0 += kT * kU) {
-    u32x4 val[kU];
-    uint8_t* dst[kU];
+  for (int32_t j = 0; j < v.group; ++j) {  // each layer of the group
+    const uint8_t* pool_l = v.pool_l + j * v.pool_stride;
+    uint8_t* out = v.out + j * v.out_stride;
+    for (int32_t g0 = 0; g0 < total; g0 += kT * kU) {
+      u32x4 val[kU];
+      uint8_t* dst[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int32_t g = g0 + u * kT + tid;
-      dst[u] = nullptr;
-      val[u] = u32x4{0u, 0u, 0u, 0u};
-      if (g < total) {
-        const int32_t el = pdiv(g, v.magic);
-        const int32_t pc = g - el * v.pieces;
-        const int32_t code = src[el];
-        if (code != kSkip) dst[u] = v.out + (int64_t)(lo + el) * p.row_bytes + pc * 16;
-        if (code >= 0)
-          val[u] = *reinterpret_cast<const u32x4*>(v.pool_l + (int64_t)code * p.row_bytes +
-                                                   pc * 16);
+      for (int u = 0; u < kU; ++u) {
+        const int32_t g = g0 + u * kT + tid;
+        dst[u] = nullptr;
+        val[u] = u32x4{0u, 0u, 0u, 0u};
+        if (g < total) {
+          const int32_t el = pdiv(g, v.magic);
+          const int32_t pc = g - el * v.pieces;
+          const int32_t code = src[el];
+          if (code != kSkip) dst[u] = out + (int64_t)(lo + el) * p.row_bytes + pc * 16;
+          if (code >= 0)
+            val[u] = *reinterpret_cast<const u32x4*>(pool_l + (int64_t)code * p.row_bytes +
+                                                     pc * 16);
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
-      if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
+      for (int u = 0; u < kU; ++u)
+        if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
+    }
   }
 }
 
@@ -411,27 +422,32 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   const int32_t n_dup = cnt[1];
   HS_FILL_MARK(3);
 
-  // ---- host rows of the first entries, kHostUnroll reads in flight a thread
+  // ---- host rows of the first entries, in each layer of the group,
+  // kHostUnroll reads in flight a thread
   const int32_t total = n_first * v.pieces;
-  for (int32_t g0 = 0; g0 < total; g0 += kT * kHostUnroll) {
-    u32x4 val[kHostUnroll];
-    uint8_t* dst[kHostUnroll];
+  for (int32_t l = 0; l < v.group; ++l) {
+    const uint8_t* host_l = v.host_l + l * v.host_stride;
+    uint8_t* out = v.out + l * v.out_stride;
+    for (int32_t g0 = 0; g0 < total; g0 += kT * kHostUnroll) {
+      u32x4 val[kHostUnroll];
+      uint8_t* dst[kHostUnroll];
 #pragma unroll
-    for (int u = 0; u < kHostUnroll; ++u) {
-      const int32_t g = g0 + u * kT + tid;
-      dst[u] = nullptr;
-      if (g < total) {
-        const int32_t j = pdiv(g, v.magic);
-        const int32_t pc = g - j * v.pieces;
-        const int32_t e = list[j];
-        const int64_t hrow = (int64_t)((uint32_t)src[e] & ~kHostTag);
-        val[u] = *reinterpret_cast<const u32x4*>(v.host_l + hrow * p.row_bytes + pc * 16);
-        dst[u] = v.out + (int64_t)e * p.row_bytes + pc * 16;
+      for (int u = 0; u < kHostUnroll; ++u) {
+        const int32_t g = g0 + u * kT + tid;
+        dst[u] = nullptr;
+        if (g < total) {
+          const int32_t j = pdiv(g, v.magic);
+          const int32_t pc = g - j * v.pieces;
+          const int32_t e = list[j];
+          const int64_t hrow = (int64_t)((uint32_t)src[e] & ~kHostTag);
+          val[u] = *reinterpret_cast<const u32x4*>(host_l + hrow * p.row_bytes + pc * 16);
+          dst[u] = out + (int64_t)e * p.row_bytes + pc * 16;
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kHostUnroll; ++u)
-      if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
+      for (int u = 0; u < kHostUnroll; ++u)
+        if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
+    }
   }
   if (n_dup == 0) return;
   __syncthreads();  // this workgroup's row writes are visible to it
@@ -439,24 +455,27 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   // ---- later entries of the owned miss tokens copy the first entry's row
   const int32_t total2 = n_dup * v.pieces;
   const int32_t* dl = list + p.lds_n - n_dup;
-  for (int32_t g0 = 0; g0 < total2; g0 += kT * kU) {
-    u32x4 val[kU];
-    uint8_t* dst[kU];
+  for (int32_t l = 0; l < v.group; ++l) {
+    uint8_t* out = v.out + l * v.out_stride;
+    for (int32_t g0 = 0; g0 < total2; g0 += kT * kU) {
+      u32x4 val[kU];
+      uint8_t* dst[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int32_t g = g0 + u * kT + tid;
-      dst[u] = nullptr;
-      if (g < total2) {
-        const int32_t j = pdiv(g, v.magic);
-        const int32_t pc = g - j * v.pieces;
-        const int32_t e = dl[j];
-        val[u] = *reinterpret_cast<const u32x4*>(v.out + (int64_t)src[e] * p.row_bytes + pc * 16);
-        dst[u] = v.out + (int64_t)e * p.row_bytes + pc * 16;
+      for (int u = 0; u < kU; ++u) {
+        const int32_t g = g0 + u * kT + tid;
+        dst[u] = nullptr;
+        if (g < total2) {
+          const int32_t j = pdiv(g, v.magic);
+          const int32_t pc = g - j * v.pieces;
+          const int32_t e = dl[j];
+          val[u] = *reinterpret_cast<const u32x4*>(out + (int64_t)src[e] * p.row_bytes + pc * 16);
+          dst[u] = out + (int64_t)e * p.row_bytes + pc * 16;
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
-      if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
+      for (int u = 0; u < kU; ++u)
+        if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
+    }
   }
 }
 

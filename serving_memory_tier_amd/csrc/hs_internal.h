@@ -120,6 +120,11 @@ struct MoveParams {
   int32_t num_reqs;
   int32_t rows_per_rl;
   uint8_t* out;                 // may be null in fused mode (copies only)
+  // layer groups sharing one top-K list and one hot-buffer state: num_layers
+  // counts groups, each of `group` consecutive layers of the `layers` pool
+  // planes; codes and row ids are per group, output rows per layer
+  int32_t group = 1;
+  int32_t layers = 0;           // 0: num_layers
 };
 
 // Entries per wave in the row mover: a wave owns whole entries, so the codes
@@ -167,6 +172,9 @@ struct FetchParams {
   const int32_t* topk;
   int32_t entries;
   uint8_t* out;
+  // layer groups (as MoveParams): num_layers counts groups of `group` layers
+  int32_t group;
+  int32_t layers;
   // set by prepare_fetch
   int32_t miss_groups, miss_splits, gather_splits;
   int32_t lds_n, miss_tab_n, gather_e, gather_tab_n;

@@ -16,7 +16,8 @@ import numpy as np
 import torch
 
 from .api import (HostPool, batch_of, hs_gather, hs_offload_prefix_pages, hs_plan_replay,
-                  hs_resolve, hs_resolve_commit, hs_resolve_decide, hs_resolve_move, layout_of)
+                  hs_resolve, hs_resolve_commit, hs_resolve_decide, hs_resolve_grouped,
+                  hs_resolve_move, layout_of)
 
 PAGE = 64
 ROW = 656
@@ -39,11 +40,15 @@ class DeviceRun:
         self.hbt = torch.from_numpy(wl.host_block_table).to(dev)
         self.ctx = torch.from_numpy(wl.ctx0.astype(np.int32)).to(dev)
         self.hot = torch.from_numpy(wl.hot_blocks).to(dev)
-        self.tok = torch.full((wl.R, wl.L, wl.C), -1, dtype=i32, device=dev)
-        self.stp = torch.zeros((wl.R, wl.L, wl.C), dtype=i32, device=dev)  # uint32 bits
+        # hot-buffer state, lists, row ids and stats per layer group (one group
+        # per layer unless the workload's layers share top-K lists); the
+        # output has every layer's rows
+        NG = wl.NG
+        self.tok = torch.full((wl.R, NG, wl.C), -1, dtype=i32, device=dev)
+        self.stp = torch.zeros((wl.R, NG, wl.C), dtype=i32, device=dev)  # uint32 bits
         N = wl.P * wl.K
-        self.rows = torch.empty((wl.R, wl.L, wl.P, wl.K), dtype=i32, device=dev)
-        self.stats = torch.empty((wl.R, wl.L, 8), dtype=i32, device=dev)
+        self.rows = torch.empty((wl.R, NG, wl.P, wl.K), dtype=i32, device=dev)
+        self.stats = torch.empty((wl.R, NG, 8), dtype=i32, device=dev)
         self.out = torch.empty((wl.R, wl.L, wl.P, wl.K, ROW), dtype=torch.uint8, device=dev)
         self.layout = layout_of(PAGE, ROW, wl.L, wl.C, wl.pool_rows, wl.host_rows)
         self.batch = batch_of(wl.R, wl.max_pages, self.pool, self.host_pool, self.bt, self.hbt,
@@ -78,7 +83,10 @@ class DeviceRun:
             topk = self.topk[i]
         stamp = s.stamp if stamp is None else stamp
         out = self.out if gather else None
-        if self.wl.P == 1:
+        if self.wl.G > 1:
+            hs_resolve_grouped(self.layout, self.batch, self.wl.G, topk, self.wl.P, self.wl.K,
+                               stamp, self.rows, out, self.stats, None, 0, stream)
+        elif self.wl.P == 1:
             hs_resolve(self.layout, self.batch, topk, self.wl.K, stamp, self.rows, out,
                        self.stats, stream)
         else:
@@ -86,6 +94,7 @@ class DeviceRun:
                            out, self.stats, None, 0, stream)
 
     def gather(self, stream=None) -> None:
+        assert self.wl.G == 1, "row ids are per layer group; gather each layer's plane"
         hs_gather(self.layout, self.pool, self.rows, self.wl.R, self.entries, self.out, stream)
 
     def post(self, i: int, stream=None) -> None:
@@ -105,6 +114,11 @@ class DeviceRun:
         n = s.offload.shape[0]
         if n and self.pairs[i] is None:
             self.pairs[i] = torch.from_numpy(np.ascontiguousarray(s.offload)).to(self.device)
+        if self.wl.G > 1:
+            hs_resolve_grouped(self.layout, self.batch, self.wl.G, self.topk[i], self.wl.P,
+                               self.wl.K, s.stamp, self.rows, self.out if gather else None,
+                               self.stats, self.pairs[i] if n else None, n, stream)
+            return
         hs_plan_replay(self.layout, self.batch, self.topk[i], self.wl.P, self.wl.K, s.stamp,
                        self.rows, self.out if gather else None, self.stats,
                        self.pairs[i] if n else None, n, stream)
@@ -147,7 +161,12 @@ class DeviceRun:
             hip.memcpy_h2d(dst, src, 4, stream)
         st = self.stats if stats is None else stats
         n_off = s.offload.shape[0]
-        if serial:
+        if wl.G > 1:
+            assert not serial, "layer groups have no serial staged form"
+            hs_resolve_grouped(self.layout, self.batches[i], wl.G, self.topk[i], wl.P, wl.K,
+                               s.stamp, self.rows, self.out, st,
+                               self.pairs[i] if n_off else None, n_off, stream)
+        elif serial:
             hs_resolve_decide(self.layout, self.batches[i], self.topk[i], wl.P, wl.K, s.stamp,
                               self.rows, None, st, stream)
             hs_resolve_move(self.layout, self.batches[i], self.topk[i], wl.P, wl.K, self.rows,
@@ -172,6 +191,15 @@ class DeviceRun:
             hip.memcpy_h2d(dst, src, 4, stream)
         st = self.stats if stats is None else stats
         L, B, T = self.layout, self.batches[i], self.topk[i]
+        if wl.G > 1:
+            # one call: its fused launch, commit and offload under one event pair
+            n_off = s.offload.shape[0] if offload else 0
+            hip.record(ev[0], stream)
+            hs_resolve_grouped(L, B, wl.G, T, wl.P, wl.K, s.stamp, self.rows, self.out, st,
+                               self.pairs[i] if n_off else None, n_off, stream)
+            for k in (1, 2, 3):
+                hip.record(ev[k], stream)
+            return
         hip.record(ev[0], stream)
         hs_resolve_decide(L, B, T, wl.P, wl.K, s.stamp, self.rows, self.out, st, stream)
         hip.record(ev[1], stream)

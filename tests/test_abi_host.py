@@ -112,6 +112,18 @@ def test_plan_rejects_bad_call(lib):
     assert f(4, 2048, None, 3) == 1      # pairs missing
 
 
+def test_grouped_rejects_bad_call(lib):
+    lay, bat = _layout(num_layers=4), _batch()
+    g = lambda G, K=2048: lib.hs_resolve_grouped(ctypes.byref(lay), ctypes.byref(bat), G, 0x1000,
+                                                 1, K, ctypes.c_uint32(1), 0x1000, None, 0x1000,
+                                                 None, 0, None)
+    assert g(3) == 1       # 3 does not divide 4 layers
+    assert g(0) == 1
+    assert g(-2) == 1
+    assert g(2, K=0) == 1
+    assert g(2, K=8193) == 2
+
+
 def test_stages_reject_bad_call(lib):
     lay, bat = _layout(), _batch()
     L, B = ctypes.byref(lay), ctypes.byref(bat)

@@ -300,3 +300,55 @@ def test_offload_entry_point():
     finally:
         hv = None
         hp.close()
+
+
+GROUPED = [
+    # name, R, L, G, P, K, C, page, rb, n_pages, hostile
+    ("g2_l4", 3, 4, 2, 1, 700, 1024, 64, 656, 120, False),
+    ("g4_l4_plan", 2, 4, 4, 2, 512, 2048, 64, 656, 150, False),
+    ("g2_hostile", 4, 4, 2, 1, 300, 512, 32, 656, 40, True),
+    ("g3_l6_rb64", 2, 6, 3, 1, 400, 512, 16, 64, 60, False),
+]
+
+
+@pytest.mark.parametrize("gather", [True, False], ids=["gather", "copies_only"])
+@pytest.mark.parametrize("name,R,L,G,P,K,C,page,rb,n_pages,hostile", GROUPED,
+                         ids=[c[0] for c in GROUPED])
+def test_random_grouped_cases(name, R, L, G, P, K, C, page, rb, n_pages, hostile, gather):
+    """hs_resolve_grouped against the oracle's grouped resolve: state and lists
+    per layer group, copies and gathered rows per layer."""
+    import serving_memory_tier_amd as hs
+    rs = np.random.default_rng(zlib.crc32(name.encode()))
+    n_blocks = R * (C // page) + n_pages * R // 2 + 8
+    a = random_arrays(rs, R, L, C, page, rb, n_pages, n_blocks, n_pages, hostile)
+    NG = L // G
+    a["tok"] = np.ascontiguousarray(a["tok"][:, :NG])
+    a["stp"] = np.ascontiguousarray(a["stp"][:, :NG])
+    case = GpuCase(page, a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"], a["hot"],
+                   a["tok"].copy(), a["stp"].copy(), C)
+    try:
+        for step in range(3):
+            _say(f"[edges] grouped {name} gather={gather} step {step}")
+            lists = random_lists(rs, R, NG, P, K, a["ctx"])
+            topk = np.ascontiguousarray(lists[:, :, 0] if P == 1 else lists)
+            stamp = 5 + 2 * step
+            t = torch.from_numpy(topk).cuda()
+            rows = torch.empty(topk.shape, dtype=torch.int32, device="cuda")
+            stats = torch.empty((R, NG, 8), dtype=torch.int32, device="cuda")
+            out = (torch.empty((R, L) + topk.shape[2:] + (rb,), dtype=torch.uint8, device="cuda")
+                   if gather else None)
+            hs.hs_resolve_grouped(case.layout, case.batch, G, t, P, K, stamp, rows, out, stats)
+            torch.cuda.synchronize()
+            o_rows, o_stats, o_out = oracle.resolve_grouped(
+                a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"], a["hot"], a["tok"], a["stp"],
+                topk, stamp, G, gather, page=page)
+            tok, stp, pool, host = case.state()
+            assert np.array_equal(rows.cpu().numpy(), o_rows)
+            assert np.array_equal(stats.cpu().numpy(), o_stats)
+            if gather:
+                assert np.array_equal(out.cpu().numpy(), o_out)
+            assert np.array_equal(tok, a["tok"])
+            assert np.array_equal(stp, a["stp"])
+            assert np.array_equal(pool, a["pool"])
+    finally:
+        case.close()

@@ -44,7 +44,7 @@ def _say(msg: str) -> None:
 
 
 def run_parity(wl, requests=None, n_steps=None, hit_replay=False, fused_plan=False,
-               check_content=True, mode="call"):
+               check_content=True, mode="call", gather=True):
     from serving_memory_tier_amd.runner import DeviceRun
 
     dev = DeviceRun(wl)
@@ -62,21 +62,22 @@ def run_parity(wl, requests=None, n_steps=None, hit_replay=False, fused_plan=Fal
             if fused_plan:
                 dev.plan_step(i)
             elif mode == "call":
-                dev.resolve(i)
+                dev.resolve(i, gather=gather)
             else:
                 stages.run(mode, dev.layout, dev.batch, dev.topk[i], wl.P, wl.K, step.stamp,
                            dev.rows, dev.out, dev.stats)
             torch.cuda.synchronize()
-            rows, stats, out = ora.resolve(step)
+            rows, stats, out = ora.resolve(step, gather=gather)
             totals += stats.sum(axis=(0, 1))
             assert np.array_equal(dev.rows[req].cpu().numpy(), rows), f"row ids, step {i}"
             assert np.array_equal(dev.stats[req].cpu().numpy(), stats), f"stats, step {i}"
             assert np.array_equal(dev.tok[req].cpu().numpy(), ora.tok), f"slot tokens, step {i}"
             assert np.array_equal(dev.stp[req].cpu().numpy().view(np.uint32), ora.stp), \
                 f"slot stamps, step {i}"
-            g_out = dev.out[req].cpu().numpy()
-            assert np.array_equal(g_out, out), f"gathered rows, step {i}"
-            if check_content:
+            if gather:
+                g_out = dev.out[req].cpu().numpy()
+                assert np.array_equal(g_out, out), f"gathered rows, step {i}"
+            if gather and check_content:
                 assert np.array_equal(g_out, expected_content(wl, step.topk[ora.req], rows,
                                                               ora.req)), f"content, step {i}"
             assert np.array_equal(dev.pool[:, hot_rows].cpu().numpy(),
@@ -155,6 +156,18 @@ def test_multi_layer_full_sampled():
 def test_mixed_state_stages_sampled(mode):
     wl = hs_gen.mixed_state(steps=4)
     run_parity(wl, requests=[0, 1, 64, 127], mode=mode)
+
+
+@pytest.mark.parametrize("gather", [True, False])
+def test_grouped_decode(gather):
+    """Layers sharing a top-K list (IndexShare): 32 requests x 4 layers in one
+    group, resolved once per group, every layer's rows moved."""
+    wl = hs_gen.grouped_decode(steps=6)
+    if gather:
+        totals = run_parity(wl)
+    else:
+        totals = run_parity(wl, gather=False)
+    assert totals[1] > 0 and totals[2] > 0
 
 
 def test_determinism_repeat():
