@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="mixed_decode",
-                    choices=["mixed_decode", "no_residency", "mixed_state", "multi_layer", "grouped_decode"])
+                    choices=["mixed_decode", "no_residency", "mixed_state", "multi_layer", "grouped_decode",
+                             "grouped_decode_per_layer"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -70,6 +71,8 @@ def build_workload(name: str, n_steps: int):
         return hs_gen.mixed_state(steps=n_steps)
     if name == "grouped_decode":
         return hs_gen.grouped_decode(steps=n_steps)
+    if name == "grouped_decode_per_layer":
+        return hs_gen.ungrouped(hs_gen.grouped_decode(steps=n_steps))
     return hs_gen.multi_layer(turns=n_steps)
 
 
@@ -242,8 +245,11 @@ def main():
                    "hbm_gbps": round(com_bytes / max(commit_us, 1e-3) / 1e3, 1)},
     }
     if wl.G > 1:
+        # one event pair spans the whole hs_resolve_grouped call
         kernels["resolve_fill"]["note"] = ("layer groups of %d: the whole hs_resolve_grouped call "
                                            "(fused launch, commit, offload)" % wl.G)
+        kernels.pop("commit")
+        kernels.pop("offload", None)
     if off:
         page_layers = [wl.steps[W + K + j].offload.shape[0] * wl.L for j, _ in off]
         off_us = 1e3 * float(np.mean([ms for _, ms in off]))

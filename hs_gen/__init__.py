@@ -6,8 +6,8 @@ this package resolves, gathers or copies KV rows.
 
 from .content import PAGE, ROW_BYTES, content_np, content_torch, fill_rows
 from .workloads import (CONFIGS, Spec, Step, Workload, build, grouped_decode, mixed_decode,
-                        mixed_state, multi_layer, no_residency, tiny)
+                        mixed_state, multi_layer, no_residency, tiny, ungrouped)
 
 __all__ = ["PAGE", "ROW_BYTES", "content_np", "content_torch", "fill_rows", "CONFIGS", "Spec",
            "Step", "Workload", "build", "tiny", "mixed_decode", "multi_layer", "no_residency",
-           "mixed_state", "grouped_decode"]
+           "mixed_state", "grouped_decode", "ungrouped"]

@@ -440,6 +440,21 @@ def grouped_decode(seed: int = 1005, steps: int = 16, R: int = 32, L: int = 4,
                       group=G))
 
 
+def ungrouped(wl: Workload) -> Workload:
+    """The same workload with one group per layer: each layer gets its group's
+    top-K list (and, when run, a hot-buffer state of its own) -- the per-layer
+    alternative a grouped resolve replaces."""
+    import copy
+    if wl.G == 1:
+        return wl
+    out = copy.copy(wl)
+    out.name = wl.name + "_per_layer"
+    out.G = 1
+    out.steps = [Step(stamp=s.stamp, ctx=s.ctx, topk=np.repeat(s.topk, wl.G, axis=1),
+                      bt_set=s.bt_set, hbt_set=s.hbt_set, offload=s.offload) for s in wl.steps]
+    return out
+
+
 CONFIGS = {
     "tiny": tiny,
     "mixed_decode": mixed_decode,
