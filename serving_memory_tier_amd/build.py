@@ -17,7 +17,24 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-function"]
 
 
+POLICY_SRC = os.path.join(HERE, "csrc", "policy.cpp")
+POLICY_LIB = os.path.join(HERE, "libhs_policy.so")
+
+
+def build_policy() -> str:
+    """The host-only residency policy library (no HIP), with g++."""
+    tmp = POLICY_LIB + ".tmp"
+    cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-I",
+           os.path.join(ROOT, "include"), "-o", tmp, POLICY_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("g++ failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, POLICY_LIB)
+    return POLICY_LIB
+
+
 def build(verbose: bool = False) -> str:
+    build_policy()
     out = os.path.join(HERE, "libhisparse.so")
     tmp = out + ".tmp"
     cmd = (["hipcc"] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp] +

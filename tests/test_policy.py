@@ -1,0 +1,196 @@
+"""The host-side residency policy (libhs_policy.so) against the rules the pages
+give it, on the CPU: GPU-first (nothing leaves the pool while it has room),
+the tail never leaves, a page becomes a null placeholder only after its host
+copy was queued in an earlier step, the coldest eligible pages go first, a
+request holds a hot lease exactly while it has a placeholder, pool blocks are
+never used twice, and the edits reproduce the policy's own tables."""
+
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import serving_memory_tier_amd as hs
+from serving_memory_tier_amd import policy as pol
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not os.path.exists(pol.LIB_PATH):
+        from serving_memory_tier_amd import build
+        build.build_policy()
+    pol.lib()
+
+
+class Mirror:
+    """The caller's view: tables and leases rebuilt from the edits alone."""
+
+    def __init__(self, R, max_pages, hb):
+        self.bt = np.full((R, max_pages), -1, np.int32)
+        self.hbt = np.full((R, max_pages), -1, np.int32)
+        self.hot = np.full((R, hb), -1, np.int32)
+        self.queued = {}    # (r, page) -> call index the host copy was queued in
+
+    def apply(self, e: pol.Edits, call: int, page_of_block):
+        for r, p, v in e.bt_set:
+            self.bt[r, p] = v
+        for r, p, v in e.hbt_set:
+            self.hbt[r, p] = v
+        for r, j, v in e.hot_set:
+            self.hot[r, j] = v
+        for db, hb in e.offload:
+            self.queued[page_of_block[int(db)]] = call
+
+
+def _pages(ctx, page):
+    return (ctx + page - 1) // page
+
+
+def _simulate(seed, R=6, page=16, n_blocks=60, hb=2, tail=2, steps=120, K=24, admit_host=True):
+    rs = np.random.default_rng(seed)
+    max_pages = 64
+    p = pol.Policy(page, n_blocks, 4096, R, max_pages, hb, tail)
+    m = Mirror(R, max_pages, hb)
+    last_use = np.zeros((R, max_pages), np.int64)
+    ctx = rs.integers(3 * page, 12 * page, size=R)
+    call = 0
+    stats = dict(evicted=0, leased=0)
+
+    def page_of_block():
+        out = {}
+        for r in range(R):
+            for pg in range(max_pages):
+                if m.bt[r, pg] >= 0:
+                    out[int(m.bt[r, pg])] = (r, pg)
+        return out
+
+    for r in range(R):
+        host = None
+        if admit_host and r % 2:
+            # a reused prefix: complete pages already on host (private host ids 3000+)
+            host = np.array([3000 + 64 * r + q for q in range(int(ctx[r]) // page)], np.int32)
+        e = p.admit(r, int(ctx[r]), host)
+        call += 1
+        m.apply(e, call, page_of_block())
+    prev = None
+    for s in range(1, steps + 1):
+        free_before = p.free_blocks()
+        new_ctx = ctx + rs.integers(0, 6, size=R)
+        topk = None
+        if prev is not None:
+            topk = prev
+            for r in range(R):
+                for t in prev[r]:
+                    if 0 <= t < ctx[r]:
+                        last_use[r, t // page] = s
+        tails_before = {r: _pages(int(new_ctx[r]), page) for r in range(R)}
+        e = p.step(s, np.arange(R), new_ctx, topk)
+        call += 1
+        bt_before = m.bt.copy()
+        m.apply(e, call, page_of_block())
+        ctx = new_ctx
+        stats["evicted"] += e.evicted
+        stats["leased"] += e.leased
+
+        # the edits reproduce the policy's own tables
+        for r in range(R):
+            bt, hbt, hot = p.tables(r)
+            assert np.array_equal(bt, m.bt[r]) and np.array_equal(hbt, m.hbt[r])
+            assert np.array_equal(hot, m.hot[r])
+        # pool blocks: resident pages and leases are disjoint and account for the pool
+        used = [int(b) for b in m.bt.ravel() if b >= 0] + [int(b) for b in m.hot.ravel() if b >= 0]
+        assert len(used) == len(set(used))
+        assert all(0 <= b < n_blocks for b in used)
+        assert len(used) + p.free_blocks() == n_blocks
+        # GPU-first: evictions only when the step's demand exceeded the free blocks
+        nulled = [(int(r), int(pg)) for r, pg, v in e.bt_set if v < 0 and bt_before[r, pg] >= 0]
+        assert len(nulled) == e.evicted
+        if nulled:
+            new_blocks = sum(1 for r, pg, v in e.bt_set if v >= 0)
+            assert free_before < new_blocks + e.leased * hb
+        for r, pg in nulled:
+            # not the tail, complete, and its host copy queued in an earlier call
+            assert pg < tails_before[r] - tail
+            assert (pg + 1) * page <= ctx[r]
+            assert m.hbt[r, pg] >= 0 or m.queued.get((r, pg), call) < call
+        # coldest first: no page left resident and eligible is colder than an evicted one
+        if nulled:
+            worst = max((last_use[r, pg], r, pg) for r, pg in nulled)
+            for r in range(R):
+                for pg in range(_pages(int(ctx[r]), page) - tail):
+                    if m.bt[r, pg] < 0 or (pg + 1) * page > ctx[r]:
+                        continue
+                    eligible = m.hbt[r, pg] >= 0 or m.queued.get((r, pg), call) < call
+                    if eligible:
+                        assert (last_use[r, pg], r, pg) > worst
+        # the tail of every request is resident
+        for r in range(R):
+            np_ = _pages(int(ctx[r]), page)
+            assert (m.bt[r, max(0, np_ - tail):np_] >= 0).all()
+        # a lease exactly while a placeholder exists; resets for new leases
+        for r in range(R):
+            has_ph = bool((m.bt[r, :_pages(int(ctx[r]), page)] < 0).any())
+            assert has_ph == bool((m.hot[r] >= 0).all())
+            assert (m.hot[r] >= 0).all() or (m.hot[r] < 0).all()
+        granted = {int(r) for r, j, v in e.hot_set if v >= 0}
+        assert granted == set(e.reset.tolist())
+        prev = [rs.integers(0, int(ctx[r]), size=K) for r in range(R)]
+    # finishing returns everything
+    for r in range(R):
+        e = p.finish(r)
+        m.apply(e, call + 1, {})
+    assert p.free_blocks() == n_blocks
+    p.close()
+    return stats
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_policy_rules_under_pressure(seed):
+    st = _simulate(seed)
+    assert st["evicted"] > 0 and st["leased"] > 0   # the pool did run short
+
+
+def test_no_pressure_no_eviction():
+    st = _simulate(11, n_blocks=4000, admit_host=False)
+    assert st["evicted"] == 0 and st["leased"] == 0
+
+
+def test_admission_of_a_host_prefix_takes_a_lease():
+    p = pol.Policy(16, 40, 100, 2, 32, 2, 2)
+    e = p.admit(0, 16 * 10 + 5, np.arange(10, dtype=np.int32))
+    bt, hbt, hot = p.tables(0)
+    # pages 0..8 host-only (page 9 is in the tail with the partial page 10)
+    assert (bt[:9] == -1).all() and (bt[9:11] >= 0).all()
+    assert (hbt[:10] == np.arange(10)).all()
+    assert (hot >= 0).all() and e.leased == 1 and e.reset.tolist() == [0]
+    assert p.free_blocks() == 40 - 2 - 2
+    p.close()
+
+
+def test_pool_exhaustion_is_an_error():
+    p = pol.Policy(16, 3, 100, 2, 32, 2, 1)
+    p.admit(0, 16, None)                     # one page
+    with pytest.raises(pol.PolicyError) as ei:
+        p.step(1, [0], [16 * 5])             # four new pages, nothing evictable
+    assert ei.value.status == pol.ERR_POOL_EXHAUSTED
+
+
+def test_rejects_bad_arguments():
+    with pytest.raises(pol.PolicyError):
+        pol.Policy(0, 10, 10, 1, 4, 1, 1)
+    p = pol.Policy(16, 10, 10, 2, 4, 1, 1)
+    with pytest.raises(pol.PolicyError):
+        p.admit(5, 16)                       # no such request slot
+    with pytest.raises(pol.PolicyError):
+        p.admit(0, 16 * 5)                   # more pages than the table has
+    p.admit(0, 16)
+    with pytest.raises(pol.PolicyError):
+        p.admit(0, 16)                       # already admitted
+    with pytest.raises(pol.PolicyError):
+        p.step(1, [0], [8])                  # context shrinks
+    with pytest.raises(pol.PolicyError):
+        p.step(1, [1], [32])                 # not admitted
+    p.close()
+    assert hs.lib  # the GPU library's binding is importable alongside
