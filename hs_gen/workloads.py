@@ -45,6 +45,12 @@ class Step:
     bt_set: np.ndarray         # int64 [n, 3] (r, page, value) applied before the step
     hbt_set: np.ndarray        # int64 [n, 3] (r, page, value) applied before the step
     offload: np.ndarray        # int32 [n, 2] (device block, host block) copied after the step
+    # residency decided step by step (build_dynamic); empty for scripted workloads
+    hot_set: np.ndarray = field(default_factory=lambda: np.zeros((0, 3), np.int64))
+    reset: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+    # pages that take a fresh pool block before the step: their rows (the
+    # tokens of the page) are written into the block, as the forward would
+    new_pages: np.ndarray = field(default_factory=lambda: np.zeros((0, 3), np.int64))
 
 
 @dataclass
@@ -70,6 +76,12 @@ class Workload:
     steps: list = field(default_factory=list)
     classes: np.ndarray | None = None   # int8 [R]: 0 full, 1 mixed, 2 none (informational)
     G: int = 1                          # layers per group sharing one top-K list (IndexShare)
+
+    @property
+    def dynamic(self) -> bool:
+        """Residency decided step by step: blocks are reused and leases move."""
+        return any(s.new_pages.shape[0] or s.hot_set.shape[0] or s.reset.shape[0]
+                   for s in self.steps)
 
     @property
     def NG(self) -> int:
@@ -108,6 +120,15 @@ class Workload:
         dp = self.dev_pages
         if requests is not None:
             dp = dp[np.isin(dp[:, 0], np.asarray(requests))]
+        self.write_pages(pool, dp, compute_device)
+
+    def write_pages(self, pool: torch.Tensor, pages: np.ndarray, compute_device=None) -> None:
+        """Write the rows of the pages (r, page, block) into their pool blocks
+        (uint8 [L, rows, 656]), every layer: the tokens of the page, valid or
+        not yet, as the forward pass would write them."""
+        dp = np.asarray(pages, dtype=np.int64).reshape(-1, 3)
+        if dp.shape[0] == 0:
+            return
         r, p, b = dp[:, 0], dp[:, 1], dp[:, 2]
         o = np.arange(PAGE, dtype=np.int64)
         rows = torch.from_numpy((b[:, None] * PAGE + o[None, :]).ravel())
@@ -438,6 +459,91 @@ def grouped_decode(seed: int = 1005, steps: int = 16, R: int = 32, L: int = 4,
     return build(Spec(name="grouped_decode", seed=seed, R=R, L=L, K=2048, C=4096, steps=steps,
                       ctx0=np.full(R, 74160), classes=np.ones(R, np.int8), tail_frac=0.25,
                       group=G))
+
+
+def build_dynamic(spec: Spec, residency, n_blocks: int, host_base: int) -> Workload:
+    """A workload whose residency is decided step by step by ``residency``
+    instead of being scripted: contexts and top-K lists are drawn as in
+    ``build`` (they do not depend on residency); ``residency`` is any object
+    with ``admit(r, ctx, host_block_of_page)`` and ``step(stamp, reqs, ctx,
+    topk)`` returning edits with ``bt_set``, ``hbt_set``, ``hot_set``,
+    ``reset`` and ``offload`` (the residency policy's, in the tests);
+    ``admit`` also takes whether the prefix starts resident (class 0).  Each
+    request starts with the host copies of its complete pages (a reused
+    prefix), in host blocks ``host_base`` and up (the decider's own host
+    blocks lie below); the decider chooses what stays resident."""
+    R, L, P, K, C = spec.R, spec.L, spec.P, spec.K, spec.C
+    if P != 1 or C % PAGE:
+        raise ValueError("one query position per step and whole-page hot buffers")
+    G = spec.group
+    NG = L // G
+    seed = spec.seed
+    ctx0 = spec.ctx0.astype(np.int64)
+    ctx_steps = [ctx0 + (s + 1) * spec.append for s in range(spec.steps)]
+    ctx_final = ctx_steps[-1] if spec.steps else ctx0
+    max_pages = int(((ctx_final + PAGE - 1) // PAGE).max())
+    src = np.arange(R, dtype=np.int64) + 1
+    # the reused prefix: host copies of the complete pages, private per request
+    done0 = ctx0 // PAGE
+    host_of_page = []
+    host_pages, host_src = [], []
+    base = host_base
+    for r in range(R):
+        ids = np.arange(base, base + int(done0[r]), dtype=np.int64)
+        base += int(done0[r])
+        host_of_page.append(ids.astype(np.int32))
+        host_pages.append(np.stack([ids, np.arange(done0[r])], 1))
+        host_src.append(np.full(done0[r], src[r]))
+    n_host_blocks = base
+    bt = np.full((R, max_pages), -1, np.int32)
+    hbt = np.full((R, max_pages), -1, np.int32)
+    hot = np.full((R, C // PAGE), -1, np.int32)
+    dev_pages = []
+    for r in range(R):
+        # class 0: the prefix stays resident (with its host copy); else host-only
+        e = residency.admit(r, int(ctx0[r]), host_of_page[r], bool(spec.classes[r] == 0))
+        for rr, p, v in e.hbt_set:
+            hbt[rr, p] = v
+        for rr, p, v in e.bt_set:
+            bt[rr, p] = v
+            if v >= 0:
+                dev_pages.append((rr, p, v))
+        for rr, j, v in e.hot_set:
+            hot[rr, j] = v
+    wl = Workload(name=spec.name, seed=seed, R=R, L=L, P=P, K=K, C=C, n_blocks=n_blocks,
+                  n_host_blocks=n_host_blocks, max_pages=max_pages, ctx0=ctx0.astype(np.int32),
+                  block_table=bt, host_block_table=hbt, hot_blocks=hot, src=src,
+                  dev_pages=np.array(dev_pages, np.int64).reshape(-1, 3),
+                  host_pages=np.concatenate(host_pages, 0).astype(np.int64),
+                  host_src=np.concatenate(host_src).astype(np.int64),
+                  classes=spec.classes.astype(np.int8), G=G)
+    ov_n, rc_n, _ = _split_counts(K, spec.mix)
+    prev = [[None] * NG for _ in range(R)]
+    last = None
+    for s in range(spec.steps):
+        ctx = ctx_steps[s]
+        e = residency.step(s + 1, np.arange(R), ctx.astype(np.int32), last)
+        topk = np.full((R, NG, P, K), -1, dtype=np.int32)
+        for r in range(R):
+            c = int(ctx[r])
+            for g in range(NG):
+                kk = rng.key(seed, 0x70C, s, r, g)
+                p0 = _mix(kk, prev[r][g], c, K, ov_n, rc_n, spec.recent_window,
+                          spec.first_recent_share)
+                prev[r][g] = p0
+                topk[r, g, 0] = p0
+        # the decider warms pages by every list of the step (all groups)
+        last = topk.reshape(R, -1)
+        new_pages = np.array([(r, p, v) for r, p, v in e.bt_set if v >= 0],
+                             np.int64).reshape(-1, 3)
+        wl.steps.append(Step(stamp=s + 1, ctx=ctx.astype(np.int32), topk=topk,
+                             bt_set=np.asarray(e.bt_set, np.int64).reshape(-1, 3),
+                             hbt_set=np.asarray(e.hbt_set, np.int64).reshape(-1, 3),
+                             offload=np.asarray(e.offload, np.int32).reshape(-1, 2),
+                             hot_set=np.asarray(e.hot_set, np.int64).reshape(-1, 3),
+                             reset=np.asarray(e.reset, np.int64).reshape(-1),
+                             new_pages=new_pages))
+    return wl
 
 
 def ungrouped(wl: Workload) -> Workload:

@@ -2,7 +2,9 @@
 pinned host pool, tables, hot-buffer state) and steps it through the hot path.
 
 Between steps it applies the scheduler's decisions the workload describes --
-nulling pages that left the resident tail, recording new host copies -- as
+nulling pages that left the resident tail, recording new host copies, and
+for workloads whose residency policy runs step by step new pool blocks with
+their rows, hot-block leases and the reset of a re-leased hot buffer -- as
 plain device-tensor writes; these are host-side residency policy, not part of
 the hot path.  Each step then calls the C ABI through the binding:
 ``hs_resolve`` (or ``hs_plan_replay`` for several query positions), whose
@@ -29,6 +31,7 @@ class DeviceRun:
         dev = torch.device(device)
         self.device = dev
         cdev = content_device or device
+        self.cdev = cdev
         self.pool = torch.zeros((wl.L, wl.pool_rows, ROW), dtype=torch.uint8, device=dev)
         wl.fill_device_pool(self.pool, compute_device=cdev)
         self.host_pool = HostPool(wl.L * wl.host_rows * ROW)
@@ -67,10 +70,18 @@ class DeviceRun:
 
     def pre(self, i: int) -> None:
         s = self.wl.steps[i]
-        for arr, t in ((s.hbt_set, self.hbt), (s.bt_set, self.bt)):
+        for arr, t in ((s.hbt_set, self.hbt), (s.bt_set, self.bt), (s.hot_set, self.hot)):
             if arr.shape[0]:
                 a = torch.from_numpy(arr).to(self.device)
                 t[a[:, 0], a[:, 1]] = a[:, 2].to(torch.int32)
+        if s.reset.shape[0]:
+            # a new or returned lease: the request's hot buffer starts empty
+            rr = torch.from_numpy(s.reset).to(self.device)
+            self.tok[rr] = -1
+            self.stp[rr] = 0
+        # pages that took a block (possibly one another page or lease held)
+        # get their rows, as the forward pass writes them
+        self.wl.write_pages(self.pool, s.new_pages, compute_device=self.cdev)
         self.ctx.copy_(torch.from_numpy(s.ctx.astype(np.int32)))
 
     # -- hot path -----------------------------------------------------------
@@ -129,6 +140,8 @@ class DeviceRun:
         pinned memory, so that a run of steps (``launch_step``) needs no host
         work between kernels and captures into a graph as it stands."""
         wl = self.wl
+        if wl.dynamic:
+            raise ValueError("steps with lease changes and page writes need pre() between them")
         n = len(wl.steps)
         self.ctx_all = torch.from_numpy(
             np.stack([s.ctx for s in wl.steps]).astype(np.int32)).to(self.device)

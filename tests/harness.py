@@ -25,6 +25,8 @@ class OracleRun:
 
     def __init__(self, wl: hs_gen.Workload, requests=None):
         self.wl = wl
+        if requests is not None and wl.dynamic:
+            raise ValueError("blocks move between requests: simulate the whole batch")
         self.req = np.arange(wl.R) if requests is None else np.asarray(requests, dtype=np.int64)
         R = self.req.size
         self.pool = np.zeros((wl.L, wl.pool_rows, ROW), dtype=np.uint8)
@@ -55,6 +57,13 @@ class OracleRun:
             self.hbt[r, p] = v
         for r, p, v in self._rows_of(step.bt_set):
             self.bt[r, p] = v
+        for r, j, v in self._rows_of(step.hot_set):
+            self.hot[r, j] = v
+        for r in step.reset:
+            if int(r) in self.pos:
+                self.tok[self.pos[int(r)]] = -1
+                self.stp[self.pos[int(r)]] = 0
+        self.wl.write_pages(torch.from_numpy(self.pool), step.new_pages)
         self.ctx = np.ascontiguousarray(step.ctx[self.req])
 
     def resolve(self, step: hs_gen.Step, gather: bool = True, topk=None, stamp=None):
@@ -68,6 +77,8 @@ class OracleRun:
                               self.tok, self.stp, np.ascontiguousarray(topk), stamp, gather)
 
     def pairs(self, step: hs_gen.Step) -> np.ndarray:
+        if self.req.size == self.wl.R:
+            return np.ascontiguousarray(step.offload).reshape(-1, 2)
         keep = [i for i, (db, _) in enumerate(step.offload) if int(db) in self.own_blocks]
         return np.ascontiguousarray(step.offload[keep]).reshape(-1, 2)
 
@@ -75,6 +86,53 @@ class OracleRun:
         pr = self.pairs(step)
         if pr.shape[0]:
             oracle.offload(self.pool, self.host, pr)
+
+
+class PolicyDecider:
+    """The residency policy (libhs_policy.so) as a workload's step-by-step
+    decider: admission and per-step edits, with the policy's host blocks
+    below the workload's reused-prefix host blocks."""
+
+    def __init__(self, R, n_blocks, n_host_blocks, max_pages, C, tail_pages):
+        from serving_memory_tier_amd import policy as pol
+        self.p = pol.Policy(PAGE, n_blocks, n_host_blocks, R, max_pages, C // PAGE, tail_pages)
+        self.evicted = 0
+        self.leased = 0
+
+    def admit(self, r, ctx, host_block_of_page, resident_prefix):
+        e = self.p.admit(r, ctx, host_block_of_page, resident_prefix)
+        self.leased += e.leased
+        return e
+
+    def step(self, stamp, reqs, ctx, topk):
+        e = self.p.step(stamp, reqs, ctx, topk)
+        self.evicted += e.evicted
+        self.leased += e.leased
+        return e
+
+
+def policy_workload(name="policy_decode", seed=1006, R=8, L=2, K=256, C=512, steps=24,
+                    ctx_lo=4096, ctx_hi=12288, append=40, slack=24, tail_pages=4, group=1,
+                    n_host_blocks=4096):
+    """A decode workload whose residency the policy decides step by step.
+    Even requests start fully resident (their prefix also on host), odd ones
+    host-only behind placeholders; the pool holds what admission needs plus
+    ``slack`` blocks, so the appended tokens soon force evictions of the
+    coldest pages and new hot leases.  Returns (workload, decider)."""
+    rs = np.random.default_rng(seed)
+    ctx0 = rs.integers(ctx_lo, ctx_hi, size=R)
+    classes = np.where(np.arange(R) % 2 == 0, 0, 2).astype(np.int8)
+    pages0 = (ctx0 + PAGE - 1) // PAGE
+    need = 0
+    for r in range(R):
+        need += int(pages0[r]) if classes[r] == 0 else tail_pages + C // PAGE
+    n_blocks = need + slack
+    max_pages = int((ctx0.max() + steps * append + PAGE - 1) // PAGE)
+    dec = PolicyDecider(R, n_blocks, n_host_blocks, max_pages, C, tail_pages)
+    spec = hs_gen.Spec(name=name, seed=seed, R=R, L=L, K=K, C=C, steps=steps, ctx0=ctx0,
+                       classes=classes, append=append, group=group)
+    wl = hs_gen.build_dynamic(spec, dec, n_blocks, n_host_blocks)
+    return wl, dec
 
 
 def expected_content(wl: hs_gen.Workload, topk: np.ndarray, rows: np.ndarray,

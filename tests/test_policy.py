@@ -194,3 +194,38 @@ def test_rejects_bad_arguments():
         p.step(1, [1], [32])                 # not admitted
     p.close()
     assert hs.lib  # the GPU library's binding is importable alongside
+
+
+@pytest.mark.parametrize("group", [1, 2])
+def test_policy_driven_oracle_run(group):
+    """The policy's edits drive the oracle step by step (blocks reused for new
+    pages and leases, leases granted mid-run with an emptied hot buffer, host
+    copies backing every nulled page): every gathered row still holds its
+    token's content, and the hot buffer never serves a stale row."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from harness import OracleRun, expected_content, policy_workload
+    wl, dec = policy_workload(group=group, L=2 * group)
+    assert dec.evicted > 0 and dec.leased > wl.R // 2   # some resident requests got leases
+    ora = OracleRun(wl)
+    totals = np.zeros(8, np.int64)
+    for i, s in enumerate(wl.steps):
+        ora.pre(s)
+        for r in s.reset:
+            assert (ora.tok[r] == -1).all()
+        rows, stats, out = ora.resolve(s)
+        totals += stats.sum(axis=(0, 1))
+        assert np.array_equal(out, expected_content(wl, s.topk, rows)), f"step {i}"
+        ora.post(s)
+    assert totals[1] > 0 and totals[2] > 0 and totals[0] > 0
+    # every host copy the tables know of (reused prefixes and the copies the
+    # policy queued) holds its page's content, every layer
+    import hs_gen
+    o = np.arange(hs_gen.PAGE)
+    for r in range(wl.R):
+        for p in np.nonzero(ora.hbt[r] >= 0)[0]:
+            rows = int(ora.hbt[r, p]) * hs_gen.PAGE + o
+            for layer in range(wl.L):
+                exp = hs_gen.content_np(np.full(o.size, layer), np.full(o.size, wl.src[r]),
+                                        p * hs_gen.PAGE + o)
+                assert np.array_equal(ora.host[layer, rows], exp), (r, p, layer)
