@@ -219,7 +219,9 @@ def main():
     # stages on the launch stream (the fused resolve-and-fill launch, the
     # commit, the offload), HIP events on that stream around every kernel
     events = [[hev.new_event() for _ in range(4)] for _ in range(KE)]
+    busy = QueueFiller()
     for j in range(KE):
+        busy.fill()
         dev.launch_step_timed(W + K + j, hev, sp0, events[j], stats=stats_all[W + K + j])
     torch.cuda.synchronize()
 
@@ -265,6 +267,7 @@ def main():
     rep = [[hev.new_event() for _ in range(4)] for _ in range(NR)]
     rep_stats = torch.zeros((wl.R, wl.NG, 8), dtype=torch.int32, device="cuda")
     for j in range(NR):
+        busy.fill()
         dev.launch_step_timed(last, hev, sp0, rep[j], stats=rep_stats, offload=False)
     torch.cuda.synchronize()
     rs = rep_stats.sum(dim=(0, 1)).cpu().numpy()
@@ -278,6 +281,13 @@ def main():
                   "hbm_gbps": round(rep_bytes / r_step / 1e3, 1),
                   "hbm_frac": round(rep_bytes / r_step / 1e3 / HBM_PEAK_GBPS, 4),
                   "resolve_fill_hbm_gbps": round(r_fused_bytes / r_fused / 1e3, 1)}
+
+    # page coldness for the residency policy: hs_page_touch over the last
+    # step's lists, HIP events around each launch
+    page_touch = touch_cost(wl, dev, hev, sp0, last, n=20, busy=busy)
+    busy.close()
+    kernels["page_touch"] = page_touch
+    policy = policy_cost(wl, dev)
 
     # the dominant kernel of a step -- the fused resolve-and-fill launch -- and
     # the resource that bounds it: the host link while it carries misses (its
@@ -316,8 +326,10 @@ def main():
                      "resident": round(st_all[0] / K, 1)},
         "kernels": kernels,
         "kernel_timing": f"HIP events on the launch stream around every kernel, over {KE} "
-                         f"steps launched as hs_plan_replay's stages after the timed ones",
+                         f"steps launched as hs_plan_replay's stages after the timed ones, each "
+                         f"queued behind a 0.3 ms device spin so no event waits on the host",
         "hit_replay": hit_replay,
+        "policy": policy,
         "roofline": roofline,
         "cpu_baseline": None,
     }
@@ -337,6 +349,113 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+class QueueFiller:
+    """A ~0.3 ms spin on the device (no memory traffic, so caches stay as the
+    previous kernels left them) enqueued ahead of a timed launch sequence:
+    the host has queued the whole sequence before the GPU reaches its first
+    event, so the events time the kernels, not the host's launch calls."""
+
+    def __init__(self, target_us: float = 300.0):
+        import torch
+        probe = 1 << 20
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(probe)          # first call loads the kernel
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(probe)
+        b.record()
+        torch.cuda.synchronize()
+        us_per_cycle = a.elapsed_time(b) * 1e3 / probe
+        self.cycles = int(max(1 << 14, min(1 << 30, target_us / max(us_per_cycle, 1e-9))))
+
+    def fill(self) -> None:
+        import torch
+        torch.cuda._sleep(self.cycles)
+
+    def close(self) -> None:
+        pass
+
+
+def touch_cost(wl, dev, hev, stream: int, i: int, n: int, busy=None):
+    """hs_page_touch on step i's lists, n launches timed with HIP events on
+    the launch stream; algorithmic bytes: every list entry read once, one
+    4-byte word written per distinct page touched."""
+    import numpy as np
+    import torch
+
+    from serving_memory_tier_amd import hs_page_touch
+    use = torch.zeros((wl.R, wl.max_pages), dtype=torch.int32, device="cuda")
+    E = wl.NG * wl.P * wl.K
+    ev = [(hev.new_event(), hev.new_event()) for _ in range(n)]
+    for j in range(n):
+        if busy is not None:
+            busy.fill()
+        hev.record(ev[j][0], stream)
+        hs_page_touch(dev.layout, dev.batches[i], dev.topk[i], E, wl.steps[i].stamp, use, stream)
+        hev.record(ev[j][1], stream)
+    torch.cuda.synchronize()
+    us = 1e3 * float(np.mean([hev.elapsed_ms(a, b) for a, b in ev]))
+    pages = int((use != 0).sum().item())
+    nbytes = wl.R * E * 4 + pages * 4
+    return {"us": round(us, 2), "hbm_bytes": nbytes, "hbm_gbps": round(nbytes / us / 1e3, 1),
+            "pages_touched": pages}
+
+
+def policy_cost(wl, dev, n: int = 20):
+    """Host cost of one residency-policy step at this batch's shape: every
+    request admitted with its complete pages on host (resident prefix for
+    every other request), then n steps of one appended token each, with
+    coldness from the GPU's per-page stamps (hs_page_touch) or from the lists
+    themselves.  Milliseconds per step, median; the policy never runs on the
+    decode path, this is what it costs between steps."""
+    import numpy as np
+    import torch
+
+    from serving_memory_tier_amd import hs_page_touch
+    from serving_memory_tier_amd import policy as pol
+    R, E = wl.R, wl.NG * wl.P * wl.K
+    ctx = wl.ctx0.astype(np.int64).copy()
+    pages0 = (ctx + PAGE - 1) // PAGE
+    max_pages = int(pages0.max()) + n + 2
+    need = int(pages0[::2].sum()) + (R - R // 2) * (4 + wl.C // PAGE)
+    host_total = int((ctx // PAGE).sum())
+    out = {}
+    for form in ("page_stamps", "lists"):
+        p = pol.Policy(PAGE, need + 8, host_total + R * (n + 2), R, max_pages, wl.C // PAGE, 4)
+        base = R * (n + 2)
+        for r in range(R):
+            hb = np.arange(base, base + int(ctx[r]) // PAGE, dtype=np.int32)
+            base += hb.size
+            p.admit(r, int(ctx[r]), hb, r % 2 == 0)
+        use = torch.zeros((R, max_pages), dtype=torch.int32, device="cuda")
+        c_dev = torch.from_numpy(ctx.astype(np.int32)).cuda()
+        from serving_memory_tier_amd._lib import HsBatch
+        batch = HsBatch(R, max_pages, None, None, None, None, c_dev.data_ptr(), None, None, None)
+        times = []
+        c = ctx.copy()
+        for s in range(n):
+            i = s % len(wl.steps)
+            topk = dev.topk[i]
+            hs_page_touch(dev.layout, batch, topk, E, s + 1, use)
+            torch.cuda.synchronize()
+            c = c + 1
+            if form == "page_stamps":
+                u = use.cpu().numpy().view(np.uint32)
+                t0 = time.perf_counter()
+                p.step_pages(np.arange(R), c, u)
+            else:
+                lists = topk.cpu().numpy().reshape(R, -1)
+                t0 = time.perf_counter()
+                p.step(s + 2, np.arange(R), c, lists)
+            times.append(time.perf_counter() - t0)
+            c_dev.copy_(torch.from_numpy(c.astype(np.int32)))
+        out[form + "_ms"] = round(1e3 * float(np.median(times)), 3)
+        p.close()
+    out["note"] = ("host ms per policy step (median of %d) at this batch's shape; the GPU's "
+                   "per-page stamps (hs_page_touch) replace a scan of every list entry" % n)
+    return out
 
 
 def cpu_baseline(wl, budget_s: float):

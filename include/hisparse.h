@@ -253,6 +253,29 @@ hs_status hs_resolve_commit(const hs_layout* layout, const hs_batch* batch, cons
                             int32_t num_pos, int32_t top_k, int32_t* row_ids,
                             uint8_t* gather_out, hipStream_t stream);
 
+/*
+ * hs_page_touch -- page coldness for the host-side residency policy ("Use
+ * sparsity when needed": under pressure a request gives up its coldest
+ * pages first).  For every request r < batch->num_reqs and every entry
+ * t = topk[r * entries_per_req + e], e < entries_per_req, with
+ * 0 <= t < ctx_len[r] and t / page_size < max_pages:
+ *   page_use[r * max_pages + t / page_size] = stamp.
+ * Every other word of page_use (device [R][max_pages], caller-owned) keeps
+ * its value.  topk is device memory, any [R][...] list layout flattened per
+ * request (e.g. [R][L][P][K] with entries_per_req = L * P * K, or one group
+ * list per layer group); padding (-1) and out-of-range entries stamp
+ * nothing.  Uses batch->num_reqs, max_pages and ctx_len only.  Enqueue it
+ * after a step's resolve on the same stream and copy page_use to host when
+ * the policy runs (hs_policy_step_pages reads it), so the policy never reads
+ * the lists themselves.  Any stamp value is stored as given.
+ * Errors: HS_ERR_INVALID_ARGUMENT (null pointer with work to do, negative
+ * sizes, bad layout), HS_ERR_UNSUPPORTED (entries_per_req over 67,107,840),
+ * HS_ERR_LAUNCH.
+ */
+hs_status hs_page_touch(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                        int32_t entries_per_req, uint32_t stamp, uint32_t* page_use,
+                        hipStream_t stream);
+
 /* A static English description of a status code. */
 const char* hs_status_string(hs_status status);
 

@@ -51,7 +51,7 @@ typedef int32_t hs_policy_status;
 #define HS_POLICY_ERR_HOST_EXHAUSTED 3   /* completed pages need more host blocks than exist */
 
 typedef struct {
-  int32_t page_size;               /* tokens per page */
+  int32_t page_size;               /* tokens per page, a power of two */
   int32_t num_blocks;              /* device blocks in the pool */
   int32_t num_host_blocks;         /* blocks in the pinned host pool */
   int32_t max_requests;            /* request slots 0..max_requests-1 */
@@ -108,6 +108,17 @@ hs_policy_status hs_policy_finish(hs_policy* p, int32_t req, hs_policy_edits* ed
 hs_policy_status hs_policy_step(hs_policy* p, int32_t stamp, const int32_t* req,
                                 const int32_t* ctx_len, int32_t n, const int32_t* topk,
                                 int32_t k, hs_policy_edits* edits);
+
+/* hs_policy_step with page coldness given per page instead of as lists:
+ * page_use[i * page_stride + page] is the last stamp at which a top-K list of
+ * req[i] selected a token of that page (0 = never), as hs_page_touch writes
+ * it on the GPU; a page's coldness becomes the later of its own and this
+ * one.  Pages at or beyond page_stride keep their coldness.  Stamps here
+ * and in hs_policy_step share one scale: use one form throughout.
+ * page_use may be NULL when page_stride is 0. */
+hs_policy_status hs_policy_step_pages(hs_policy* p, const int32_t* req, const int32_t* ctx_len,
+                                      int32_t n, const uint32_t* page_use, int32_t page_stride,
+                                      hs_policy_edits* edits);
 
 /* Read-only views for tests: the policy's block table row, host table row
  * and lease of `req` (arrays of max_pages, max_pages, hot_blocks_per_request

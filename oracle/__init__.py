@@ -1,4 +1,5 @@
-"""CPU oracle for the top-K resolver, row gather and prefix-page offload.
+"""CPU oracle for the top-K resolver, row gather, prefix-page offload and page
+coldness stamps.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  It wraps the plain
@@ -52,8 +53,9 @@ def _load():
         lib.oracle_resolve_grouped.argtypes = [i32, i32, i32, i32, i32, i64, i64, i64, i64, i32,
                                                i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, u32,
                                                vp, vp, vp]
+        lib.oracle_page_touch.argtypes = [i32, i32, i32, i32, vp, vp, u32, vp]
         for f in (lib.oracle_gather, lib.oracle_offload, lib.oracle_resolve,
-                  lib.oracle_resolve_grouped):
+                  lib.oracle_resolve_grouped, lib.oracle_page_touch):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -98,6 +100,20 @@ def offload(pool: np.ndarray, host: np.ndarray, pairs: np.ndarray, page: int = P
     assert L2 == L and rb == rb2 and rb % 16 == 0
     _load().oracle_offload(page, rb, L, pool_rows, pool_rows * rb, host_rows, host_rows * rb,
                            _ptr(pool), _ptr(host), _ptr(pairs), pairs.shape[0])
+
+
+def page_touch(ctx_len: np.ndarray, topk: np.ndarray, stamp: int, page_use: np.ndarray,
+               page: int = PAGE) -> None:
+    """Page coldness in place: page_use[r, t // page] = stamp for every entry t
+    of topk[r] (any shape [R, ...], flattened per request) with 0 <= t < ctx_len[r]
+    and t // page < max_pages.  page_use: uint32 [R, max_pages]."""
+    _check(page_use, np.uint32, "page_use")
+    ctx = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    R, max_pages = page_use.shape
+    t = np.ascontiguousarray(topk, dtype=np.int32).reshape(R, -1)
+    assert ctx.shape == (R,)
+    _load().oracle_page_touch(page, R, max_pages, t.shape[1], _ptr(ctx), _ptr(t), stamp,
+                              _ptr(page_use))
 
 
 def resolve(pool: np.ndarray, host: np.ndarray, block_table: np.ndarray,

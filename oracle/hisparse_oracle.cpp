@@ -26,6 +26,9 @@
 //   [SHARE] "Use sparsity when needed": GLM 5.3's IndexShare places one
 //           indexer layer per 4 sparse-MLA layers, so a group of layers
 //           attends to one top-K list.
+//   [COLD]  "Use sparsity when needed": under pressure a request frees its
+//           coldest pages in place; a page's coldness here is the last stamp
+//           at which a top-K list selected one of its tokens.
 //
 // Where the pages leave a choice open the plainest reading is taken:
 //   * null placeholder / no host copy / empty slot = a negative entry;
@@ -260,6 +263,25 @@ int oracle_offload(int32_t page, int32_t row_bytes, int32_t L, int64_t pool_rows
     for (int32_t l = 0; l < L; ++l)
       std::memcpy(host + l * host_layer_stride + hb * page_bytes,
                   pool + l * pool_layer_stride + db * page_bytes, (size_t)page_bytes);
+  }
+  return 0;
+}
+
+// Page coldness ([COLD]): for every request r and every list entry t of
+// topk[r][0..E) that is a token of the context (0 <= t < ctx_len[r]) on a
+// page the table has (t / page < max_pages), the page's word in
+// page_use[r][max_pages] becomes `stamp`; every other word keeps its value.
+int oracle_page_touch(int32_t page, int32_t R, int32_t max_pages, int32_t E,
+                      const int32_t* ctx_len, const int32_t* topk, uint32_t stamp,
+                      uint32_t* page_use) {
+  for (int32_t r = 0; r < R; ++r) {
+    for (int32_t e = 0; e < E; ++e) {
+      const int64_t t = topk[(int64_t)r * E + e];
+      if (t < 0 || t >= ctx_len[r]) continue;
+      const int64_t pg = t / page;
+      if (pg >= max_pages) continue;
+      page_use[(int64_t)r * max_pages + pg] = stamp;
+    }
   }
   return 0;
 }

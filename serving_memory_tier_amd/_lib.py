@@ -19,7 +19,7 @@ HS_MAX_HOT_CAPACITY = 8192
 EXPORTS = ("hs_resolve", "hs_gather", "hs_offload_prefix_pages", "hs_plan_replay",
            "hs_resolve_grouped",
            "hs_resolve_decide", "hs_resolve_fetch", "hs_resolve_move", "hs_resolve_commit",
-           "hs_status_string", "hs_last_error", "hs_host_alloc", "hs_host_free",
+           "hs_page_touch", "hs_status_string", "hs_last_error", "hs_host_alloc", "hs_host_free",
            "hs_host_device_pointer")
 
 
@@ -66,6 +66,7 @@ def lib():
         L.hs_resolve_fetch.argtypes = [lay, bat, vp, i32, i32, vp, vp]
         L.hs_resolve_move.argtypes = [lay, bat, vp, i32, i32, vp, vp, vp]
         L.hs_resolve_commit.argtypes = [lay, bat, vp, i32, i32, vp, vp, vp]
+        L.hs_page_touch.argtypes = [lay, bat, vp, i32, u32, vp, vp]
         L.hs_status_string.argtypes = [i32]
         L.hs_status_string.restype = ctypes.c_char_p
         L.hs_last_error.argtypes = []

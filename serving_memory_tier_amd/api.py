@@ -130,6 +130,13 @@ def hs_offload_prefix_pages(layout: HsLayout, kv_pool, host_pool, pairs, n: int,
                                          _stream(stream)), "hs_offload_prefix_pages")
 
 
+def hs_page_touch(layout: HsLayout, batch: HsBatch, topk, entries_per_req: int, stamp: int,
+                  page_use, stream=None) -> None:
+    _check(lib().hs_page_touch(ctypes.byref(layout), ctypes.byref(batch), _ptr(topk),
+                               entries_per_req, stamp, _ptr(page_use), _stream(stream)),
+           "hs_page_touch")
+
+
 def hs_host_alloc(nbytes: int) -> int:
     p = ctypes.c_void_p()
     _check(lib().hs_host_alloc(nbytes, ctypes.byref(p)), "hs_host_alloc")

@@ -374,6 +374,28 @@ hs_status hs_offload_prefix_pages(const hs_layout* layout, const uint8_t* kv_poo
                   "offload launch");
 }
 
+hs_status hs_page_touch(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                        int32_t entries_per_req, uint32_t stamp, uint32_t* page_use,
+                        hipStream_t stream) {
+  hs_status s = check_layout(layout);
+  if (s != HS_OK) return s;
+  if (!batch || batch->num_reqs < 0 || batch->max_pages < 1 || entries_per_req < 0)
+    return HS_ERR_INVALID_ARGUMENT;
+  if (entries_per_req > hs::kTouchMaxEntries) return HS_ERR_UNSUPPORTED;
+  if (batch->num_reqs == 0 || entries_per_req == 0) return HS_OK;
+  if (!topk || !page_use || !batch->ctx_len) return HS_ERR_INVALID_ARGUMENT;
+  hs::TouchParams p;
+  p.topk = topk;
+  p.ctx_len = batch->ctx_len;
+  p.page_use = page_use;
+  p.entries = entries_per_req;
+  p.num_reqs = batch->num_reqs;
+  p.max_pages = batch->max_pages;
+  p.page_shift = log2i(layout->page_size);
+  p.stamp = stamp;
+  return from_hip(hs::launch_page_touch(p, stream), "page touch launch");
+}
+
 const char* hs_last_error(void) { return g_last_error; }
 
 const char* hs_status_string(hs_status status) {

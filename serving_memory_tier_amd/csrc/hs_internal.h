@@ -204,4 +204,23 @@ struct OffloadParams {
 
 hipError_t launch_offload(const OffloadParams& p, hipStream_t stream);
 
+// Page coldness stamps from the top-K lists: for every request r and entry
+// t = topk[r * entries + e] with 0 <= t < min(ctx_len[r], max_pages <<
+// page_shift), page_use[r * max_pages + (t >> page_shift)] = stamp.
+struct TouchParams {
+  const int32_t* topk;
+  const int32_t* ctx_len;
+  uint32_t* page_use;
+  int64_t entries;      // entries per request
+  int32_t num_reqs;
+  int32_t max_pages;
+  int32_t page_shift;
+  uint32_t stamp;
+};
+
+constexpr int64_t kTouchPerBlock = 1024;
+constexpr int64_t kTouchMaxEntries = kTouchPerBlock * 65535;
+
+hipError_t launch_page_touch(const TouchParams& p, hipStream_t stream);
+
 }  // namespace hs

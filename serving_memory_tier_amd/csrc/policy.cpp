@@ -28,6 +28,7 @@ struct Req {
   std::vector<char> own_host;      // the host block is the policy's (freed at finish)
   std::vector<uint32_t> last_use;  // coldness: last stamp a top-K list touched the page
   std::vector<int32_t> hot;        // leased blocks, empty = no lease
+  int32_t copied_upto = 0;         // pages below have a host copy, valid or queued
 };
 
 struct Out {
@@ -77,6 +78,7 @@ void clear_counts(hs_policy_edits* e) {
 
 struct hs_policy {
   hs_policy_config cfg;
+  int32_t page_shift = 0;            // log2(page_size)
   std::vector<int32_t> free_blocks;  // popped from the back: lowest block first
   std::vector<int32_t> free_host;
   std::vector<Req> reqs;
@@ -120,14 +122,21 @@ struct hs_policy {
         if (copied) cands.push_back({q.last_use[p], r, p});
       }
     }
-    std::sort(cands.begin(), cands.end(), [](const Cand& a, const Cand& b) {
+    const auto colder = [](const Cand& a, const Cand& b) {
       if (a.use != b.use) return a.use < b.use;
       if (a.r != b.r) return a.r < b.r;
       return a.p < b.p;
-    });
-    size_t i = 0;
+    };
+    // only the coldest few are needed: order them a batch at a time
+    size_t i = 0, ordered = 0;
     while ((int32_t)free_blocks.size() < need) {
       if (i == cands.size()) return HS_POLICY_ERR_POOL_EXHAUSTED;
+      if (i == ordered) {
+        const size_t want = std::max<size_t>(64, 2 * (size_t)(need - (int32_t)free_blocks.size()));
+        const size_t upto = std::min(cands.size(), ordered + want);
+        std::partial_sort(cands.begin() + ordered, cands.begin() + upto, cands.end(), colder);
+        ordered = upto;
+      }
       const Cand c = cands[i++];
       Req& q = reqs[c.r];
       free_block(q.bt[c.p]);
@@ -162,7 +171,7 @@ struct hs_policy {
   hs_policy_status queue_copies(int32_t r, Out& out) {
     Req& q = reqs[r];
     const int32_t complete = q.ctx / cfg.page_size;
-    for (int32_t p = 0; p < complete; ++p) {
+    for (int32_t p = q.copied_upto; p < complete; q.copied_upto = ++p) {
       if (q.host_of[p] >= 0 || q.bt[p] < 0) continue;
       if (free_host.empty()) return HS_POLICY_ERR_HOST_EXHAUSTED;
       const int32_t hb = free_host.back();
@@ -177,17 +186,74 @@ struct hs_policy {
   }
 };
 
+namespace {
+
+hs_policy_status check_step(const hs_policy* p, const int32_t* req, const int32_t* ctx_len,
+                            int32_t n) {
+  if (!p || n < 0 || (n > 0 && (!req || !ctx_len))) return HS_POLICY_ERR_INVALID_ARGUMENT;
+  for (int32_t i = 0; i < n; ++i) {
+    if (req[i] < 0 || req[i] >= p->cfg.max_requests || !p->reqs[req[i]].active)
+      return HS_POLICY_ERR_INVALID_ARGUMENT;
+    const Req& q = p->reqs[req[i]];
+    if (ctx_len[i] < q.ctx || p->pages_of(ctx_len[i]) > p->cfg.max_pages)
+      return HS_POLICY_ERR_INVALID_ARGUMENT;
+  }
+  return HS_POLICY_OK;
+}
+
+// Host copies queued after the previous step are now valid.
+void publish_copies(hs_policy* p, Out& out) {
+  ++p->step;
+  for (const auto& t : p->pending) {
+    Req& q = p->reqs[std::get<0>(t)];
+    q.hbt[std::get<1>(t)] = std::get<2>(t);
+    out.hbt(std::get<0>(t), std::get<1>(t), std::get<2>(t));
+  }
+  p->pending.clear();
+}
+
+// The rest of a step, once coldness is up to date: appended tokens take
+// blocks, pressure evicts, leases are granted, completed pages are queued.
+hs_policy_status finish_step(hs_policy* p, const int32_t* req, const int32_t* ctx_len,
+                             int32_t n, Out& out) {
+  hs_policy_status s;
+  // appended tokens: new pages take blocks
+  std::vector<std::pair<int32_t, int32_t>> new_pages;
+  for (int32_t i = 0; i < n; ++i) {
+    Req& q = p->reqs[req[i]];
+    const int32_t old_np = p->pages_of(q.ctx), new_np = p->pages_of(ctx_len[i]);
+    for (int32_t pg = old_np; pg < new_np; ++pg) new_pages.emplace_back(req[i], pg);
+    q.ctx = ctx_len[i];
+  }
+  std::vector<char> lease_want(p->cfg.max_requests, 0);
+  s = p->make_room((int32_t)new_pages.size(), lease_want, out);
+  if (s != HS_POLICY_OK) return s;
+  for (const auto& np : new_pages) {
+    Req& q = p->reqs[np.first];
+    q.bt[np.second] = p->take_block();
+    out.bt(np.first, np.second, q.bt[np.second]);
+  }
+  p->grant(lease_want, out);
+  // completed pages: proactive host copies, queued after the step
+  for (int32_t i = 0; i < n; ++i)
+    if ((s = p->queue_copies(req[i], out)) != HS_POLICY_OK) return s;
+  return out.ok ? HS_POLICY_OK : HS_POLICY_ERR_INVALID_ARGUMENT;
+}
+
+}  // namespace
+
 extern "C" {
 
 hs_policy_status hs_policy_create(const hs_policy_config* cfg, hs_policy** out) {
   if (!cfg || !out) return HS_POLICY_ERR_INVALID_ARGUMENT;
   *out = nullptr;
-  if (cfg->page_size < 1 || cfg->num_blocks < 0 || cfg->num_host_blocks < 0 ||
-      cfg->max_requests < 1 || cfg->max_pages < 1 || cfg->hot_blocks_per_request < 1 ||
+  if (cfg->page_size < 1 || (cfg->page_size & (cfg->page_size - 1)) != 0 ||
+      cfg->num_blocks < 0 || cfg->num_host_blocks < 0 || cfg->max_requests < 1 || cfg->max_pages < 1 || cfg->hot_blocks_per_request < 1 ||
       cfg->tail_pages < 1)
     return HS_POLICY_ERR_INVALID_ARGUMENT;
   hs_policy* p = new hs_policy();
   p->cfg = *cfg;
+  while ((1 << p->page_shift) < cfg->page_size) ++p->page_shift;
   for (int32_t b = cfg->num_blocks - 1; b >= 0; --b) p->free_blocks.push_back(b);
   for (int32_t b = cfg->num_host_blocks - 1; b >= 0; --b) p->free_host.push_back(b);
   p->reqs.resize(cfg->max_requests);
@@ -290,53 +356,42 @@ hs_policy_status hs_policy_step(hs_policy* p, int32_t stamp, const int32_t* req,
                                 const int32_t* ctx_len, int32_t n, const int32_t* topk,
                                 int32_t k, hs_policy_edits* edits) {
   clear_counts(edits);
-  if (!p || n < 0 || (n > 0 && (!req || !ctx_len)) || k < 0 || (k > 0 && !topk))
-    return HS_POLICY_ERR_INVALID_ARGUMENT;
-  for (int32_t i = 0; i < n; ++i) {
-    if (req[i] < 0 || req[i] >= p->cfg.max_requests || !p->reqs[req[i]].active)
-      return HS_POLICY_ERR_INVALID_ARGUMENT;
-    const Req& q = p->reqs[req[i]];
-    if (ctx_len[i] < q.ctx || p->pages_of(ctx_len[i]) > p->cfg.max_pages)
-      return HS_POLICY_ERR_INVALID_ARGUMENT;
-  }
+  hs_policy_status s = check_step(p, req, ctx_len, n);
+  if (s != HS_POLICY_OK) return s;
+  if (k < 0 || (k > 0 && !topk)) return HS_POLICY_ERR_INVALID_ARGUMENT;
   Out out{edits};
-  ++p->step;
-  // host copies queued after the previous step are now valid
-  for (const auto& t : p->pending) {
-    Req& q = p->reqs[std::get<0>(t)];
-    q.hbt[std::get<1>(t)] = std::get<2>(t);
-    out.hbt(std::get<0>(t), std::get<1>(t), std::get<2>(t));
-  }
-  p->pending.clear();
+  publish_copies(p, out);
   // coldness from the last step's lists
+  const int32_t shift = p->page_shift;
   for (int32_t i = 0; i < n && k > 0; ++i) {
     Req& q = p->reqs[req[i]];
-    for (int32_t j = 0; j < k; ++j) {
-      const int32_t t = topk[(int64_t)i * k + j];
-      if (t >= 0 && t < q.ctx) q.last_use[t / p->cfg.page_size] = (uint32_t)stamp;
-    }
+    const int32_t* t = topk + (int64_t)i * k;
+    uint32_t* use = q.last_use.data();
+    for (int32_t j = 0; j < k; ++j)
+      if (t[j] >= 0 && t[j] < q.ctx) use[t[j] >> shift] = (uint32_t)stamp;
   }
-  // appended tokens: new pages take blocks
-  std::vector<std::pair<int32_t, int32_t>> new_pages;
-  for (int32_t i = 0; i < n; ++i) {
-    Req& q = p->reqs[req[i]];
-    const int32_t old_np = p->pages_of(q.ctx), new_np = p->pages_of(ctx_len[i]);
-    for (int32_t pg = old_np; pg < new_np; ++pg) new_pages.emplace_back(req[i], pg);
-    q.ctx = ctx_len[i];
-  }
-  std::vector<char> lease_want(p->cfg.max_requests, 0);
-  hs_policy_status s = p->make_room((int32_t)new_pages.size(), lease_want, out);
+  return finish_step(p, req, ctx_len, n, out);
+}
+
+hs_policy_status hs_policy_step_pages(hs_policy* p, const int32_t* req, const int32_t* ctx_len,
+                                      int32_t n, const uint32_t* page_use, int32_t page_stride,
+                                      hs_policy_edits* edits) {
+  clear_counts(edits);
+  hs_policy_status s = check_step(p, req, ctx_len, n);
   if (s != HS_POLICY_OK) return s;
-  for (const auto& np : new_pages) {
-    Req& q = p->reqs[np.first];
-    q.bt[np.second] = p->take_block();
-    out.bt(np.first, np.second, q.bt[np.second]);
+  if (page_stride < 0 || (n > 0 && page_stride > 0 && !page_use))
+    return HS_POLICY_ERR_INVALID_ARGUMENT;
+  Out out{edits};
+  publish_copies(p, out);
+  // coldness from the stamps the GPU wrote per page: a page keeps the later
+  // of its own stamp and the table's
+  for (int32_t i = 0; i < n && page_stride > 0; ++i) {
+    Req& q = p->reqs[req[i]];
+    const uint32_t* u = page_use + (int64_t)i * page_stride;
+    const int32_t np = std::min(p->pages_of(q.ctx), page_stride);
+    for (int32_t pg = 0; pg < np; ++pg) q.last_use[pg] = std::max(q.last_use[pg], u[pg]);
   }
-  p->grant(lease_want, out);
-  // completed pages: proactive host copies, queued after the step
-  for (int32_t i = 0; i < n; ++i)
-    if ((s = p->queue_copies(req[i], out)) != HS_POLICY_OK) return s;
-  return out.ok ? HS_POLICY_OK : HS_POLICY_ERR_INVALID_ARGUMENT;
+  return finish_step(p, req, ctx_len, n, out);
 }
 
 hs_policy_status hs_policy_tables(const hs_policy* p, int32_t req, int32_t* bt, int32_t* hbt,

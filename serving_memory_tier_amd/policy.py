@@ -67,10 +67,11 @@ def lib():
         L.hs_policy_admit.argtypes = [vp, i32, i32, vp, i32, ctypes.POINTER(_Edits)]
         L.hs_policy_finish.argtypes = [vp, i32, ctypes.POINTER(_Edits)]
         L.hs_policy_step.argtypes = [vp, i32, vp, vp, i32, vp, i32, ctypes.POINTER(_Edits)]
+        L.hs_policy_step_pages.argtypes = [vp, vp, vp, i32, vp, i32, ctypes.POINTER(_Edits)]
         L.hs_policy_tables.argtypes = [vp, i32, vp, vp, vp]
         L.hs_policy_free_blocks.argtypes = [vp]
         for f in (L.hs_policy_create, L.hs_policy_admit, L.hs_policy_finish, L.hs_policy_step,
-                  L.hs_policy_tables, L.hs_policy_free_blocks):
+                  L.hs_policy_step_pages, L.hs_policy_tables, L.hs_policy_free_blocks):
             f.restype = i32
         _lib = L
     return _lib
@@ -146,6 +147,21 @@ class Policy:
         self._check(lib().hs_policy_step(self.h, stamp, r.ctypes.data, c.ctypes.data, r.size,
                                          None if t is None else t.ctypes.data, k,
                                          ctypes.byref(e)), "step")
+        return self._out(e)
+
+    def step_pages(self, reqs, ctx_lens, page_use=None) -> Edits:
+        """A step with coldness given per page: page_use uint32 [n, stride]
+        (row i for reqs[i]), e.g. hs_page_touch's table copied to host."""
+        r = np.ascontiguousarray(reqs, np.int32)
+        c = np.ascontiguousarray(ctx_lens, np.int32)
+        u = None if page_use is None else np.ascontiguousarray(page_use, np.uint32)
+        if u is not None and u.shape[0] != r.size:
+            raise ValueError("page_use needs one row per request")
+        stride = 0 if u is None else u.shape[1]
+        e = self._edits()
+        self._check(lib().hs_policy_step_pages(self.h, r.ctypes.data, c.ctypes.data, r.size,
+                                               None if u is None else u.ctypes.data, stride,
+                                               ctypes.byref(e)), "step_pages")
         return self._out(e)
 
     def tables(self, req: int):

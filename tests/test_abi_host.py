@@ -171,3 +171,24 @@ def test_host_alloc_rejects(lib):
     assert lib.hs_host_alloc(64, None) == 1
     assert lib.hs_host_free(None) == 0
     assert lib.hs_host_device_pointer(None, ctypes.byref(p)) == 1
+
+
+def test_page_touch_rejects(lib):
+    lay = _layout()
+    b = HsBatch(4, 16, None, None, None, None, 0x1000, None, None, None)
+    t = lambda lay_, bat, topk, E, use: lib.hs_page_touch(
+        ctypes.byref(lay_) if lay_ is not None else None,
+        ctypes.byref(bat) if bat is not None else None, topk, E, 5, use, None)
+    assert t(None, b, 0x1000, 8, 0x1000) == 1
+    assert t(lay, None, 0x1000, 8, 0x1000) == 1
+    assert t(lay, b, None, 8, 0x1000) == 1
+    assert t(lay, b, 0x1000, 8, None) == 1
+    assert t(lay, b, 0x1000, -1, 0x1000) == 1
+    assert t(lay, b, 0x1000, 1024 * 65535 + 1, 0x1000) == 2
+    nb = HsBatch(4, 16, None, None, None, None, None, None, None, None)
+    assert t(lay, nb, 0x1000, 8, 0x1000) == 1                # no context lengths
+    bad = HsBatch(4, 0, None, None, None, None, 0x1000, None, None, None)
+    assert t(lay, bad, 0x1000, 8, 0x1000) == 1               # no table columns
+    assert t(lay, b, None, 0, None) == 0                     # nothing to do
+    empty = HsBatch(0, 16, None, None, None, None, None, None, None, None)
+    assert t(lay, empty, None, 8, None) == 0

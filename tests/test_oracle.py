@@ -463,3 +463,40 @@ def test_grouped_with_one_layer_per_group_is_resolve():
         for x, y in zip(ra, rb):
             assert np.array_equal(x, y)
         assert np.array_equal(a.pool, b.pool) and np.array_equal(a.tok, b.tok)
+
+
+def test_page_touch_worked_example():
+    """Page coldness by hand (page 4): request 0 (context 12) selects tokens
+    3 (page 0), 6 (page 1) and 9 (page 2); 12 lies past the context and -1
+    is padding, so page 3 keeps its old stamp.  Request 1 (context 16)
+    selects 12 and 15 (page 3); 16 is past the context, -5 invalid."""
+    use = np.array([[7, 7, 7, 7], [1, 2, 3, 4]], np.uint32)
+    topk = np.array([[3, 9, 12, -1, 6, -1], [15, 16, -5, 12, -1, -1]], np.int32)
+    oracle.page_touch(np.array([12, 16], np.int32), topk, 9, use, page=4)
+    assert use.tolist() == [[9, 9, 9, 7], [1, 2, 3, 9]]
+
+
+def test_page_touch_is_the_set_of_selected_pages():
+    """On random lists (padding, out-of-range and past-the-table tokens
+    included), exactly the pages holding a selected context token carry the
+    new stamp, and every other word is unchanged."""
+    rs = np.random.default_rng(5)
+    R, max_pages, E = 12, 40, 24
+    PAGE = hs_gen.PAGE
+    ctx = rs.integers(1, 45 * PAGE, size=R).astype(np.int32)   # some contexts exceed the table
+    topk = rs.integers(-3, 46 * PAGE, size=(R, 2, E // 2)).astype(np.int32)
+    # the context's last token and the first one past it, on every request
+    topk[:, 0, 0] = ctx - 1
+    topk[:, 1, 0] = ctx
+    old = rs.integers(1, 1000, size=(R, max_pages)).astype(np.uint32)
+    use = old.copy()
+    oracle.page_touch(ctx, topk, 4242, use)
+    for r in range(R):
+        t = topk[r].ravel()
+        t = t[(t >= 0) & (t < ctx[r])]
+        pages = set((t // PAGE).tolist()) & set(range(max_pages))
+        touched = set(np.nonzero(use[r] == 4242)[0].tolist())
+        assert touched == pages
+        keep = np.ones(max_pages, bool)
+        keep[list(pages)] = False
+        assert np.array_equal(use[r][keep], old[r][keep])

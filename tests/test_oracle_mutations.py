@@ -42,6 +42,9 @@ MUTANTS = {
     "dup_count_wrong": ("stats[6] = n_nonpad - (int32_t)nonpad.size();", "stats[6] = 0;"),
     "grouped_copies_skip_last_layer": ("for (int32_t l = l0 + 1; l < l0 + G; ++l)",
                                        "for (int32_t l = l0 + 1; l < l0 + G - 1; ++l)"),
+    "page_touch_ctx_off_by_one": ("if (t < 0 || t >= ctx_len[r]) continue;",
+                                  "if (t < 0 || t > ctx_len[r]) continue;"),
+    "page_touch_wrong_page": ("const int64_t pg = t / page;", "const int64_t pg = (t + 1) / page;"),
     "grouped_gather_wrong_group": ("const int64_t row = rows[((int64_t)r * NG + l / G) * N + i];",
                                    "const int64_t row = rows[((int64_t)r * NG + l % NG) * N + i];"),
 }
@@ -55,7 +58,9 @@ FAST_PINS = ["tests/test_oracle.py::test_worked_example_steps",
              "tests/test_oracle.py::test_offload_copies_every_layer_and_leaves_pool",
              "tests/test_oracle.py::test_tiny_workload_invariants",
              "tests/test_oracle.py::test_grouped_equals_per_layer_resolve",
-             "tests/test_oracle.py::test_grouped_rows_hold_each_layers_content"]
+             "tests/test_oracle.py::test_grouped_rows_hold_each_layers_content",
+             "tests/test_oracle.py::test_page_touch_worked_example",
+             "tests/test_oracle.py::test_page_touch_is_the_set_of_selected_pages"]
 
 
 def test_unmutated_source_passes_the_pins():

@@ -7,6 +7,7 @@ never used twice, and the edits reproduce the policy's own tables."""
 
 from __future__ import annotations
 
+import ctypes
 import os
 
 import numpy as np
@@ -192,6 +193,16 @@ def test_rejects_bad_arguments():
         p.step(1, [0], [8])                  # context shrinks
     with pytest.raises(pol.PolicyError):
         p.step(1, [1], [32])                 # not admitted
+    e = pol._Edits()
+    r, c = np.zeros(1, np.int32), np.full(1, 16, np.int32)
+    assert pol.lib().hs_policy_step_pages(p.h, r.ctypes.data, c.ctypes.data, 1, None, 4,
+                                          ctypes.byref(e)) == pol.ERR_INVALID_ARGUMENT
+    assert pol.lib().hs_policy_step_pages(p.h, r.ctypes.data, c.ctypes.data, 1, None, -1,
+                                          ctypes.byref(e)) == pol.ERR_INVALID_ARGUMENT
+    with pytest.raises(ValueError):
+        p.step_pages([0], [16], np.zeros((2, 4), np.uint32))   # one row per request
+    with pytest.raises(pol.PolicyError):
+        pol.Policy(48, 10, 10, 1, 4, 1, 1)   # pages of a power-of-two size only
     p.close()
     assert hs.lib  # the GPU library's binding is importable alongside
 
@@ -229,3 +240,63 @@ def test_policy_driven_oracle_run(group):
                 exp = hs_gen.content_np(np.full(o.size, layer), np.full(o.size, wl.src[r]),
                                         p * hs_gen.PAGE + o)
                 assert np.array_equal(ora.host[layer, rows], exp), (r, p, layer)
+
+
+class PageUseDecider:
+    """The policy driven by per-page coldness stamps (hs_policy_step_pages),
+    the table hs_page_touch keeps on the GPU, here written by the oracle's
+    page_touch from the previous step's lists at that step's stamp."""
+
+    def __init__(self, R, n_blocks, n_host_blocks, max_pages, C, tail_pages, touch):
+        self.p = pol.Policy(64, n_blocks, n_host_blocks, R, max_pages, C // 64, tail_pages)
+        self.use = np.zeros((R, max_pages), np.uint32)
+        self.ctx = np.zeros(R, np.int32)
+        self.touch = touch
+
+    def admit(self, r, ctx, host_block_of_page, resident_prefix):
+        self.ctx[r] = ctx
+        return self.p.admit(r, ctx, host_block_of_page, resident_prefix)
+
+    def step(self, stamp, reqs, ctx, topk):
+        if topk is not None:
+            self.touch(self.ctx, topk, stamp - 1, self.use)
+        self.ctx = np.asarray(ctx, np.int32).copy()
+        return self.p.step_pages(reqs, ctx, self.use[np.asarray(reqs)])
+
+
+def _same_edits(a, b):
+    for sa, sb in zip(a.steps, b.steps):
+        for f in ("bt_set", "hbt_set", "hot_set", "reset", "offload", "new_pages"):
+            assert np.array_equal(getattr(sa, f), getattr(sb, f)), (sa.stamp, f)
+    assert len(a.steps) == len(b.steps)
+
+
+@pytest.mark.parametrize("group", [1, 2])
+def test_page_stamps_drive_the_same_decisions_as_lists(group):
+    """Coldness from per-page stamps (one word per page) and from the lists
+    themselves rank pages alike, so the policy makes the same edits."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    import hs_gen
+    import oracle
+    from harness import policy_workload
+    wl, dec = policy_workload(group=group, L=2 * group)
+    assert dec.evicted > 0
+    # the same workload, its decider reading page stamps
+    holder = {}
+
+    class Capture(PageUseDecider):
+        def __init__(self, *a):
+            super().__init__(*a, touch=oracle.page_touch)
+            holder["d"] = self
+
+    R, mp = wl.R, int(max(wl.max_pages, 1))
+    d = Capture(R, wl.n_blocks, dec.p.cfg.num_host_blocks, dec.p.cfg.max_pages, wl.C,
+                dec.p.cfg.tail_pages)
+    spec = hs_gen.Spec(name=wl.name, seed=wl.seed, R=R, L=wl.L, K=wl.K, C=wl.C,
+                       steps=len(wl.steps), ctx0=wl.ctx0.astype(np.int64),
+                       classes=wl.classes, append=int(wl.steps[0].ctx[0] - wl.ctx0[0]),
+                       group=group)
+    wl2 = hs_gen.build_dynamic(spec, d, wl.n_blocks, dec.p.cfg.num_host_blocks)
+    assert mp == wl2.max_pages
+    _same_edits(wl, wl2)
