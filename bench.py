@@ -379,24 +379,26 @@ class QueueFiller:
 
 
 def touch_cost(wl, dev, hev, stream: int, i: int, n: int, busy=None):
-    """hs_page_touch on step i's lists, n launches timed with HIP events on
-    the launch stream; algorithmic bytes: every list entry read once, one
-    4-byte word written per distinct page touched."""
+    """hs_page_touch on step i's lists: n launches back to back between one
+    pair of HIP events on the launch stream; algorithmic bytes: every list
+    entry read once, one 4-byte word written per distinct page touched."""
     import numpy as np
     import torch
 
     from serving_memory_tier_amd import hs_page_touch
     use = torch.zeros((wl.R, wl.max_pages), dtype=torch.int32, device="cuda")
     E = wl.NG * wl.P * wl.K
-    ev = [(hev.new_event(), hev.new_event()) for _ in range(n)]
+    # a launch takes a few microseconds, less than an event pair's own cost:
+    # time n launches back to back between one pair
+    a, b = hev.new_event(), hev.new_event()
+    if busy is not None:
+        busy.fill()
+    hev.record(a, stream)
     for j in range(n):
-        if busy is not None:
-            busy.fill()
-        hev.record(ev[j][0], stream)
         hs_page_touch(dev.layout, dev.batches[i], dev.topk[i], E, wl.steps[i].stamp, use, stream)
-        hev.record(ev[j][1], stream)
+    hev.record(b, stream)
     torch.cuda.synchronize()
-    us = 1e3 * float(np.mean([hev.elapsed_ms(a, b) for a, b in ev]))
+    us = 1e3 * hev.elapsed_ms(a, b) / n
     pages = int((use != 0).sum().item())
     nbytes = wl.R * E * 4 + pages * 4
     return {"us": round(us, 2), "hbm_bytes": nbytes, "hbm_gbps": round(nbytes / us / 1e3, 1),
