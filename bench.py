@@ -42,8 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="mixed_decode",
-                    choices=["mixed_decode", "no_residency", "mixed_state", "multi_layer", "grouped_decode",
-                             "grouped_decode_per_layer"])
+                    choices=["mixed_decode", "no_residency", "mixed_state", "mtp_state",
+                             "multi_layer", "grouped_decode", "grouped_decode_per_layer"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -69,6 +69,8 @@ def build_workload(name: str, n_steps: int):
         return hs_gen.no_residency(steps=n_steps)
     if name == "mixed_state":
         return hs_gen.mixed_state(steps=n_steps)
+    if name == "mtp_state":
+        return hs_gen.mtp_state(steps=n_steps)
     if name == "grouped_decode":
         return hs_gen.grouped_decode(steps=n_steps)
     if name == "grouped_decode_per_layer":

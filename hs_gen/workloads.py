@@ -450,6 +450,22 @@ def mixed_state(seed: int = 1004, steps: int = 16, R: int = 128) -> Workload:
                       ctx0=ctx0, classes=cls, tail_frac=0.25, P=4, shared_src=True))
 
 
+def mtp_state(seed: int = 1004, steps: int = 16, R: int = 128) -> Workload:
+    """mixed_state with the hot buffer sized for speculative decoding (the
+    note on multi-token prediction in the section that estimates the effect
+    for a configuration: every verified token must fit at once, (speculative
+    tokens + 2) x top-K rows): 3 speculative tokens, a 4-position plan,
+    5 x 2048 = 10,240 slots per request; the same contexts, classes and lists
+    as mixed_state."""
+    u = (rng.draws(rng.key(seed, 0xC7), 0, R) >> np.uint64(11)).astype(np.float64) / float(1 << 53)
+    ctx0 = np.floor(np.exp(np.log(8192.0) + u * (np.log(1e6) - np.log(8192.0)))).astype(np.int64)
+    n_full, n_mixed = int(math.floor(0.4 * R)), int(math.floor(0.4 * R))
+    cls = np.array([0] * n_full + [1] * n_mixed + [2] * (R - n_full - n_mixed), dtype=np.int8)
+    cls = cls[rng.permutation(rng.key(seed, 0xC1A5), R)]
+    return build(Spec(name="mtp_state", seed=seed, R=R, L=1, K=2048, C=5 * 2048, steps=steps,
+                      ctx0=ctx0, classes=cls, tail_frac=0.25, P=4, shared_src=True))
+
+
 def grouped_decode(seed: int = 1005, steps: int = 16, R: int = 32, L: int = 4,
                    G: int = 4) -> Workload:
     """mixed_decode with IndexShare ("Use sparsity when needed": one indexer
@@ -568,4 +584,5 @@ CONFIGS = {
     "no_residency": no_residency,
     "mixed_state": mixed_state,
     "grouped_decode": grouped_decode,
+    "mtp_state": mtp_state,
 }

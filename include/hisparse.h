@@ -69,7 +69,7 @@ typedef int32_t hs_status;
 
 /* Limits of the resolver kernel (one workgroup per request-layer, state in LDS). */
 #define HS_MAX_ENTRIES 8192       /* P * K per request-layer */
-#define HS_MAX_HOT_CAPACITY 8192  /* C */
+#define HS_MAX_HOT_CAPACITY 12288 /* C: up to (speculative tokens + 2) x 2048 for 4 tokens */
 
 typedef struct {
   int32_t page_size;          /* tokens per page: a power of two, 1..4096 (64 here) */

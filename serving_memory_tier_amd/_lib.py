@@ -14,7 +14,7 @@ HS_ERR_UNSUPPORTED = 2
 HS_ERR_LAUNCH = 3
 HS_ERR_HIP = 4
 HS_MAX_ENTRIES = 8192
-HS_MAX_HOT_CAPACITY = 8192
+HS_MAX_HOT_CAPACITY = 12288
 
 EXPORTS = ("hs_resolve", "hs_gather", "hs_offload_prefix_pages", "hs_plan_replay",
            "hs_resolve_grouped",

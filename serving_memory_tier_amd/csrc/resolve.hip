@@ -43,6 +43,7 @@
 #include <stdint.h>
 
 #include "fill.h"
+#include "hisparse.h"
 #include "hs_internal.h"
 
 // Phase markers for timing builds; empty in the library.
@@ -59,10 +60,12 @@ constexpr int kThreads = kResolveThreads;
 constexpr int kWaves = kThreads / 64;
 constexpr int32_t kNone = 0x7fffffff;    // "no slot yet" / sort padding
 constexpr int32_t kNoHost = 0x7ffffffe;  // not resident, no host copy (unless it hits)
-// ures of an assigned miss: kMissBase | first_entry << 13 | slot, so that one
+// ures of an assigned miss: kMissBase | first_entry << 14 | slot, so that one
 // atomicMin over the token's entries marks its first occurrence
 constexpr int32_t kMissBase = 1 << 30;
-constexpr int32_t kMissInit = kMissBase | (0x1fff << 13);
+constexpr int kMissSlotBits = 14;                          // slots < 16384
+constexpr int32_t kMissSlotMask = (1 << kMissSlotBits) - 1;
+constexpr int32_t kMissInit = kMissBase | (0x1fff << kMissSlotBits);
 // stamp groups taken one at a time before falling back to a full radix sort
 constexpr int kMaxGroups = 16;
 constexpr int32_t kRowPad = -1;
@@ -80,7 +83,6 @@ struct LdsPlan {
   uint32_t off_ures;   // int32[max(N, sort_n / 2)]: per distinct token: slot or code
                        // (unr and ures together are the sort's exchange buffer)
   uint32_t off_mk;     // uint16[N]: miss rank -> index into the distinct list
-  uint32_t off_stp;    // uint32[C]: slot stamps
   uint32_t off_flag;   // uint8[C]: 0 free, 1 hit, 2 unusable
   uint32_t off_red;    // int32[kRed]: scan / reduction scratch
   uint32_t off_bits;   // uint32[bits_words]: membership filter of the distinct list
@@ -102,7 +104,6 @@ __host__ __device__ inline LdsPlan make_plan(int32_t N, int32_t C, int32_t ES) {
   p.off_unr = o;  o += 4u * (uint32_t)half;   // contiguous with ures (sort exchange)
   p.off_ures = o; o = align16(o + 4u * (uint32_t)half);
   p.off_mk = o;   o = align16(o + 2u * (uint32_t)N);
-  p.off_stp = o;  o = align16(o + 4u * (uint32_t)C);
   p.off_flag = o; o = align16(o + (uint32_t)C);
   p.off_red = o;  o = align16(o + 4u * (uint32_t)kRed);
   // 4 filter bits per possible distinct token (at least 4096): a slot whose
@@ -186,15 +187,24 @@ __device__ int block_compact(const bool (&pred)[E], int (&pos)[E], int* red) {
   }
   __syncthreads();
   if (w == 0) {
-    constexpr int n = E * kWaves;  // <= 128: two counts per lane
-    const int i0 = 2 * l, i1 = 2 * l + 1;
-    const int v0 = i0 < n ? red[i0] : 0;
-    const int v1 = i1 < n ? red[i1] : 0;
-    const int s = v0 + v1;
+    constexpr int n = E * kWaves;            // < kRed
+    constexpr int per = (n + 63) / 64;       // consecutive counts per lane
+    int v[per];
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < per; ++k) {
+      const int i = per * l + k;
+      v[k] = i < n ? red[i] : 0;
+      s += v[k];
+    }
     const int inc = wave_incl_scan(s);
-    const int ex = inc - s;
-    if (i0 < n) red[i0] = ex;
-    if (i1 < n) red[i1] = ex + v0;
+    int ex = inc - s;
+#pragma unroll
+    for (int k = 0; k < per; ++k) {
+      const int i = per * l + k;
+      if (i < n) red[i] = ex;
+      ex += v[k];
+    }
     if (l == 63) red[n] = inc;
   }
   __syncthreads();
@@ -471,7 +481,6 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   int32_t* unr = reinterpret_cast<int32_t*>(lds + plan.off_unr);
   int32_t* ures = reinterpret_cast<int32_t*>(lds + plan.off_ures);
   uint16_t* mk = reinterpret_cast<uint16_t*>(lds + plan.off_mk);
-  uint32_t* sst = reinterpret_cast<uint32_t*>(lds + plan.off_stp);
   uint8_t* sflag = reinterpret_cast<uint8_t*>(lds + plan.off_flag);
   int* red = reinterpret_cast<int*>(lds + plan.off_red);
   uint32_t* fbits = reinterpret_cast<uint32_t*>(lds + plan.off_bits);
@@ -522,14 +531,17 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
     hbv[s] = inrange ? hbt[v >> ps] : -1;
   }
   for (int wi = tid; wi < (1 << fb) / 32; wi += kThreads) fbits[wi] = 0u;
+  // each thread keeps its slots' tokens and stamps in registers
   int32_t tokq[EC];
+  uint32_t cst[EC];
 #pragma unroll
   for (int j = 0; j < EC; ++j) {
     const int q = j * kThreads + tid;
     tokq[j] = -1;
+    cst[j] = 0xffffffffu;
     if (q < C) {
       tokq[j] = stok[q];
-      sst[q] = sstp[q];
+      cst[j] = sstp[q];
       const int32_t hb = hot[q >> ps];
       sflag[q] = (hb >= 0 && hb < pool_blocks) ? 0 : 2;
     }
@@ -661,14 +673,13 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
     // the least-recent stamp among the usable non-hit slots, its group size,
     // and the number of such slots; non-candidates carry stamp ~0 and are
     // never taken (every candidate group is found before them)
-    uint32_t cst[EC];
     uint32_t v = 0xffffffffu;
     int c = 0, nv = 0;
 #pragma unroll
     for (int j = 0; j < EC; ++j) {
       const int q = j * kThreads + tid;
       const bool cand = q < C && sflag[q] == 0;
-      cst[j] = cand ? sst[q] : 0xffffffffu;
+      if (!cand) cst[j] = 0xffffffffu;
       nv += cand ? 1 : 0;
       if (cand) {
         if (cst[j] < v) {
@@ -730,8 +741,8 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
         const int q = j * kThreads + tid;
         predC[j] = q < C && sflag[q] == 0;
         if (predC[j]) {
-          mn = min(mn, sst[q]);
-          mx = max(mx, sst[q]);
+          mn = min(mn, cst[j]);
+          mx = max(mx, cst[j]);
         }
       }
       block_minmax(mn, mx, red);
@@ -753,7 +764,8 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
           one[j] = false;
           if (e < nv) {
             qs[j] = srcb[e];
-            one[j] = ((sst[qs[j]] - mn) >> bit) & 1u;
+            // the pre-call stamps: nothing is stored before the last barrier
+            one[j] = ((sstp[qs[j]] - mn) >> bit) & 1u;
           }
           predC[j] = e < nv && !one[j];
         }
@@ -790,7 +802,8 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
     if (A > 0 && kk[s] >= 0) {
       const int32_t code = ures[kk[s]];
       if (code >= kMissBase && code != kNone)
-        atomicMin(&ures[kk[s]], kMissBase | ((sbase + 64 * s) << 13) | (code & 0x1fff));
+        atomicMin(&ures[kk[s]],
+                  kMissBase | ((sbase + 64 * s) << kMissSlotBits) | (code & kMissSlotMask));
     }
   }
   if (A > 0) __syncthreads();
@@ -802,8 +815,8 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
     if (kk[s] >= 0) {
       const int32_t code = ures[kk[s]];
       if (code >= kMissBase && code != kNone) {
-        const int32_t q = code & 0x1fff;
-        row = -(8 + 2 * q + (((code >> 13) & 0x1fff) == i ? 1 : 0));
+        const int32_t q = code & kMissSlotMask;
+        row = -(8 + 2 * q + (((code >> kMissSlotBits) & 0x1fff) == i ? 1 : 0));
       } else if (code >= 0 && code < C) {
         row = (hot[code >> ps] << ps) | (code & pm);
       } else if (code < 0) {
@@ -851,9 +864,12 @@ hipError_t launch_ec(const KernelArgs& a, int grid, hipStream_t stream) {
   return launch_kernel(fn, dim3(grid), dim3(kThreads), a.lds_bytes, stream, a);
 }
 
-// Largest rounds per thread needed: HS_MAX_ENTRIES and HS_MAX_HOT_CAPACITY
-// are 8192, i.e. 8192 / kThreads rounds.
-constexpr int kMaxRounds = 8192 / kThreads;
+// Largest rounds per thread needed: HS_MAX_ENTRIES (8192) entries and
+// HS_MAX_HOT_CAPACITY (12288) slots, i.e. 8 and 12 rounds of kThreads.
+constexpr int kMaxRounds = HS_MAX_ENTRIES / kThreads;
+constexpr int kMaxSlotRounds = HS_MAX_HOT_CAPACITY / kThreads;
+static_assert(kMaxRounds == 8 && kMaxSlotRounds == 12, "round instantiations below");
+static_assert(HS_MAX_HOT_CAPACITY <= (1 << kMissSlotBits), "slot field of the miss code");
 
 template <int ES, bool FILL>
 hipError_t launch_es(const KernelArgs& a, int grid, int EC, hipStream_t stream) {
@@ -864,8 +880,9 @@ hipError_t launch_es(const KernelArgs& a, int grid, int EC, hipStream_t stream) 
       case 1: return launch_ec<ES, 1, FILL>(a, grid, stream);
       case 2: return launch_ec<ES, 2, FILL>(a, grid, stream);
       case 4: return launch_ec<ES, 4, FILL>(a, grid, stream);
-      case 8: return launch_ec<ES, (8 <= kMaxRounds ? 8 : kMaxRounds), FILL>(a, grid, stream);
-      default: return launch_ec<ES, kMaxRounds, FILL>(a, grid, stream);
+      case 8: return launch_ec<ES, 8, FILL>(a, grid, stream);
+      case 12: return launch_ec<ES, 12, FILL>(a, grid, stream);
+      default: return hipErrorInvalidValue;
     }
   }
 }
@@ -887,6 +904,12 @@ int round_up_pow2_rounds(int n) {
   return e <= 1 ? 1 : e <= 2 ? 2 : e <= 4 ? 4 : e <= 8 ? 8 : 16;
 }
 
+// Rounds of kThreads slots per thread covering C: 1, 2, 4, 8 or 12.
+int slot_rounds(int n) {
+  const int e = (n + kThreads - 1) / kThreads;
+  return e <= 8 ? round_up_pow2_rounds(n) : e <= 12 ? 12 : 16;
+}
+
 }  // namespace
 
 size_t resolve_lds_bytes(int32_t entries, int32_t hot_capacity) {
@@ -895,7 +918,7 @@ size_t resolve_lds_bytes(int32_t entries, int32_t hot_capacity) {
 
 hipError_t launch_resolve(const ResolveParams& p, const FetchParams* fill, hipStream_t stream) {
   const int ES = round_up_pow2_rounds(p.entries);
-  const int EC = round_up_pow2_rounds(p.hot_capacity);
+  const int EC = slot_rounds(p.hot_capacity);
   KernelArgs a;
   a.p = p;
   a.plan = make_plan(p.entries, p.hot_capacity, ES);

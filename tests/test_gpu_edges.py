@@ -208,6 +208,11 @@ CASES = [
     ("k1", 4, 1, 1, 1, 64, 64, 656, 30, False),
     ("max_entries", 2, 1, 4, 2048, 8192, 64, 656, 400, False),
     ("max_capacity", 2, 1, 1, 2048, 8192, 64, 656, 300, False),
+    # speculative decoding's sizing: (3 speculative tokens + 2) x 2048 slots for
+    # a 4-position plan, and the largest capacity the resolver takes
+    ("mtp_capacity", 2, 1, 4, 2048, 10240, 64, 656, 400, False),
+    ("max_capacity_12k", 2, 1, 1, 2048, 12288, 64, 656, 400, False),
+    ("hostile_c9216", 3, 1, 2, 900, 9216, 64, 656, 300, True),
     ("min_capacity", 5, 1, 1, 300, 64, 64, 656, 40, False),
     ("page16", 3, 2, 2, 700, 1024, 16, 656, 900, False),
     ("page128_rb64", 3, 1, 1, 1500, 2048, 128, 64, 80, False),
@@ -350,5 +355,46 @@ def test_random_grouped_cases(name, R, L, G, P, K, C, page, rb, n_pages, hostile
             assert np.array_equal(tok, a["tok"])
             assert np.array_equal(stp, a["stp"])
             assert np.array_equal(pool, a["pool"])
+    finally:
+        case.close()
+
+
+@pytest.mark.parametrize("mode", stages.MODES)
+@pytest.mark.parametrize("C", [512, 10240])
+def test_victims_across_many_stamp_groups(C, mode):
+    """Every slot holds a token the lists do not ask for, each slot with a
+    stamp of its own, and a list misses more tokens than sixteen stamp groups
+    hold: the resolver takes its victims through its full sort of the
+    candidates by stamp instead of group by group."""
+    rs = np.random.default_rng(zlib.crc32(f"groups{C}".encode()))
+    page, rb, R, L = 64, 656, 2, 1
+    K = min(2048, C // 2)
+    n_pages = 2 * (C // page) + 4 * (K // page)
+    ctx = np.full(R, n_pages * page, np.int32)
+    n_blocks = R * (C // page) + 4
+    pool = rs.integers(0, 256, size=(L, n_blocks * page, rb), dtype=np.uint8)
+    host = rs.integers(0, 256, size=(L, R * n_pages * page, rb), dtype=np.uint8)
+    bt = np.full((R, n_pages), -1, np.int32)                    # nothing resident
+    hbt = np.stack([rs.permutation(n_pages) + r * n_pages for r in range(R)]).astype(np.int32)
+    hot = (np.arange(R * (C // page)).reshape(R, C // page) + 2).astype(np.int32)
+    tok = np.stack([rs.permutation(C) for _ in range(R)]).reshape(R, L, C).astype(np.int32)
+    stp = np.stack([rs.permutation(C) + 1 for _ in range(R)]).reshape(R, L, C).astype(np.uint32)
+    a = dict(pool=pool, host=host, bt=bt, hbt=hbt, ctx=ctx, hot=hot, tok=tok, stp=stp)
+    case = GpuCase(page, pool, host, bt, hbt, ctx, hot, tok.copy(), stp.copy(), C)
+    try:
+        # step 1: K distinct misses beyond the slots' tokens; step 2: half of
+        # them again (now hits) and fresh misses
+        first = np.stack([rs.choice(np.arange(C, n_pages * page), K, replace=False)
+                          for _ in range(R)]).reshape(R, L, K).astype(np.int32)
+        _say(f"[edges] stamp groups C={C} {mode} step 1")
+        _, st = _compare(case, a, first, C + 5, mode=mode)
+        assert (st[..., 2] == K).all() and (st[..., 3] == 0).all()
+        second = first.copy()
+        for r in range(R):
+            fresh = np.setdiff1d(np.arange(C, n_pages * page), first[r, 0])
+            second[r, 0, K // 2:] = rs.choice(fresh, K - K // 2, replace=False)
+        _say(f"[edges] stamp groups C={C} {mode} step 2")
+        _, st = _compare(case, a, second, C + 9, mode=mode)
+        assert (st[..., 1] == K // 2).all()
     finally:
         case.close()

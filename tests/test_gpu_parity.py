@@ -148,6 +148,21 @@ def test_mixed_state_full_sampled():
     run_parity(wl, requests=sample, fused_plan=True)
 
 
+def test_mtp_state_full_sampled():
+    """The speculative-decoding sizing at full size: 128 requests, a
+    4-position plan of 2048 each, 10,240 hot slots per request."""
+    wl = hs_gen.mtp_state(steps=8)
+    assert wl.C == 10240 and wl.P * wl.K == 8192
+    sample = []
+    for c in (0, 1, 2):
+        sample += list(np.nonzero(wl.classes == c)[0][:2])
+    sample += [int(np.argmax(wl.ctx0))]
+    sample = sorted(set(int(s) for s in sample))
+    totals = run_parity(wl, requests=sample, fused_plan=True)
+    assert totals[3] == 0          # the plan's union always fits: no overflow
+    assert totals[1] > 0 and totals[2] > 0
+
+
 def test_multi_layer_full_sampled():
     wl = hs_gen.multi_layer(turns=4)
     run_parity(wl, requests=[0, 17, 63], fused_plan=False)
