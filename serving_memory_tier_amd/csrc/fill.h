@@ -363,6 +363,35 @@ __device__ void fill_gather(const FetchParams& p, int32_t* lds, int32_t rl, int3
   }
 }
 
+// Pieces [g_lo, g_hi) of the host rows of the first entries list[], U reads
+// in flight a thread; g_lo is a multiple of kT.
+template <int U>
+__device__ __forceinline__ void host_rows(const FetchParams& p, const Rl& v, const int32_t* list,
+                                          const int32_t* src, const uint8_t* host_l,
+                                          uint8_t* out, int32_t g_lo, int32_t g_hi) {
+  const int tid = threadIdx.x;
+  for (int32_t g0 = g_lo; g0 < g_hi; g0 += kT * U) {
+    u32x4 val[U];
+    uint8_t* dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t g = g0 + u * kT + tid;
+      dst[u] = nullptr;
+      if (g < g_hi) {
+        const int32_t j = pdiv(g, v.magic);
+        const int32_t pc = g - j * v.pieces;
+        const int32_t e = list[j];
+        const int64_t hrow = (int64_t)((uint32_t)src[e] & ~kHostTag);
+        val[u] = *reinterpret_cast<const u32x4*>(host_l + hrow * p.row_bytes + pc * 16);
+        dst[u] = out + (int64_t)e * p.row_bytes + pc * 16;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
+  }
+}
+
 // Miss workgroup s of S for one request-layer: the rows of the miss tokens t
 // with t mod S == s, each read once from the host into its first entry and
 // then copied to its later entries.
@@ -423,32 +452,12 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   HS_FILL_MARK(3);
 
   // ---- host rows of the first entries, in each layer of the group,
-  // kHostUnroll reads in flight a thread
+  // kHostUnroll reads in flight a thread (more in flight at the end of the
+  // step, when the gathers are done, gains nothing: the link is the bound)
   const int32_t total = n_first * v.pieces;
-  for (int32_t l = 0; l < v.group; ++l) {
-    const uint8_t* host_l = v.host_l + l * v.host_stride;
-    uint8_t* out = v.out + l * v.out_stride;
-    for (int32_t g0 = 0; g0 < total; g0 += kT * kHostUnroll) {
-      u32x4 val[kHostUnroll];
-      uint8_t* dst[kHostUnroll];
-#pragma unroll
-      for (int u = 0; u < kHostUnroll; ++u) {
-        const int32_t g = g0 + u * kT + tid;
-        dst[u] = nullptr;
-        if (g < total) {
-          const int32_t j = pdiv(g, v.magic);
-          const int32_t pc = g - j * v.pieces;
-          const int32_t e = list[j];
-          const int64_t hrow = (int64_t)((uint32_t)src[e] & ~kHostTag);
-          val[u] = *reinterpret_cast<const u32x4*>(host_l + hrow * p.row_bytes + pc * 16);
-          dst[u] = out + (int64_t)e * p.row_bytes + pc * 16;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kHostUnroll; ++u)
-        if (dst[u]) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst[u]));
-    }
-  }
+  for (int32_t l = 0; l < v.group; ++l)
+    host_rows<kHostUnroll>(p, v, list, src, v.host_l + l * v.host_stride, v.out + l * v.out_stride,
+                           0, total);
   if (n_dup == 0) return;
   __syncthreads();  // this workgroup's row writes are visible to it
 

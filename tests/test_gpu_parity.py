@@ -232,3 +232,28 @@ def test_policy_driven_decode():
     totals = run_parity(wl)
     _say(f"[parity] policy_decode totals {totals.tolist()}")
     assert totals[2] > 0
+
+
+def test_plan_rows_replayed_by_gather():
+    """Speculative decoding ("Integration with the rest of vLLM": a per-step
+    replayable plan): the draft and verify forwards of a step re-read the
+    plan's rows with hs_gather on its row ids, at the hot buffer size for
+    three speculative tokens, and get exactly the plan's own gathered rows."""
+    from serving_memory_tier_amd.runner import DeviceRun
+    wl = hs_gen.mtp_state(steps=3)
+    dev = DeviceRun(wl)
+    dev.upload_steps()
+    try:
+        for i in range(len(wl.steps)):
+            _say(f"[parity] plan replay step {i}")
+            dev.pre(i)
+            dev.plan_step(i)
+            torch.cuda.synchronize()
+            planned = dev.out.clone()
+            for forward in range(2):       # draft, then verify
+                dev.out.zero_()
+                dev.gather()
+                torch.cuda.synchronize()
+                assert torch.equal(dev.out, planned), f"forward {forward}, step {i}"
+    finally:
+        dev.close()
