@@ -276,6 +276,51 @@ hs_status hs_page_touch(const hs_layout* layout, const hs_batch* batch, const in
                         int32_t entries_per_req, uint32_t stamp, uint32_t* page_use,
                         hipStream_t stream);
 
+/*
+ * hs_sparse_mla_decode -- gather-free consumption of the resolved rows: sparse
+ * MLA decode attention that reads every selected row in place, by the row
+ * id the resolver returned ("Use sparsity when needed": hot pages live in the
+ * same KV-cache tensor as resident pages, so the sparse MLA kernel sees them
+ * as ordinary pages; "How it works": one row id whether resident or hot).
+ * No gathered copy of the rows is made.
+ * Row format (layout->row_bytes must be 656, else HS_ERR_UNSUPPORTED): 512
+ * latent values in OCP FP8 E4M3, then 4 little-endian float32 scales (scale
+ * t for latent values [128 t, 128 t + 128)), then 64 rope values in
+ * bfloat16.  A row's key is its scaled latent values followed by its rope
+ * values (576); its value is the scaled latent values (512).
+ * For token i < num_tokens and head h < num_heads:
+ *   s_j = sm_scale * <q[i][h], key(row_ids[i][j])> over j < top_k whose row id
+ *         lies in [0, layout->pool_rows) (others select nothing);
+ *   out[i][h] = sum_j softmax(s)_j value(row_ids[i][j]);
+ *   lse[i][h] = log(sum_j exp(s_j)) (natural log); out 0 and lse -inf when
+ *   no row is selected.
+ * Arguments: kv_layer = one layer of the pool (device, 16-byte aligned; add
+ * the layer stride to kv_pool); row_ids device [num_tokens][top_k] (e.g. a
+ * plan's [R][P][K] row ids for one layer, tokens = R * P); q device bf16
+ * [num_tokens][num_heads][576]; out device float [num_tokens][num_heads][512];
+ * lse device float [num_tokens][num_heads]; num_heads a multiple of 16;
+ * workspace: device memory of at least hs_sparse_mla_workspace_bytes(...)
+ * bytes, 16-byte aligned (may be NULL when that is 0), overwritten.
+ * Precision: keys and values are used exactly (E4M3 values are bfloat16
+ * values; the scales are applied in float32), products accumulate in
+ * float32, the probabilities times the value scales are rounded to bfloat16
+ * for the value products.
+ * Execution: all on `stream`; calls sharing a workspace must not overlap.
+ * Errors: HS_ERR_INVALID_ARGUMENT (null or misaligned pointers with work to
+ * do, a short workspace, num_heads not a positive multiple of 16, negative
+ * sizes, bad layout), HS_ERR_UNSUPPORTED (row_bytes != 656, more than 65535
+ * tokens), HS_ERR_LAUNCH.
+ */
+hs_status hs_sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
+                               const int32_t* row_ids, int32_t num_tokens, int32_t top_k,
+                               const uint16_t* q, int32_t num_heads, float sm_scale, float* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Bytes of workspace hs_sparse_mla_decode needs for these sizes (0 when it
+ * needs none, or for non-positive sizes). */
+size_t hs_sparse_mla_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t top_k);
+
 /* A static English description of a status code. */
 const char* hs_status_string(hs_status status);
 

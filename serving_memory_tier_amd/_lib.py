@@ -19,7 +19,8 @@ HS_MAX_HOT_CAPACITY = 12288
 EXPORTS = ("hs_resolve", "hs_gather", "hs_offload_prefix_pages", "hs_plan_replay",
            "hs_resolve_grouped",
            "hs_resolve_decide", "hs_resolve_fetch", "hs_resolve_move", "hs_resolve_commit",
-           "hs_page_touch", "hs_status_string", "hs_last_error", "hs_host_alloc", "hs_host_free",
+           "hs_page_touch", "hs_sparse_mla_decode", "hs_sparse_mla_workspace_bytes",
+           "hs_status_string", "hs_last_error", "hs_host_alloc", "hs_host_free",
            "hs_host_device_pointer")
 
 
@@ -67,6 +68,9 @@ def lib():
         L.hs_resolve_move.argtypes = [lay, bat, vp, i32, i32, vp, vp, vp]
         L.hs_resolve_commit.argtypes = [lay, bat, vp, i32, i32, vp, vp, vp]
         L.hs_page_touch.argtypes = [lay, bat, vp, i32, u32, vp, vp]
+        L.hs_sparse_mla_decode.argtypes = [lay, vp, vp, i32, i32, vp, i32, ctypes.c_float, vp,
+                                           vp, vp, sz, vp]
+        L.hs_sparse_mla_workspace_bytes.argtypes = [i32, i32, i32]
         L.hs_status_string.argtypes = [i32]
         L.hs_status_string.restype = ctypes.c_char_p
         L.hs_last_error.argtypes = []
@@ -78,5 +82,6 @@ def lib():
             if name in ("hs_status_string", "hs_last_error"):
                 continue
             getattr(L, name).restype = i32
+        L.hs_sparse_mla_workspace_bytes.restype = sz
         _lib = L
     return _lib

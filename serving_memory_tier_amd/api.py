@@ -137,6 +137,24 @@ def hs_page_touch(layout: HsLayout, batch: HsBatch, topk, entries_per_req: int, 
            "hs_page_touch")
 
 
+def hs_sparse_mla_workspace_bytes(num_tokens: int, num_heads: int, top_k: int) -> int:
+    return int(lib().hs_sparse_mla_workspace_bytes(num_tokens, num_heads, top_k))
+
+
+def hs_sparse_mla_decode(layout: HsLayout, kv_layer, row_ids, num_tokens: int, top_k: int, q,
+                         num_heads: int, sm_scale: float, out, lse, workspace=None,
+                         workspace_bytes: int = 0, stream=None) -> None:
+    """kv_layer: a uint8 device tensor (one layer of the pool) or a device
+    address; workspace: a device tensor of hs_sparse_mla_workspace_bytes."""
+    kv = kv_layer if isinstance(kv_layer, int) else _ptr(kv_layer)
+    if workspace is not None and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().hs_sparse_mla_decode(ctypes.byref(layout), kv, _ptr(row_ids), num_tokens, top_k,
+                                      _ptr(q), num_heads, sm_scale, _ptr(out), _ptr(lse),
+                                      _ptr(workspace), workspace_bytes, _stream(stream)),
+           "hs_sparse_mla_decode")
+
+
 def hs_host_alloc(nbytes: int) -> int:
     p = ctypes.c_void_p()
     _check(lib().hs_host_alloc(nbytes, ctypes.byref(p)), "hs_host_alloc")

@@ -7,7 +7,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["resolve.hip", "copy.hip", "fetch.hip", "touch.hip", "api.hip"]
+SOURCES = ["resolve.hip", "copy.hip", "fetch.hip", "touch.hip", "attend.hip", "api.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are switched off for all HIP code (hipcc's host pass

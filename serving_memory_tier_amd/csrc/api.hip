@@ -396,6 +396,62 @@ hs_status hs_page_touch(const hs_layout* layout, const hs_batch* batch, const in
   return from_hip(hs::launch_page_touch(p, stream), "page touch launch");
 }
 
+namespace {
+
+// The attention plan for a call, and the workspace it needs (0: one split).
+hs::AttendParams attend_plan(int32_t num_tokens, int32_t num_heads, int32_t top_k,
+                             size_t* workspace) {
+  hs::AttendParams p{};
+  p.num_tokens = num_tokens;
+  p.num_heads = num_heads;
+  p.top_k = top_k;
+  hs::plan_attend(p, hs::kAttendTargetGroups);
+  *workspace = p.splits > 1 ? (size_t)num_tokens * p.splits * num_heads * (512 + 2) * 4 : 0;
+  return p;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+}  // namespace
+
+size_t hs_sparse_mla_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t top_k) {
+  if (num_tokens <= 0 || num_heads <= 0 || top_k < 0) return 0;
+  size_t ws = 0;
+  attend_plan(num_tokens, num_heads, top_k, &ws);
+  return ws;
+}
+
+hs_status hs_sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
+                               const int32_t* row_ids, int32_t num_tokens, int32_t top_k,
+                               const uint16_t* q, int32_t num_heads, float sm_scale, float* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  hs_status s = check_layout(layout);
+  if (s != HS_OK) return s;
+  if (layout->row_bytes != 656) return HS_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || top_k < 0 || num_heads <= 0 || num_heads % 16 != 0)
+    return HS_ERR_INVALID_ARGUMENT;
+  if (num_tokens > 65535 || num_heads > 16 * 65535) return HS_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return HS_OK;
+  if (!q || !out || !lse || (top_k > 0 && (!kv_layer || !row_ids))) return HS_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(out) || (kv_layer && !aligned16(kv_layer)))
+    return HS_ERR_INVALID_ARGUMENT;
+  size_t need = 0;
+  hs::AttendParams p = attend_plan(num_tokens, num_heads, top_k, &need);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return HS_ERR_INVALID_ARGUMENT;
+  p.kv = kv_layer;
+  p.pool_rows = layout->pool_rows;
+  p.row_ids = row_ids;
+  p.q = q;
+  p.sm_scale = sm_scale;
+  p.out = out;
+  p.lse = lse;
+  p.part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.part_ml = need > 0 ? p.part_o + (size_t)num_tokens * p.splits * num_heads * 512 : nullptr;
+  return from_hip(hs::launch_attend(p, stream), "sparse MLA launch");
+}
+
 const char* hs_last_error(void) { return g_last_error; }
 
 const char* hs_status_string(hs_status status) {

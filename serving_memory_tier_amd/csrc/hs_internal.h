@@ -223,4 +223,33 @@ constexpr int64_t kTouchMaxEntries = kTouchPerBlock * 65535;
 
 hipError_t launch_page_touch(const TouchParams& p, hipStream_t stream);
 
+// Sparse MLA decode over rows read in place by row id (attend.hip): 656-byte
+// FP8 MLA rows, 576-wide bf16 queries, 512-wide float32 outputs.
+constexpr int kAttendThreads = 256;
+constexpr int kAttendHeadsPerGroup = 64;   // heads per workgroup (16 per wave)
+constexpr int kAttendMaxSplits = 64;       // key splits per (token, head group), at most
+constexpr int64_t kAttendTargetGroups = 512;
+
+struct AttendParams {
+  const uint8_t* kv;        // one layer of the pool
+  int64_t pool_rows;
+  const int32_t* row_ids;   // [tokens][top_k]
+  int32_t top_k;
+  int32_t num_tokens;
+  const uint16_t* q;        // [tokens][heads][576] bf16
+  int32_t num_heads;
+  float sm_scale;
+  float* out;               // [tokens][heads][512]
+  float* lse;               // [tokens][heads]
+  float* part_o;            // workspace: [tokens][splits][heads][512]
+  float* part_ml;           // workspace: [tokens][splits][heads][2]
+  int32_t splits;
+  int32_t keys_per_split;   // a multiple of 32
+};
+
+size_t attend_lds_bytes();
+// Sets splits and keys_per_split for about target_groups workgroups.
+void plan_attend(AttendParams& p, int64_t target_groups);
+hipError_t launch_attend(const AttendParams& p, hipStream_t stream);
+
 }  // namespace hs

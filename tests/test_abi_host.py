@@ -26,7 +26,8 @@ def lib():
 
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "hisparse.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:hs_status|const char\*)\s+(hs_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:hs_status|const char\*|size_t)\s+(hs_\w+)\s*\(", text,
+                                 re.M)))
 
 
 def test_exports_every_declared_function(lib):
@@ -193,3 +194,25 @@ def test_page_touch_rejects(lib):
     assert t(lay, b, None, 0, None) == 0                     # nothing to do
     empty = HsBatch(0, 16, None, None, None, None, None, None, None, None)
     assert t(lay, empty, None, 8, None) == 0
+
+
+def test_sparse_mla_rejects(lib):
+    lay = _layout()
+    P = 0x1000
+    f = lambda lay_, kv, ids, T, K, q, H, out, lse, ws, wsb: lib.hs_sparse_mla_decode(
+        ctypes.byref(lay_), kv, ids, T, K, q, H, 0.1, out, lse, ws, wsb, None)
+    need = lib.hs_sparse_mla_workspace_bytes(32, 128, 2048)
+    assert need > 0
+    assert f(_layout(row_bytes=512), P, P, 1, 64, P, 16, P, P, P, need) == 2
+    assert f(lay, P, P, 1, 64, P, 24, P, P, P, need) == 1        # heads not a multiple of 16
+    assert f(lay, P, P, 1, 64, P, 0, P, P, P, need) == 1
+    assert f(lay, P, P, -1, 64, P, 16, P, P, P, need) == 1
+    assert f(lay, P, P, 70000, 64, P, 16, P, P, P, need) == 2
+    assert f(lay, None, P, 1, 64, P, 16, P, P, P, need) == 1
+    assert f(lay, P, None, 1, 64, P, 16, P, P, P, need) == 1
+    assert f(lay, P, P, 1, 64, None, 16, P, P, P, need) == 1
+    assert f(lay, P, P, 1, 64, P + 4, 16, P, P, P, need) == 1    # misaligned queries
+    assert f(lay, P, P, 32, 2048, P, 128, P, P, None, need) == 1  # workspace needed
+    assert f(lay, P, P, 32, 2048, P, 128, P, P, P, need - 16) == 1
+    assert f(lay, P, P, 0, 64, None, 16, None, None, None, 0) == 0   # nothing to do
+    assert lib.hs_sparse_mla_workspace_bytes(0, 16, 64) == 0
