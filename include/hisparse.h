@@ -277,6 +277,23 @@ hs_status hs_page_touch(const hs_layout* layout, const hs_batch* batch, const in
                         hipStream_t stream);
 
 /*
+ * hs_resolve_in_place -- hs_plan_replay for consumers that read the rows in
+ * place by row id (hs_sparse_mla_decode): the same row ids, stats, hot-buffer
+ * state, pool and offload as hs_plan_replay with gather_out = NULL, but the
+ * misses' host reads run while the resolver decides, as in the overlapped
+ * form, staged through `staging` instead of a gathered output: no resident
+ * or hot row is copied anywhere.
+ * staging: device [R][L][P][K][row_bytes], caller-owned scratch; only the
+ * rows of missed tokens' first entries (and of misses left without a slot)
+ * are written, its contents afterwards are unspecified.
+ * Errors: as hs_plan_replay; a NULL staging is HS_ERR_INVALID_ARGUMENT.
+ */
+hs_status hs_resolve_in_place(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                              int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
+                              uint8_t* staging, int32_t* stats, const int32_t* offload_pairs,
+                              int32_t n_offload, hipStream_t stream);
+
+/*
  * hs_sparse_mla_decode -- gather-free consumption of the resolved rows: sparse
  * MLA decode attention that reads every selected row in place, by the row
  * id the resolver returned ("Use sparsity when needed": hot pages live in the

@@ -16,7 +16,7 @@ from ._lib import (EXPORTS, HS_ERR_HIP, HS_ERR_INVALID_ARGUMENT, HS_ERR_LAUNCH,
 from .api import (HostPool, batch_of, hs_gather, hs_host_alloc, hs_host_device_pointer,
                   hs_host_free, hs_offload_prefix_pages, hs_plan_replay, hs_resolve,
                   hs_resolve_commit, hs_resolve_decide, hs_resolve_fetch, hs_resolve_grouped,
-                  hs_resolve_move, hs_page_touch, hs_sparse_mla_decode,
+                  hs_resolve_move, hs_page_touch, hs_resolve_in_place, hs_sparse_mla_decode,
                   hs_sparse_mla_workspace_bytes,
                   hs_status_string, layout_of)
 
@@ -28,7 +28,7 @@ __all__ = [
     "hs_offload_prefix_pages", "hs_plan_replay", "hs_resolve_grouped", "hs_resolve_decide",
     "hs_resolve_fetch",
     "hs_resolve_move", "hs_resolve_commit", "hs_page_touch",
-    "hs_sparse_mla_decode", "hs_sparse_mla_workspace_bytes",
+    "hs_resolve_in_place", "hs_sparse_mla_decode", "hs_sparse_mla_workspace_bytes",
     "hs_status_string", "hs_host_alloc",
     "hs_host_free", "hs_host_device_pointer",
 ]

@@ -19,7 +19,7 @@ HS_MAX_HOT_CAPACITY = 12288
 EXPORTS = ("hs_resolve", "hs_gather", "hs_offload_prefix_pages", "hs_plan_replay",
            "hs_resolve_grouped",
            "hs_resolve_decide", "hs_resolve_fetch", "hs_resolve_move", "hs_resolve_commit",
-           "hs_page_touch", "hs_sparse_mla_decode", "hs_sparse_mla_workspace_bytes",
+           "hs_page_touch", "hs_resolve_in_place", "hs_sparse_mla_decode", "hs_sparse_mla_workspace_bytes",
            "hs_status_string", "hs_last_error", "hs_host_alloc", "hs_host_free",
            "hs_host_device_pointer")
 
@@ -68,6 +68,7 @@ def lib():
         L.hs_resolve_move.argtypes = [lay, bat, vp, i32, i32, vp, vp, vp]
         L.hs_resolve_commit.argtypes = [lay, bat, vp, i32, i32, vp, vp, vp]
         L.hs_page_touch.argtypes = [lay, bat, vp, i32, u32, vp, vp]
+        L.hs_resolve_in_place.argtypes = [lay, bat, vp, i32, i32, u32, vp, vp, vp, vp, i32, vp]
         L.hs_sparse_mla_decode.argtypes = [lay, vp, vp, i32, i32, vp, i32, ctypes.c_float, vp,
                                            vp, vp, sz, vp]
         L.hs_sparse_mla_workspace_bytes.argtypes = [i32, i32, i32]

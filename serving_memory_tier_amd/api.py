@@ -137,6 +137,15 @@ def hs_page_touch(layout: HsLayout, batch: HsBatch, topk, entries_per_req: int, 
            "hs_page_touch")
 
 
+def hs_resolve_in_place(layout: HsLayout, batch: HsBatch, topk, num_pos: int, top_k: int,
+                        stamp: int, row_ids, staging, stats, offload_pairs=None, n_offload: int = 0,
+                        stream=None) -> None:
+    _check(lib().hs_resolve_in_place(ctypes.byref(layout), ctypes.byref(batch), _ptr(topk),
+                                     num_pos, top_k, ctypes.c_uint32(stamp), _ptr(row_ids),
+                                     _ptr(staging), _ptr(stats), _ptr(offload_pairs), n_offload,
+                                     _stream(stream)), "hs_resolve_in_place")
+
+
 def hs_sparse_mla_workspace_bytes(num_tokens: int, num_heads: int, top_k: int) -> int:
     return int(lib().hs_sparse_mla_workspace_bytes(num_tokens, num_heads, top_k))
 

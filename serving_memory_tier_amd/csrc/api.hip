@@ -141,7 +141,8 @@ hs::FetchParams fetch_params(const hs_layout* lay, const hs_batch* b, const int3
 
 hs_status launch_decide(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
                         int32_t N, uint32_t stamp, int32_t* row_ids, int32_t* stats,
-                        hipStream_t stream, uint8_t* fill_out = nullptr, int32_t group = 1) {
+                        hipStream_t stream, uint8_t* fill_out = nullptr, int32_t group = 1,
+                        bool misses_only = false) {
   if ((int64_t)b->num_reqs * lay->num_layers == 0) return HS_OK;
   // with layer groups the resolver runs once per (request, group): the state,
   // lists and row ids are per group
@@ -175,6 +176,7 @@ hs_status launch_decide(const hs_layout* lay, const hs_batch* b, const int32_t* 
     hs::FetchParams f = fetch_params(&glay, b, topk, N, fill_out);
     f.group = group;
     f.layers = lay->num_layers;
+    f.misses_only = misses_only ? 1 : 0;
     return from_hip(hs::launch_resolve(p, &f, stream), "resolver launch");
   }
   return from_hip(hs::launch_resolve(p, nullptr, stream), "resolver launch");
@@ -250,7 +252,8 @@ bool fetch_fits(const hs_layout* lay, int32_t N) {
 hs_status resolve_common(const hs_layout* lay, const hs_batch* b, const int32_t* topk,
                          int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
                          uint8_t* gather_out, int32_t* stats, const int32_t* offload_pairs,
-                         int32_t n_offload, hipStream_t stream, int32_t group = 1) {
+                         int32_t n_offload, hipStream_t stream, int32_t group = 1,
+                         uint8_t* staging = nullptr) {
   hs_status s = check_resolve(lay, b, topk, num_pos, top_k, row_ids);
   if (s != HS_OK) return s;
   if (group < 1 || lay->num_layers % group != 0) return HS_ERR_INVALID_ARGUMENT;
@@ -259,7 +262,14 @@ hs_status resolve_common(const hs_layout* lay, const hs_batch* b, const int32_t*
   if (n_offload > 0 && (!offload_pairs || !b->kv_pool || !b->host_pool))
     return HS_ERR_INVALID_ARGUMENT;
   const int32_t N = num_pos * top_k;
-  if (gather_out && fetch_fits(lay, N)) {
+  if (staging && fetch_fits(lay, N)) {
+    // rows read in place later: only the misses' host rows are staged, at
+    // their first entries, while the resolver decides; commit moves them
+    s = launch_decide(lay, b, topk, N, stamp, row_ids, stats, stream, staging, group, true);
+    if (s != HS_OK) return s;
+    s = launch_move_mode(lay, b, topk, N, row_ids, staging, hs::kMoveCommit, stream, group);
+    if (s != HS_OK) return s;
+  } else if (gather_out && fetch_fits(lay, N)) {
     s = launch_decide(lay, b, topk, N, stamp, row_ids, stats, stream, gather_out, group);
     if (s != HS_OK) return s;
     s = launch_move_mode(lay, b, topk, N, row_ids, gather_out, hs::kMoveCommit, stream, group);
@@ -295,6 +305,15 @@ hs_status hs_plan_replay(const hs_layout* layout, const hs_batch* batch, const i
                          int32_t n_offload, hipStream_t stream) {
   return resolve_common(layout, batch, topk, num_pos, top_k, stamp, row_ids, gather_out, stats,
                         offload_pairs, n_offload, stream);
+}
+
+hs_status hs_resolve_in_place(const hs_layout* layout, const hs_batch* batch, const int32_t* topk,
+                              int32_t num_pos, int32_t top_k, uint32_t stamp, int32_t* row_ids,
+                              uint8_t* staging, int32_t* stats, const int32_t* offload_pairs,
+                              int32_t n_offload, hipStream_t stream) {
+  if (!staging) return HS_ERR_INVALID_ARGUMENT;
+  return resolve_common(layout, batch, topk, num_pos, top_k, stamp, row_ids, nullptr, stats,
+                        offload_pairs, n_offload, stream, 1, staging);
 }
 
 hs_status hs_resolve_grouped(const hs_layout* layout, const hs_batch* batch, int32_t group_layers,

@@ -71,7 +71,7 @@ int64_t prepare_fetch(FetchParams& p, size_t* lds_bytes) {
   const int64_t pairs = n_rl * S;
   p.miss_groups = (int32_t)(pairs < kFetchHostGroups ? pairs : kFetchHostGroups);
   // gather workgroups: gather_e entries each
-  p.gather_splits = (p.entries + p.gather_e - 1) / p.gather_e;
+  p.gather_splits = p.misses_only ? 0 : (p.entries + p.gather_e - 1) / p.gather_e;
   return p.miss_groups + n_rl * p.gather_splits;
 }
 

@@ -458,7 +458,7 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   for (int32_t l = 0; l < v.group; ++l)
     host_rows<kHostUnroll>(p, v, list, src, v.host_l + l * v.host_stride, v.out + l * v.out_stride,
                            0, total);
-  if (n_dup == 0) return;
+  if (n_dup == 0 || p.misses_only) return;
   __syncthreads();  // this workgroup's row writes are visible to it
 
   // ---- later entries of the owned miss tokens copy the first entry's row

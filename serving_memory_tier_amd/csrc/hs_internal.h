@@ -179,6 +179,9 @@ struct FetchParams {
   int32_t miss_groups, miss_splits, gather_splits;
   int32_t lds_n, miss_tab_n, gather_e, gather_tab_n;
   uint32_t piece_magic;
+  // 1: no gather workgroups; the misses' host rows go to their first entries
+  // only (a staging buffer for callers that read rows in place)
+  int32_t misses_only = 0;
 };
 
 // Bytes of dynamic LDS a fill workgroup needs for N entries.

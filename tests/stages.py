@@ -9,7 +9,9 @@ the library against the oracle:
   serial  -- hs_resolve_decide, then hs_resolve_move (host copies in the mover);
   staged  -- the overlapped form scheduled by the caller: hs_resolve_decide on a
              second stream, hs_resolve_fetch (the early fill of every output
-             row) on the first, a join, then hs_resolve_commit.
+             row) on the first, a join, then hs_resolve_commit;
+  in_place -- hs_resolve_in_place: no gathered rows (``out`` is only staging
+             for the misses' host rows), for consumers that read rows by id.
 """
 
 from __future__ import annotations
@@ -18,7 +20,7 @@ import torch
 
 import serving_memory_tier_amd as hs
 
-MODES = ("call", "fused", "serial", "staged")
+MODES = ("call", "fused", "serial", "staged", "in_place")
 
 
 def run(mode, layout, batch, topk, P, K, stamp, rows, out, stats, pairs=None, n_pairs=0,
@@ -29,6 +31,10 @@ def run(mode, layout, batch, topk, P, K, stamp, rows, out, stats, pairs=None, n_
             hs.hs_resolve(layout, batch, topk, K, stamp, rows, out, stats)
         else:
             hs.hs_plan_replay(layout, batch, topk, P, K, stamp, rows, out, stats, pairs, n_pairs)
+        return
+    if mode == "in_place":
+        assert out is not None, "the in-place form stages misses in a buffer of the output's size"
+        hs.hs_resolve_in_place(layout, batch, topk, P, K, stamp, rows, out, stats, pairs, n_pairs)
         return
     main = torch.cuda.current_stream()
     if mode == "serial":

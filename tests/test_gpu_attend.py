@@ -126,3 +126,80 @@ def test_decode_shape_sampled():
     ids = rs.integers(0, n, size=(32, 2048)).astype(np.int32)
     ids[:, -5:] = -1
     check(pool, ids, q, 1.0 / math.sqrt(576))
+
+
+def _sanitize(t: torch.Tensor) -> None:
+    """Make a pool of synthetic bytes a pool of valid FP8 MLA rows, in place
+    and the same way everywhere (so copies between pools stay copies):
+    latent bytes lose bit 6 (|value| < 2, no NaN), the scales become 1/16,
+    the rope values lose their exponent's top bits (|value| < 2)."""
+    rows = t.view(-1, 656)
+    rows[:, :512] &= 0xBF
+    rows[:, 512:528] = torch.tensor(list(np.float32(1.0 / 16).tobytes()) * 4, dtype=torch.uint8,
+                                    device=t.device)
+    rows[:, 529:656:2] &= 0xBF
+
+
+def test_consumer_reads_in_place_what_the_gather_delivers():
+    """A decode step consumed two ways gives bit-identical attention: the
+    resolver in place (hs_resolve_in_place, only the misses staged) then the
+    kernel reading the pool by row id, or the resolver with its gathered
+    output then the kernel reading the gathered rows; and both match the
+    oracle on the step's rows."""
+    import serving_memory_tier_amd as hs
+    import hs_gen
+    from serving_memory_tier_amd.runner import DeviceRun
+    wl = hs_gen.mixed_decode(steps=4)
+    T, K, H = wl.R, wl.K, 32
+    runs = []
+    for mode in ("in_place", "gathered"):
+        dev = DeviceRun(wl)
+        dev.upload_steps()
+        _sanitize(dev.pool)
+        _sanitize(dev.host)
+        runs.append(dev)
+    rs = np.random.default_rng(3)
+    q = torch.from_numpy(make_q(rs, T, H).view(np.int16)).cuda()
+    iota = torch.arange(T * K, dtype=torch.int32, device="cuda").view(T, K)
+    wsb = hs.hs_sparse_mla_workspace_bytes(T, H, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    lay_pool = hs.layout_of(64, 656, 1, 64, wl.pool_rows, 0)
+    lay_out = hs.layout_of(1, 656, 1, 64, T * K, 0)
+    scale = 1.0 / math.sqrt(576)
+    try:
+        for i, step in enumerate(wl.steps):
+            res = []
+            for mode, dev in zip(("in_place", "gathered"), runs):
+                print(f"[attend] consumer {mode} step {i}", flush=True)
+                dev.pre(i)
+                out = torch.empty((T, H, 512), dtype=torch.float32, device="cuda")
+                lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+                n = step.offload.shape[0]
+                if mode == "in_place":
+                    hs.hs_resolve_in_place(dev.layout, dev.batch, dev.topk[i], 1, K, step.stamp,
+                                           dev.rows, dev.out, dev.stats,
+                                           dev.pairs[i] if n else None, n)
+                    hs.hs_sparse_mla_decode(lay_pool, dev.pool, dev.rows, T, K, q, H, scale, out,
+                                            lse, ws, wsb)
+                else:
+                    dev.plan_step(i)
+                    hs.hs_sparse_mla_decode(lay_out, dev.out, iota, T, K, q, H, scale, out, lse,
+                                            ws, wsb)
+                torch.cuda.synchronize()
+                res.append((out.cpu().numpy(), lse.cpu().numpy(), dev.rows.cpu().numpy()))
+            assert np.array_equal(res[0][2], res[1][2]), f"row ids, step {i}"
+            assert np.array_equal(res[0][0].view(np.int32), res[1][0].view(np.int32)), i
+            assert np.array_equal(res[0][1].view(np.int32), res[1][1].view(np.int32)), i
+            # the oracle on three requests' rows, from the pool as it stands
+            pool = runs[0].pool[0].cpu().numpy()
+            ids = res[0][2].reshape(T, K)
+            qn = q.cpu().numpy().view(np.uint16)
+            for r in (0, 7, 31):
+                ref_o, ref_l = sm.sparse_mla_decode(pool, ids[r:r + 1], qn[r:r + 1], scale)
+                sel = ids[r][(ids[r] >= 0) & (ids[r] < pool.shape[0])]
+                vmax = np.abs(sm.decode_rows(pool[sel])[1]).max()
+                assert np.abs(res[0][0][r] - ref_o[0]).max() <= 2.0 ** -8 * vmax + 1e-6
+                assert np.abs(res[0][1][r] - ref_l[0]).max() <= 1e-4
+    finally:
+        for dev in runs:
+            dev.close()

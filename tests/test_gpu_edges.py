@@ -100,7 +100,8 @@ def _compare(case, inst_or_arrays, topk, stamp, pairs=None, page=None, mode="cal
     tok, stp, pool, host = case.state()
     assert np.array_equal(g_rows, o_rows)
     assert np.array_equal(g_stats, o_stats)
-    assert np.array_equal(g_out, o_out)
+    if mode != "in_place":           # there the output is only staging
+        assert np.array_equal(g_out, o_out)
     assert np.array_equal(tok, a["tok"])
     assert np.array_equal(stp, a["stp"])
     assert np.array_equal(pool, a["pool"])

@@ -125,9 +125,9 @@ def test_mixed_decode_full():
     assert totals[1] > 0 and totals[2] > 0 and totals[0] > 0
 
 
-@pytest.mark.parametrize("mode", ["serial", "staged"])
+@pytest.mark.parametrize("mode", ["serial", "staged", "in_place"])
 def test_mixed_decode_stages(mode):
-    totals = run_parity(hs_gen.mixed_decode(steps=6), mode=mode)
+    totals = run_parity(hs_gen.mixed_decode(steps=6), mode=mode, gather=mode != "in_place")
     assert totals[2] > 0
 
 
@@ -168,10 +168,10 @@ def test_multi_layer_full_sampled():
     run_parity(wl, requests=[0, 17, 63], fused_plan=False)
 
 
-@pytest.mark.parametrize("mode", ["serial", "staged"])
+@pytest.mark.parametrize("mode", ["serial", "staged", "in_place"])
 def test_mixed_state_stages_sampled(mode):
     wl = hs_gen.mixed_state(steps=4)
-    run_parity(wl, requests=[0, 1, 64, 127], mode=mode)
+    run_parity(wl, requests=[0, 1, 64, 127], mode=mode, gather=mode != "in_place")
 
 
 @pytest.mark.parametrize("gather", [True, False])
