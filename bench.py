@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 METRIC = "resolved top-K rows/s + achieved HBM & host-link GB/s vs peak, 32 req x K=2048"
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA
 HOST_LINK_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction
 ROW = 656
 PAGE = 64
@@ -55,6 +56,9 @@ def parse():
                     help="launch the timed steps one by one instead of replaying a captured graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one plain 256 MiB device copy (counter calibration runs)")
+    ap.add_argument("--consumer", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time a decode step consumed by sparse MLA attention, gathered "
+                         "and in place")
     ap.add_argument("--event-steps", type=int, default=64,
                     help="steps launched one by one with HIP events around every kernel "
                          "(per-kernel durations), after the timed steps")
@@ -287,6 +291,9 @@ def main():
     # page coldness for the residency policy: hs_page_touch over the last
     # step's lists, HIP events around each launch
     page_touch = touch_cost(wl, dev, hev, sp0, last, n=20, busy=busy)
+    consumer = None
+    if args.consumer and wl.G == 1 and wl.L == 1:
+        consumer = consumer_cost(wl, hev, sp0, busy, n_steps=min(16, len(wl.steps)))
     busy.close()
     kernels["page_touch"] = page_touch
     policy = policy_cost(wl, dev)
@@ -332,6 +339,7 @@ def main():
                          f"queued behind a 0.3 ms device spin so no event waits on the host",
         "hit_replay": hit_replay,
         "policy": policy,
+        "consumer": consumer,
         "roofline": roofline,
         "cpu_baseline": None,
     }
@@ -378,6 +386,80 @@ class QueueFiller:
 
     def close(self) -> None:
         pass
+
+
+def consumer_cost(wl, hev, stream: int, busy, n_steps: int = 16, heads: int = 128):
+    """A decode step consumed by sparse MLA attention (128 heads, 576-wide
+    queries) two ways, over the workload's first n_steps steps, each on a
+    fresh copy of the batch: the resolver with its gathered output and the
+    attention over the gathered rows, or the resolver in place
+    (hs_resolve_in_place: only the misses staged) and the attention reading
+    the pool by row id.  HIP events around the resolve and the attention of
+    every step; each step queued behind a device spin."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import serving_memory_tier_amd as hs
+    from serving_memory_tier_amd.runner import DeviceRun
+    T, K = wl.R * wl.P, wl.P * wl.K
+    q = (torch.randn((T, heads, 576), device="cuda") * 0.5).to(torch.bfloat16).view(torch.int16)
+    out = torch.empty((T, heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, heads), dtype=torch.float32, device="cuda")
+    wsb = hs.hs_sparse_mla_workspace_bytes(T, heads, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    iota = torch.arange(T * K, dtype=torch.int32, device="cuda").view(T, K)
+    scale = 1.0 / math.sqrt(576)
+    res = {}
+    for mode in ("gathered", "in_place"):
+        dev = DeviceRun(wl)
+        dev.upload_steps()
+        lay_kv = hs.layout_of(1, ROW, 1, 64, wl.pool_rows if mode == "in_place" else T * K, 0)
+        ev = [(hev.new_event(), hev.new_event(), hev.new_event()) for _ in range(n_steps)]
+        for i in range(n_steps):
+            s = wl.steps[i]
+            dev.pre(i)
+            torch.cuda.synchronize()
+            busy.fill()
+            n_off = s.offload.shape[0]
+            hev.record(ev[i][0], stream)
+            if mode == "in_place":
+                hs.hs_resolve_in_place(dev.layout, dev.batch, dev.topk[i], wl.P, wl.K, s.stamp,
+                                       dev.rows, dev.out, dev.stats,
+                                       dev.pairs[i] if n_off else None, n_off, stream)
+                hev.record(ev[i][1], stream)
+                hs.hs_sparse_mla_decode(lay_kv, dev.pool, dev.rows, T, K, q, heads, scale, out,
+                                        lse, ws, wsb, stream)
+            else:
+                hs.hs_plan_replay(dev.layout, dev.batch, dev.topk[i], wl.P, wl.K, s.stamp,
+                                  dev.rows, dev.out, dev.stats, dev.pairs[i] if n_off else None,
+                                  n_off, stream)
+                hev.record(ev[i][1], stream)
+                hs.hs_sparse_mla_decode(lay_kv, dev.out, iota, T, K, q, heads, scale, out, lse,
+                                        ws, wsb, stream)
+            hev.record(ev[i][2], stream)
+        torch.cuda.synchronize()
+        r_us = [1e3 * hev.elapsed_ms(a, b) for a, b, _ in ev]
+        a_us = [1e3 * hev.elapsed_ms(b, c) for _, b, c in ev]
+        res[mode] = {"resolve_us": round(float(np.mean(r_us)), 2),
+                     "attention_us": round(float(np.mean(a_us)), 2),
+                     "step_us": round(float(np.mean(r_us) + np.mean(a_us)), 2)}
+        dev.close()
+    flops = 2.0 * T * heads * K * (576 + 512)
+    for mode in res:
+        a = res[mode]["attention_us"]
+        res[mode]["attention_tflops"] = round(flops / a / 1e6, 1)
+        res[mode]["rows_per_s"] = round(T * K / (res[mode]["step_us"] * 1e-6))
+    best = res["in_place"]["attention_tflops"]
+    res["attention_roofline"] = {"kernel": "attend", "bound": "mfma", "achieved": best,
+                                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(best / BF16_PEAK_TFLOPS, 4),
+                                 "flops_per_launch": int(flops)}
+    res["heads"] = heads
+    res["note"] = ("decode step = resolve + sparse MLA attention; 'gathered' copies every "
+                   "selected row into a gathered buffer first, 'in_place' reads the pool by row id")
+    return res
 
 
 def touch_cost(wl, dev, hev, stream: int, i: int, n: int, busy=None):

@@ -326,7 +326,7 @@ hs_status hs_resolve_in_place(const hs_layout* layout, const hs_batch* batch, co
  * Errors: HS_ERR_INVALID_ARGUMENT (null or misaligned pointers with work to
  * do, a short workspace, num_heads not a positive multiple of 16, negative
  * sizes, bad layout), HS_ERR_UNSUPPORTED (row_bytes != 656, more than 65535
- * tokens), HS_ERR_LAUNCH.
+ * tokens, top_k over 131,072), HS_ERR_LAUNCH.
  */
 hs_status hs_sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
                                const int32_t* row_ids, int32_t num_tokens, int32_t top_k,

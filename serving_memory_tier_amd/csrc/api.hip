@@ -451,6 +451,8 @@ hs_status hs_sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
   if (num_tokens < 0 || top_k < 0 || num_heads <= 0 || num_heads % 16 != 0)
     return HS_ERR_INVALID_ARGUMENT;
   if (num_tokens > 65535 || num_heads > 16 * 65535) return HS_ERR_UNSUPPORTED;
+  if ((int64_t)top_k > (int64_t)hs::kAttendMaxSplits * hs::kAttendMaxSplitKeys)
+    return HS_ERR_UNSUPPORTED;
   if (num_tokens == 0) return HS_OK;
   if (!q || !out || !lse || (top_k > 0 && (!kv_layer || !row_ids))) return HS_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(out) || (kv_layer && !aligned16(kv_layer)))

@@ -35,7 +35,6 @@ namespace hs {
 namespace {
 
 constexpr int kT = kAttendThreads;          // 4 waves
-constexpr int kHeadsPerWave = 16;
 constexpr int kBlockKeys = 32;
 constexpr int kLatent = 512;
 constexpr int kRope = 64;
@@ -43,8 +42,11 @@ constexpr int kDim = kLatent + kRope;       // 576
 constexpr int kRowBytes = 656;
 constexpr int kPieces = kRowBytes / 16;     // 41
 constexpr int kKdStride = kDim + 8;         // bf16 per key row in LDS (padded)
-constexpr int kVtStride = kBlockKeys + 8;   // bf16 per dimension row in LDS (padded)
+constexpr int kVtStride = kBlockKeys + 4;   // bf16 per dimension row in LDS (padded: the
+                                            // transposing writes and the value reads spread
+                                            // over the banks, 8-byte aligned)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kStaleMax = 8.f;            // log2 of the largest unnormalised probability
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -56,174 +58,300 @@ struct AttendLds {
   uint16_t vt[kLatent * kVtStride];         // latent values, dimension-major
   float scale[kBlockKeys][4];
   int32_t valid[kBlockKeys];
+  int32_t ids[kAttendMaxSplitKeys];         // the split's row ids, -1 where nothing is selected
 };
 
-__device__ __forceinline__ uint32_t bf16_bits(float f) { return __float_as_uint(f) >> 16; }
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 // Two FP8 E4M3 bytes (the low or high half of w) to two bf16 in one word:
-// exact, every E4M3 value is a bf16 value.
+// exact, every E4M3 value is a bf16 value (the conversion's scale is 1).
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return bf16_bits(f[0]) | (bf16_bits(f[1]) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// Loads the block of rows [key0, key0 + 32) of token t into LDS.
-__device__ void load_block(const AttendParams& p, AttendLds& s, const int32_t* ids, int32_t key0,
-                           int32_t key_end) {
+// A block's rows are moved in pairs (rows 2 jp and 2 jp + 1, the same
+// 16-byte piece pc of both), 16 pairs x 41 pieces over the workgroup: the
+// loads are issued for the next block before the current one is computed.
+constexpr int kPairPieces = (kBlockKeys / 2) * kPieces;          // 656
+constexpr int kFetchRounds = (kPairPieces + kT - 1) / kT;        // 3
+
+struct BlockRegs {
+  u32x4 v[kFetchRounds][2];
+  int32_t id[kFetchRounds][2];
+};
+
+// Global loads of the rows of keys [k0, k0 + 32) of the split (row ids from
+// LDS) into registers.  Loads are unconditional where the pool has rows (an
+// unselected key reads row 0 and is masked when stored), so nothing waits
+// between issuing them.
+__device__ __forceinline__ void fetch_block(const AttendParams& p, const AttendLds& s,
+                                            int32_t k0, BlockRegs& b) {
   const int tid = threadIdx.x;
-  if (tid < kBlockKeys) {
-    const int32_t k = key0 + tid;
-    const int32_t id = k < key_end ? ids[k] : -1;
-    s.valid[tid] = (id >= 0 && (int64_t)id < p.pool_rows) ? id : -1;
-  }
-  __syncthreads();
-  for (int piece = tid; piece < kBlockKeys * kPieces; piece += kT) {
-    const int j = piece / kPieces;
-    const int pc = piece - j * kPieces;
-    const int32_t id = s.valid[j];
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (id >= 0) v = *reinterpret_cast<const u32x4*>(p.kv + (int64_t)id * kRowBytes + pc * 16);
-    if (pc < kLatent / 16) {
-      // 16 latent values: key-major copy and dimension-major copy
-      uint32_t w[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w[2 * i] = fp8x2_to_bf16x2<false>(v[i]);
-        w[2 * i + 1] = fp8x2_to_bf16x2<true>(v[i]);
-      }
-      uint16_t* kd = s.kd + j * kKdStride + pc * 16;
-      *reinterpret_cast<u32x4*>(kd) = u32x4{w[0], w[1], w[2], w[3]};
-      *reinterpret_cast<u32x4*>(kd + 8) = u32x4{w[4], w[5], w[6], w[7]};
+  for (int i = 0; i < kFetchRounds; ++i) {
+    const int q = tid + kT * i;
+    const int jp = q & 15, pc = q >> 4;
 #pragma unroll
-      for (int d = 0; d < 16; ++d)
-        s.vt[(pc * 16 + d) * kVtStride + j] = (uint16_t)(w[d >> 1] >> (16 * (d & 1)));
-    } else if (pc == kLatent / 16) {
-      *reinterpret_cast<u32x4*>(&s.scale[j][0]) = v;       // four float32 scales
-    } else {
-      *reinterpret_cast<u32x4*>(s.kd + j * kKdStride + kLatent + (pc - 33) * 8) = v;  // rope
+    for (int h = 0; h < 2; ++h) {
+      const int32_t id = q < kPairPieces ? s.ids[k0 + 2 * jp + h] : -1;
+      b.id[i][h] = id;
+      if (p.pool_rows > 0 && q < kPairPieces)
+        b.v[i][h] = *reinterpret_cast<const u32x4*>(p.kv + (int64_t)(id >= 0 ? id : 0) * kRowBytes +
+                                                    pc * 16);
+      else
+        b.v[i][h] = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  __syncthreads();
 }
 
+// The fetched rows into LDS: latent values converted exactly to bf16, key-major
+// and dimension-major; scales; rope values; which keys are selected.
+__device__ __forceinline__ void store_block(AttendLds& s, const BlockRegs& b) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kFetchRounds; ++i) {
+    const int q = tid + kT * i;
+    if (q >= kPairPieces) continue;
+    const int jp = q & 15, pc = q >> 4;
+    const int j0 = 2 * jp;
+    if (pc == 0) {
+      s.valid[j0] = b.id[i][0];
+      s.valid[j0 + 1] = b.id[i][1];
+    }
+    u32x4 v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v[h] = b.id[i][h] >= 0 ? b.v[i][h] : u32x4{0u, 0u, 0u, 0u};
+    if (pc < kLatent / 16) {
+      uint32_t w[2][8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[h][2 * e] = fp8x2_to_bf16x2<false>(v[h][e]);
+          w[h][2 * e + 1] = fp8x2_to_bf16x2<true>(v[h][e]);
+        }
+        uint16_t* kd = s.kd + (j0 + h) * kKdStride + pc * 16;
+        *reinterpret_cast<u32x4*>(kd) = u32x4{w[h][0], w[h][1], w[h][2], w[h][3]};
+        *reinterpret_cast<u32x4*>(kd + 8) = u32x4{w[h][4], w[h][5], w[h][6], w[h][7]};
+      }
+      // dimension-major: one word holds the dimension of both rows (the low
+      // or high halves of the two rows' words, one byte permute)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        *reinterpret_cast<uint32_t*>(s.vt + (pc * 16 + 2 * k) * kVtStride + j0) =
+            __builtin_amdgcn_perm(w[1][k], w[0][k], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(s.vt + (pc * 16 + 2 * k + 1) * kVtStride + j0) =
+            __builtin_amdgcn_perm(w[1][k], w[0][k], 0x07060302u);
+      }
+    } else if (pc == kLatent / 16) {
+      *reinterpret_cast<u32x4*>(&s.scale[j0][0]) = v[0];       // four float32 scales
+      *reinterpret_cast<u32x4*>(&s.scale[j0 + 1][0]) = v[1];
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)                                     // rope
+        *reinterpret_cast<u32x4*>(s.kd + (j0 + h) * kKdStride + kLatent + (pc - 33) * 8) = v[h];
+    }
+  }
+}
+
+// HT head tiles of 16 heads per wave: every K and V operand read from LDS
+// feeds HT MFMAs.
+template <int HT>
 __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   AttendLds& s = *reinterpret_cast<AttendLds*>(lds_raw);
   const int split = blockIdx.x, hg = blockIdx.y, t = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 15, g = l >> 4;
-  const int head = hg * (kHeadsPerWave * (kT / 64)) + w * kHeadsPerWave + col;
-  const bool head_ok = head < p.num_heads;
+  const int head0 = (hg * (kT / 64) + w) * (16 * HT) + col;   // + 16 ht
   const int32_t key_lo = split * p.keys_per_split;
   const int32_t key_end = min(p.top_k, key_lo + p.keys_per_split);
   const int32_t* ids = p.row_ids + (int64_t)t * p.top_k;
 
-  // Q^T as the B operand of the scores: this lane's head, dims 32 ks + 8 g ..
-  bf16x8 qb[kDim / 32];
-  const uint16_t* qh = p.q + ((int64_t)t * p.num_heads + (head_ok ? head : 0)) * kDim;
+  // Q^T as the B operand of the scores: this lane's heads, dims 32 ks + 8 g ..
+  bf16x8 qb[HT][kDim / 32];
 #pragma unroll
-  for (int ks = 0; ks < kDim / 32; ++ks) {
-    u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qh + ks * 32 + 8 * g) : u32x4{0, 0, 0, 0};
-    qb[ks] = __builtin_bit_cast(bf16x8, v);
+  for (int ht = 0; ht < HT; ++ht) {
+    const int head = head0 + 16 * ht;
+    const bool ok = head < p.num_heads;
+    const uint16_t* qh = p.q + ((int64_t)t * p.num_heads + (ok ? head : 0)) * kDim;
+#pragma unroll
+    for (int ks = 0; ks < kDim / 32; ++ks) {
+      u32x4 v = ok ? *reinterpret_cast<const u32x4*>(qh + ks * 32 + 8 * g) : u32x4{0, 0, 0, 0};
+      qb[ht][ks] = __builtin_bit_cast(bf16x8, v);
+    }
   }
-  f32x4 o[kLatent / 16];                     // O^T: dims 16 dt + 4 g + r, this lane's head
+  f32x4 o[HT][kLatent / 16];                 // O^T: dims 16 dt + 4 g + r, this lane's heads
 #pragma unroll
-  for (int dt = 0; dt < kLatent / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;      // log2 domain
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int dt = 0; dt < kLatent / 16; ++dt) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[HT], l_run[HT];                // log2 domain
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    m_run[ht] = -INFINITY;
+    l_run[ht] = 0.f;
+  }
   const float qk_scale = p.sm_scale * kLog2e;
 
+  // the split's row ids, padded to whole blocks, -1 where nothing is selected
+  const int32_t n_keys = key_end > key_lo ? key_end - key_lo : 0;
+  const int32_t n_pad = (n_keys + kBlockKeys - 1) / kBlockKeys * kBlockKeys;
+  for (int k = tid; k < n_pad; k += kT) {
+    int32_t id = k < n_keys ? ids[key_lo + k] : -1;
+    if (id >= 0 && (int64_t)id >= p.pool_rows) id = -1;
+    s.ids[k] = id;
+  }
+  __syncthreads();
+  BlockRegs regs;
+  if (n_keys > 0) fetch_block(p, s, 0, regs);
   for (int32_t key0 = key_lo; key0 < key_end; key0 += kBlockKeys) {
-    load_block(p, s, ids, key0, key_end);
-    // ---- scores: S^T[key][head] for the 32 keys, tiles mt of 16 keys
-    float sc[2][4];
+    store_block(s, regs);
+    __syncthreads();
+    // the next block's loads are in flight while this one is computed
+    if (key0 + kBlockKeys < key_end) fetch_block(p, s, key0 + kBlockKeys - key_lo, regs);
+    // ---- scores S^T[key][head], key tiles mt of 16: one accumulator per
+    // (key tile, head tile, latent tile or rope), filled round robin so that
+    // consecutive MFMAs never wait on each other; the key's scale of each
+    // latent tile is applied to that tile's sums in float32
+    float sc[2][HT][4];
+    {
+      f32x4 acc[2][HT][5];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x4 acc[5];
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 5; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = s.kd + (mt * 16 + col) * kKdStride + 8 * g;
+        for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-      for (int ks = 0; ks < kDim / 32; ++ks) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + ks * 32));
-        const int tile = ks < 16 ? ks / 4 : 4;
-        acc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], acc[tile], 0, 0, 0);
+          for (int tl = 0; tl < 5; ++tl) acc[mt][ht][tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        // this round's key operands (5 tiles x 2 key tiles) are read first
+        const int nt = kk < 2 ? 5 : 4;          // the rope is two steps of 32
+        bf16x8 ka[5][2];
+#pragma unroll
+        for (int tl = 0; tl < 5; ++tl)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            if (tl < nt)
+              ka[tl][mt] = __builtin_bit_cast(
+                  bf16x8, *reinterpret_cast<const u32x4*>(
+                              s.kd + (mt * 16 + col) * kKdStride + 8 * g + (tl * 4 + kk) * 32));
+#pragma unroll
+        for (int tl = 0; tl < 5; ++tl)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            if (tl < nt)
+#pragma unroll
+              for (int ht = 0; ht < HT; ++ht)
+                acc[mt][ht][tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    ka[tl][mt], qb[ht][tl * 4 + kk], acc[mt][ht][tl], 0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = mt * 16 + 4 * g + r;
-        float v = acc[4][r];
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int tl = 0; tl < 4; ++tl) v += s.scale[key][tl] * acc[tl][r];
-        sc[mt][r] = s.valid[key] >= 0 ? v * qk_scale : -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const int key = mt * 16 + 4 * g + r;
+          const bool ok = s.valid[key] >= 0;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            float v = acc[mt][ht][4][r];
+#pragma unroll
+            for (int tl = 0; tl < 4; ++tl) v += s.scale[key][tl] * acc[mt][ht][tl][r];
+            sc[mt][ht][r] = ok ? v * qk_scale : -INFINITY;
+          }
+        }
+    }
+    // ---- online softmax for each of this lane's heads over the 32 keys
+    float pr[HT][2][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      float mb = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mb = fmaxf(mb, sc[mt][ht][r]);
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      // the running max moves only when a score exceeds it by more than 2^8
+      // (probabilities stay below 256 meanwhile), so the output is rarely
+      // rescaled; the result does not depend on the stale max
+      const bool grow = mb > m_run[ht] + kStaleMax;
+      const float m_new = grow ? mb : m_run[ht];
+      const float alpha = grow ? exp2f(m_run[ht] - m_new) : 1.f;
+      float ls = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[ht][mt][r] = m_new == -INFINITY ? 0.f : exp2f(sc[mt][ht][r] - m_new);  // < 256
+          ls += pr[ht][mt][r];
+        }
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      l_run[ht] = l_run[ht] * alpha + ls;
+      m_run[ht] = m_new;
+      if (__any(grow)) {
+#pragma unroll
+        for (int dt = 0; dt < kLatent / 16; ++dt) o[ht][dt] *= alpha;
       }
     }
-    // ---- online softmax for this lane's head over the block's 32 keys
-    float mb = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mb = fmaxf(mb, sc[mt][r]);
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-    float pr[2][4], ls = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pr[mt][r] = m_new == -INFINITY ? 0.f : exp2f(sc[mt][r] - m_new);
-        ls += pr[mt][r];
-      }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < kLatent / 16; ++dt) o[dt] *= alpha;
     // ---- O^T += V^T P'^T, one latent tile (8 dimension tiles) at a time;
     // this lane's 8 keys are 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl) {
-      bf16x8 b;   // P' rounded to nearest bf16
+      bf16x8 b[HT];   // P' rounded to nearest bf16
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          b[4 * h + r] = (__bf16)(pr[h][r] * s.scale[h * 16 + 4 * g + r][tl]);
+        for (int r = 0; r < 4; ++r) {
+          const float f = s.scale[mt * 16 + 4 * g + r][tl];
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) b[ht][4 * mt + r] = (__bf16)(pr[ht][mt][r] * f);
+        }
+      // the tile's 8 value operands are read before its 8 products
+      bf16x8 va[8];
 #pragma unroll
       for (int d8 = 0; d8 < 8; ++d8) {
-        const int dt = tl * 8 + d8;
-        const uint16_t* vrow = s.vt + (dt * 16 + col) * kVtStride;
+        const uint16_t* vrow = s.vt + ((tl * 8 + d8) * 16 + col) * kVtStride;
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 4 * g);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 + 4 * g);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, o[dt], 0, 0, 0);
+        va[d8] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
+#pragma unroll
+      for (int d8 = 0; d8 < 8; ++d8)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          o[ht][tl * 8 + d8] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d8], b[ht], o[ht][tl * 8 + d8], 0, 0, 0);
     }
-    __syncthreads();   // every wave is done with the block before the next load
+    __syncthreads();   // every wave is done with the block before the next store
   }
 
-  if (!head_ok) return;
-  const int64_t th = (int64_t)t * p.num_heads + head;
-  if (p.splits == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* out = p.out + th * kLatent;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int head = head0 + 16 * ht;
+    if (head >= p.num_heads) continue;
+    const int64_t th = (int64_t)t * p.num_heads + head;
+    if (p.splits == 1) {
+      const float inv = l_run[ht] > 0.f ? 1.f / l_run[ht] : 0.f;
+      float* out = p.out + th * kLatent;
+#pragma unroll
+      for (int dt = 0; dt < kLatent / 16; ++dt)
+        *reinterpret_cast<f32x4*>(out + dt * 16 + 4 * g) = o[ht][dt] * inv;
+      if (g == 0)
+        p.lse[th] = l_run[ht] > 0.f ? (m_run[ht] + log2f(l_run[ht])) / kLog2e : -INFINITY;
+      continue;
+    }
+    const int64_t ps = ((int64_t)t * p.splits + split) * p.num_heads + head;
+    float* po = p.part_o + ps * kLatent;
 #pragma unroll
     for (int dt = 0; dt < kLatent / 16; ++dt)
-      *reinterpret_cast<f32x4*>(out + dt * 16 + 4 * g) = o[dt] * inv;
-    if (g == 0) p.lse[th] = l_run > 0.f ? (m_run + log2f(l_run)) / kLog2e : -INFINITY;
-    return;
-  }
-  const int64_t ps = ((int64_t)t * p.splits + split) * p.num_heads + head;
-  float* po = p.part_o + ps * kLatent;
-#pragma unroll
-  for (int dt = 0; dt < kLatent / 16; ++dt)
-    *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * g) = o[dt];
-  if (g == 0) {
-    p.part_ml[2 * ps] = m_run;
-    p.part_ml[2 * ps + 1] = l_run;
+      *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * g) = o[ht][dt];
+    if (g == 0) {
+      p.part_ml[2 * ps] = m_run[ht];
+      p.part_ml[2 * ps + 1] = l_run[ht];
+    }
   }
 }
 
@@ -259,9 +387,11 @@ void plan_attend(AttendParams& p, int64_t target_groups) {
   const int64_t base = (int64_t)p.num_tokens * hg;
   const int32_t blocks = (p.top_k + kBlockKeys - 1) / kBlockKeys;
   int64_t s = base > 0 ? (target_groups + base - 1) / base : 1;
-  if (s < 1) s = 1;
+  const int64_t s_min = (blocks + kAttendMaxSplitKeys / kBlockKeys - 1) /
+                        (kAttendMaxSplitKeys / kBlockKeys);   // the split's ids fit in LDS
+  if (s < s_min) s = s_min;
   if (s > blocks) s = blocks;
-  if (s > kAttendMaxSplits) s = kAttendMaxSplits;
+  if (s > kAttendMaxSplits) s = kAttendMaxSplits;   // top_k is validated against this bound
   if (s < 1) s = 1;
   const int32_t per = (int32_t)(((blocks + s - 1) / s) * kBlockKeys);
   p.keys_per_split = per;
@@ -271,11 +401,14 @@ void plan_attend(AttendParams& p, int64_t target_groups) {
 
 hipError_t launch_attend(const AttendParams& p, hipStream_t stream) {
   if (p.num_tokens == 0 || p.num_heads == 0) return hipSuccess;
+  constexpr int HT = kAttendHeadsPerGroup / (16 * (kT / 64));
+  static_assert(HT * 16 * (kT / 64) == kAttendHeadsPerGroup, "heads per workgroup");
+  auto fn = attend_kernel<HT>;
   static std::atomic<uint64_t> raised{0};
-  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(attend_kernel), raised);
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(fn), raised);
   if (e != hipSuccess) return e;
   const uint32_t hg = (uint32_t)((p.num_heads + kAttendHeadsPerGroup - 1) / kAttendHeadsPerGroup);
-  e = launch_kernel(attend_kernel, dim3((uint32_t)p.splits, hg, (uint32_t)p.num_tokens), dim3(kT),
+  e = launch_kernel(fn, dim3((uint32_t)p.splits, hg, (uint32_t)p.num_tokens), dim3(kT),
                     sizeof(AttendLds), stream, p);
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_kernel(attend_combine_kernel, dim3((uint32_t)p.num_heads, (uint32_t)p.num_tokens),

@@ -214,5 +214,6 @@ def test_sparse_mla_rejects(lib):
     assert f(lay, P, P, 1, 64, P + 4, 16, P, P, P, need) == 1    # misaligned queries
     assert f(lay, P, P, 32, 2048, P, 128, P, P, None, need) == 1  # workspace needed
     assert f(lay, P, P, 32, 2048, P, 128, P, P, P, need - 16) == 1
+    assert f(lay, P, P, 1, 64 * 2048 + 1, P, 16, P, P, P, 1 << 40) == 2   # top_k over the bound
     assert f(lay, P, P, 0, 64, None, 16, None, None, None, 0) == 0   # nothing to do
     assert lib.hs_sparse_mla_workspace_bytes(0, 16, 64) == 0
