@@ -9,18 +9,22 @@
 // key is its scaled latent values and its rope values (576), its value the
 // scaled latent values (512).
 //
-// Work split: one workgroup of 4 waves per (query token, 64 heads, key
-// split).  Per block of 32 selected rows the workgroup loads the rows by id,
-// converts the latent bytes exactly to bfloat16 (FP8 E4M3 fits bfloat16)
-// into LDS twice -- key-major for the scores, dimension-major for the
-// values -- and each wave takes 16 heads:
-//   S^T (32 keys x 16 heads) = K Q^T with 16x16x32 bf16 MFMAs, one
+// Work split: one workgroup of 8 waves per (query token, 64 heads, key
+// split).  Per block of 32 selected rows the workgroup loads the rows by id
+// (one block ahead, into registers), converts the latent bytes exactly to
+// bfloat16 (FP8 E4M3 fits bfloat16) into LDS twice -- key-major for the
+// scores, dimension-major for the values -- and wave w takes 16 heads (w & 3)
+// and one half (w >> 2), which picks its 16 keys for the scores and its 256
+// value dimensions:
+//   S^T (16 keys x 16 heads) = K Q^T with 16x16x32 bf16 MFMAs, one
 //     accumulator per 128-value latent tile and one for the rope, so the
-//     per-row scales are applied in float32 after the products;
-//   online softmax per head (each lane owns one head column);
-//   O^T (512 dims x 16 heads) += V^T P'^T, where P' = p * scale of the
-//     latent tile: the probabilities are the B operand straight from the
-//     score accumulators' registers, no LDS round trip.
+//     per-row scales are applied in float32 after the products; the two
+//     halves swap their scores through LDS;
+//   online softmax per head over the 32 keys (each lane owns one head column);
+//   O^T (256 dims x 16 heads) += V^T P'^T, where P' = p * scale of the latent
+//     tile: the probabilities are the B operand straight from registers.
+// Half the value dimensions per wave keep a wave under 256 registers, so two
+// waves share each SIMD.
 // Key splits write unnormalised partial outputs with their running max and
 // sum to the caller's workspace; a combine kernel merges them.
 
@@ -34,7 +38,7 @@
 namespace hs {
 namespace {
 
-constexpr int kT = kAttendThreads;          // 4 waves
+constexpr int kT = kAttendThreads;          // 8 waves
 constexpr int kBlockKeys = 32;
 constexpr int kLatent = 512;
 constexpr int kRope = 64;
@@ -59,6 +63,7 @@ struct AttendLds {
   float scale[kBlockKeys][4];
   int32_t valid[kBlockKeys];
   int32_t ids[kAttendMaxSplitKeys];         // the split's row ids, -1 where nothing is selected
+  float xs[4][kBlockKeys][16];              // scores per (head tile, key, head) for the exchange
 };
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -74,7 +79,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 // 16-byte piece pc of both), 16 pairs x 41 pieces over the workgroup: the
 // loads are issued for the next block before the current one is computed.
 constexpr int kPairPieces = (kBlockKeys / 2) * kPieces;          // 656
-constexpr int kFetchRounds = (kPairPieces + kT - 1) / kT;        // 3
+constexpr int kFetchRounds = (kPairPieces + kT - 1) / kT;        // 2
 
 struct BlockRegs {
   u32x4 v[kFetchRounds][2];
@@ -155,47 +160,38 @@ __device__ __forceinline__ void store_block(AttendLds& s, const BlockRegs& b) {
   }
 }
 
-// HT head tiles of 16 heads per wave: every K and V operand read from LDS
-// feeds HT MFMAs.
-template <int HT>
+
+// 8 waves: wave w takes head tile ht = w & 3 (16 heads) and half = w >> 2,
+// which picks both its key tile for the scores (keys 16 half ..) and its
+// value dimensions (256 half ..); the two halves swap scores through LDS.
 __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   AttendLds& s = *reinterpret_cast<AttendLds*>(lds_raw);
   const int split = blockIdx.x, hg = blockIdx.y, t = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 15, g = l >> 4;
-  const int head0 = (hg * (kT / 64) + w) * (16 * HT) + col;   // + 16 ht
+  const int ht = w & 3, half = w >> 2;
+  const int head = hg * 64 + ht * 16 + col;
+  const bool head_ok = head < p.num_heads;
   const int32_t key_lo = split * p.keys_per_split;
   const int32_t key_end = min(p.top_k, key_lo + p.keys_per_split);
   const int32_t* ids = p.row_ids + (int64_t)t * p.top_k;
 
-  // Q^T as the B operand of the scores: this lane's heads, dims 32 ks + 8 g ..
-  bf16x8 qb[HT][kDim / 32];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int head = head0 + 16 * ht;
-    const bool ok = head < p.num_heads;
-    const uint16_t* qh = p.q + ((int64_t)t * p.num_heads + (ok ? head : 0)) * kDim;
+  bf16x8 qb[kDim / 32];
+  {
+    const uint16_t* qh = p.q + ((int64_t)t * p.num_heads + (head_ok ? head : 0)) * kDim;
 #pragma unroll
     for (int ks = 0; ks < kDim / 32; ++ks) {
-      u32x4 v = ok ? *reinterpret_cast<const u32x4*>(qh + ks * 32 + 8 * g) : u32x4{0, 0, 0, 0};
-      qb[ht][ks] = __builtin_bit_cast(bf16x8, v);
+      u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qh + ks * 32 + 8 * g) : u32x4{0, 0, 0, 0};
+      qb[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  f32x4 o[HT][kLatent / 16];                 // O^T: dims 16 dt + 4 g + r, this lane's heads
+  f32x4 o[16];                               // O^T: dims 256 half + 16 dt + 4 g + r
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-    for (int dt = 0; dt < kLatent / 16; ++dt) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[HT], l_run[HT];                // log2 domain
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    m_run[ht] = -INFINITY;
-    l_run[ht] = 0.f;
-  }
+  for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
   const float qk_scale = p.sm_scale * kLog2e;
 
-  // the split's row ids, padded to whole blocks, -1 where nothing is selected
   const int32_t n_keys = key_end > key_lo ? key_end - key_lo : 0;
   const int32_t n_pad = (n_keys + kBlockKeys - 1) / kBlockKeys * kBlockKeys;
   for (int k = tid; k < n_pad; k += kT) {
@@ -211,105 +207,79 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
     __syncthreads();
     // the next block's loads are in flight while this one is computed
     if (key0 + kBlockKeys < key_end) fetch_block(p, s, key0 + kBlockKeys - key_lo, regs);
-    // ---- scores S^T[key][head], key tiles mt of 16: one accumulator per
-    // (key tile, head tile, latent tile or rope), filled round robin so that
-    // consecutive MFMAs never wait on each other; the key's scale of each
-    // latent tile is applied to that tile's sums in float32
-    float sc[2][HT][4];
+    // ---- scores of this wave's key tile: S^T[key 16 half + ..][head]
     {
-      f32x4 acc[2][HT][5];
+      f32x4 acc[5];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-          for (int tl = 0; tl < 5; ++tl) acc[mt][ht][tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tl = 0; tl < 5; ++tl) acc[tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow = s.kd + (half * 16 + col) * kKdStride + 8 * g;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        // this round's key operands (5 tiles x 2 key tiles) are read first
-        const int nt = kk < 2 ? 5 : 4;          // the rope is two steps of 32
-        bf16x8 ka[5][2];
+        const int nt = kk < 2 ? 5 : 4;
+        bf16x8 ka[5];
 #pragma unroll
         for (int tl = 0; tl < 5; ++tl)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            if (tl < nt)
-              ka[tl][mt] = __builtin_bit_cast(
-                  bf16x8, *reinterpret_cast<const u32x4*>(
-                              s.kd + (mt * 16 + col) * kKdStride + 8 * g + (tl * 4 + kk) * 32));
+          if (tl < nt)
+            ka[tl] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(krow + (tl * 4 + kk) * 32));
 #pragma unroll
         for (int tl = 0; tl < 5; ++tl)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            if (tl < nt)
-#pragma unroll
-              for (int ht = 0; ht < HT; ++ht)
-                acc[mt][ht][tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    ka[tl][mt], qb[ht][tl * 4 + kk], acc[mt][ht][tl], 0, 0, 0);
+          if (tl < nt)
+            acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tl], qb[tl * 4 + kk], acc[tl],
+                                                              0, 0, 0);
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int r = 0; r < 4; ++r) {
+        const int key = half * 16 + 4 * g + r;
+        float v = acc[4][r];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = mt * 16 + 4 * g + r;
-          const bool ok = s.valid[key] >= 0;
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            float v = acc[mt][ht][4][r];
-#pragma unroll
-            for (int tl = 0; tl < 4; ++tl) v += s.scale[key][tl] * acc[mt][ht][tl][r];
-            sc[mt][ht][r] = ok ? v * qk_scale : -INFINITY;
-          }
-        }
-    }
-    // ---- online softmax for each of this lane's heads over the 32 keys
-    float pr[HT][2][4];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      float mb = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mb = fmaxf(mb, sc[mt][ht][r]);
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
-      // the running max moves only when a score exceeds it by more than 2^8
-      // (probabilities stay below 256 meanwhile), so the output is rarely
-      // rescaled; the result does not depend on the stale max
-      const bool grow = mb > m_run[ht] + kStaleMax;
-      const float m_new = grow ? mb : m_run[ht];
-      const float alpha = grow ? exp2f(m_run[ht] - m_new) : 1.f;
-      float ls = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[ht][mt][r] = m_new == -INFINITY ? 0.f : exp2f(sc[mt][ht][r] - m_new);  // < 256
-          ls += pr[ht][mt][r];
-        }
-      ls += __shfl_xor(ls, 16);
-      ls += __shfl_xor(ls, 32);
-      l_run[ht] = l_run[ht] * alpha + ls;
-      m_run[ht] = m_new;
-      if (__any(grow)) {
-#pragma unroll
-        for (int dt = 0; dt < kLatent / 16; ++dt) o[ht][dt] *= alpha;
+        for (int tl = 0; tl < 4; ++tl) v += s.scale[key][tl] * acc[tl][r];
+        s.xs[ht][key][col] = s.valid[key] >= 0 ? v * qk_scale : -INFINITY;
       }
     }
-    // ---- O^T += V^T P'^T, one latent tile (8 dimension tiles) at a time;
-    // this lane's 8 keys are 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3
+    __syncthreads();   // both key tiles' scores are in LDS
+    // ---- online softmax over the block's 32 keys (both halves alike)
+    float sc[2][4];
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl) {
-      bf16x8 b[HT];   // P' rounded to nearest bf16
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[mt][r] = s.xs[ht][mt * 16 + 4 * g + r][col];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mb = fmaxf(mb, sc[mt][r]);
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const bool grow = mb > m_run + kStaleMax;
+    const float m_new = grow ? mb : m_run;
+    const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
+    float pr[2][4], ls = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[mt][r] = m_new == -INFINITY ? 0.f : exp2f(sc[mt][r] - m_new);
+        ls += pr[mt][r];
+      }
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+    if (__any(grow)) {
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) o[dt] *= alpha;
+    }
+    // ---- O^T += V^T P'^T for this wave's two latent tiles
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int tl = half * 2 + t2;
+      bf16x8 b;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float f = s.scale[mt * 16 + 4 * g + r][tl];
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) b[ht][4 * mt + r] = (__bf16)(pr[ht][mt][r] * f);
-        }
-      // the tile's 8 value operands are read before its 8 products
+        for (int r = 0; r < 4; ++r)
+          b[4 * mt + r] = (__bf16)(pr[mt][r] * s.scale[mt * 16 + 4 * g + r][tl]);
       bf16x8 va[8];
 #pragma unroll
       for (int d8 = 0; d8 < 8; ++d8) {
@@ -320,38 +290,32 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
       }
 #pragma unroll
       for (int d8 = 0; d8 < 8; ++d8)
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-          o[ht][tl * 8 + d8] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d8], b[ht], o[ht][tl * 8 + d8], 0, 0, 0);
+        o[t2 * 8 + d8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d8], b, o[t2 * 8 + d8], 0, 0, 0);
     }
     __syncthreads();   // every wave is done with the block before the next store
   }
 
+  if (!head_ok) return;
+  const int64_t th = (int64_t)t * p.num_heads + head;
+  const int d0 = half * 256;
+  if (p.splits == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* out = p.out + th * kLatent + d0;
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int head = head0 + 16 * ht;
-    if (head >= p.num_heads) continue;
-    const int64_t th = (int64_t)t * p.num_heads + head;
-    if (p.splits == 1) {
-      const float inv = l_run[ht] > 0.f ? 1.f / l_run[ht] : 0.f;
-      float* out = p.out + th * kLatent;
+    for (int dt = 0; dt < 16; ++dt)
+      *reinterpret_cast<f32x4*>(out + dt * 16 + 4 * g) = o[dt] * inv;
+    if (g == 0 && half == 0)
+      p.lse[th] = l_run > 0.f ? (m_run + log2f(l_run)) / kLog2e : -INFINITY;
+    return;
+  }
+  const int64_t ps = ((int64_t)t * p.splits + split) * p.num_heads + head;
+  float* po = p.part_o + ps * kLatent + d0;
 #pragma unroll
-      for (int dt = 0; dt < kLatent / 16; ++dt)
-        *reinterpret_cast<f32x4*>(out + dt * 16 + 4 * g) = o[ht][dt] * inv;
-      if (g == 0)
-        p.lse[th] = l_run[ht] > 0.f ? (m_run[ht] + log2f(l_run[ht])) / kLog2e : -INFINITY;
-      continue;
-    }
-    const int64_t ps = ((int64_t)t * p.splits + split) * p.num_heads + head;
-    float* po = p.part_o + ps * kLatent;
-#pragma unroll
-    for (int dt = 0; dt < kLatent / 16; ++dt)
-      *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * g) = o[ht][dt];
-    if (g == 0) {
-      p.part_ml[2 * ps] = m_run[ht];
-      p.part_ml[2 * ps + 1] = l_run[ht];
-    }
+  for (int dt = 0; dt < 16; ++dt)
+    *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * g) = o[dt];
+  if (g == 0 && half == 0) {
+    p.part_ml[2 * ps] = m_run;
+    p.part_ml[2 * ps + 1] = l_run;
   }
 }
 
@@ -401,9 +365,8 @@ void plan_attend(AttendParams& p, int64_t target_groups) {
 
 hipError_t launch_attend(const AttendParams& p, hipStream_t stream) {
   if (p.num_tokens == 0 || p.num_heads == 0) return hipSuccess;
-  constexpr int HT = kAttendHeadsPerGroup / (16 * (kT / 64));
-  static_assert(HT * 16 * (kT / 64) == kAttendHeadsPerGroup, "heads per workgroup");
-  auto fn = attend_kernel<HT>;
+  static_assert(kAttendHeadsPerGroup == 64, "64 heads per workgroup");
+  auto fn = attend_kernel;
   static std::atomic<uint64_t> raised{0};
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(fn), raised);
   if (e != hipSuccess) return e;

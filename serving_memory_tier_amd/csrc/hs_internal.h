@@ -228,14 +228,11 @@ hipError_t launch_page_touch(const TouchParams& p, hipStream_t stream);
 
 // Sparse MLA decode over rows read in place by row id (attend.hip): 656-byte
 // FP8 MLA rows, 576-wide bf16 queries, 512-wide float32 outputs.
-constexpr int kAttendThreads = 256;
-#ifndef HS_ATTEND_HEADS
-#define HS_ATTEND_HEADS 64
-#endif
+constexpr int kAttendThreads = 512;
 #ifndef HS_ATTEND_TARGET
 #define HS_ATTEND_TARGET 256
 #endif
-constexpr int kAttendHeadsPerGroup = HS_ATTEND_HEADS;   // heads per workgroup (a multiple of 64)
+constexpr int kAttendHeadsPerGroup = 64;  // heads per workgroup
 constexpr int kAttendMaxSplits = 64;       // key splits per (token, head group), at most
 constexpr int kAttendMaxSplitKeys = 2048;  // keys per split, at most (their row ids sit in LDS)
 constexpr int64_t kAttendTargetGroups = HS_ATTEND_TARGET;  // workgroups per launch to aim for
