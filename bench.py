@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--consumer", action=argparse.BooleanOptionalAction, default=True,
                     help="also time a decode step consumed by sparse MLA attention, gathered "
                          "and in place")
+    ap.add_argument("--miss-path", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the all-miss first step of the no-residency workload "
+                         "(every row over the host link)")
     ap.add_argument("--event-steps", type=int, default=64,
                     help="steps launched one by one with HIP events around every kernel "
                          "(per-kernel durations), after the timed steps")
@@ -294,6 +297,7 @@ def main():
     consumer = None
     if args.consumer and wl.G == 1 and wl.L == 1:
         consumer = consumer_cost(wl, hev, sp0, busy, n_steps=min(16, len(wl.steps)))
+    miss_path = miss_path_cost(hev, sp0, busy) if args.miss_path else None
     busy.close()
     kernels["page_touch"] = page_touch
     policy = policy_cost(wl, dev)
@@ -340,6 +344,7 @@ def main():
         "hit_replay": hit_replay,
         "policy": policy,
         "consumer": consumer,
+        "miss_path": miss_path,
         "roofline": roofline,
         "cpu_baseline": None,
     }
@@ -460,6 +465,47 @@ def consumer_cost(wl, hev, stream: int, busy, n_steps: int = 16, heads: int = 12
     res["note"] = ("decode step = resolve + sparse MLA attention; 'gathered' copies every "
                    "selected row into a gathered buffer first, 'in_place' reads the pool by row id")
     return res
+
+
+def miss_path_cost(hev, stream: int, busy, reps: int = 8):
+    """The miss path alone: the first step of the no-residency workload (8
+    requests sharing a host-only 1,000,000-token prefix, top-K 2048, an empty
+    4096-row hot buffer), where every one of the 16,384 entries is a distinct
+    miss and every row crosses the host link.  Steps 0..reps-1 of the workload
+    are each resolved from an empty hot buffer (state cleared off the clock),
+    so every call is all misses; HIP events around the fused resolve-and-fill
+    launch and the commit, each call queued behind a device spin."""
+    import numpy as np
+    import torch
+
+    import hs_gen
+    from serving_memory_tier_amd.runner import DeviceRun
+    wl = hs_gen.no_residency(steps=reps)
+    dev = DeviceRun(wl)
+    dev.upload_steps()
+    dev.stage_steps()
+    ev = [[hev.new_event() for _ in range(4)] for _ in range(reps)]
+    stats = torch.zeros((reps, wl.R, wl.NG, 8), dtype=torch.int32, device="cuda")
+    for j in range(reps):
+        dev.tok.fill_(-1)
+        dev.stp.zero_()
+        busy.fill()
+        dev.launch_step_timed(j, hev, stream, ev[j], stats=stats[j], offload=False)
+    torch.cuda.synchronize()
+    st = stats.sum(dim=(1, 2)).cpu().numpy().astype(np.int64)
+    fused = np.array([1e3 * hev.elapsed_ms(e[0], e[1]) for e in ev])
+    commit = np.array([1e3 * hev.elapsed_ms(e[1], e[2]) for e in ev])
+    host_bytes = float(np.mean((st[:, 2] + st[:, 3]) * ROW))
+    dev.close()
+    f_us, c_us = float(np.mean(fused)), float(np.mean(commit))
+    gbps = host_bytes / f_us / 1e3
+    return {"workload": "no_residency first step (8 x 2048, empty 4096-row hot buffer)",
+            "calls": reps, "misses": int(np.mean(st[:, 2])),
+            "host_link_bytes": int(host_bytes), "resolve_fill_us": round(f_us, 2),
+            "resolve_fill_us_first_call": round(float(fused[0]), 2),
+            "commit_us": round(c_us, 2), "step_us": round(f_us + c_us, 2),
+            "host_link_gbps": round(gbps, 2), "host_link_frac": round(gbps / HOST_LINK_PEAK_GBPS, 4),
+            "step_host_link_gbps": round(host_bytes / (f_us + c_us) / 1e3, 2)}
 
 
 def touch_cost(wl, dev, hev, stream: int, i: int, n: int, busy=None):
