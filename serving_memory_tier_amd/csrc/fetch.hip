@@ -21,11 +21,18 @@ __global__ void __launch_bounds__(kFillThreads) fetch_kernel(FetchParams p) {
 
 }  // namespace
 
-// Entries per gather workgroup: about kFetchGatherTarget workgroups in all,
-// kFetchGatherMin..kFetchGatherEntries entries each (a multiple of 4).
-int32_t gather_entries(int32_t entries, int64_t n_rl) {
-  int64_t per = (entries * n_rl + kFetchGatherTarget - 1) / kFetchGatherTarget;
+// Entries per gather workgroup: about `target` workgroups in all
+// (kFetchGatherTarget when target <= 0), kFetchGatherMin..kFetchGatherEntries
+// entries each (a multiple of 4).
+int32_t gather_entries(int32_t entries, int64_t n_rl, int64_t target) {
+  const bool strict = target > 0;  // at most `target` workgroups where possible
+  if (target <= 0) target = kFetchGatherTarget;
+  int64_t per = (entries * n_rl + target - 1) / target;
   if (per < kFetchGatherMin) per = kFetchGatherMin;
+  per = (per + 3) / 4 * 4;
+  while (strict && per < kFetchGatherEntries && per < entries &&
+         n_rl * ((entries + per - 1) / per) > target)
+    per += 4;
   if (per > kFetchGatherEntries) per = kFetchGatherEntries;
   if (per > entries) per = entries;
   return (int32_t)((per + 3) / 4 * 4);
@@ -56,10 +63,10 @@ size_t fetch_lds_bytes(int32_t entries, int32_t hot_capacity) {
   return 4 * fetch_lds_words(entries, ge, nullptr, nullptr);
 }
 
-int64_t prepare_fetch(FetchParams& p, size_t* lds_bytes) {
+int64_t prepare_fetch(FetchParams& p, size_t* lds_bytes, int64_t gather_target) {
   const int64_t n_rl = (int64_t)p.num_reqs * p.num_layers;
   p.lds_n = ((p.entries + 3) / 4) * 4;
-  p.gather_e = gather_entries(p.entries, n_rl);
+  p.gather_e = gather_entries(p.entries, n_rl, gather_target);
   *lds_bytes = 4 * fetch_lds_words(p.entries, p.gather_e, &p.miss_tab_n, &p.gather_tab_n);
   const uint32_t pieces = (uint32_t)(p.row_bytes >> 4);
   p.piece_magic = (uint32_t)(((1ull << 32) + pieces - 1) / pieces);
@@ -79,11 +86,21 @@ hipError_t launch_fetch(FetchParams p, hipStream_t stream) {
   const int64_t n_rl = (int64_t)p.num_reqs * p.num_layers;
   if (n_rl == 0 || p.entries == 0) return hipSuccess;
   size_t lds = 0;
-  const int64_t grid = prepare_fetch(p, &lds);
+  int64_t grid = prepare_fetch(p, &lds, 0);
   if (grid > INT32_MAX || lds > kMaxLdsBytes) return hipErrorInvalidValue;
   static std::atomic<uint64_t> raised{0};
   hipError_t err = allow_full_lds(reinterpret_cast<const void*>(fetch_kernel), raised);
   if (err != hipSuccess) return err;
+  // as many gather workgroups as fit beside the miss workgroups in one round
+  // of the chip, so that no gather range waits for a free CU
+  int64_t resident = 0;
+  err = resident_groups(reinterpret_cast<const void*>(fetch_kernel), kFillThreads, lds, &resident);
+  if (err != hipSuccess) return err;
+  const int64_t target = resident - p.miss_groups;
+  if (!p.misses_only && target >= kFetchGatherMinGroups) {
+    grid = prepare_fetch(p, &lds, target);
+    if (grid > INT32_MAX || lds > kMaxLdsBytes) return hipErrorInvalidValue;
+  }
   return launch_kernel(fetch_kernel, dim3((uint32_t)grid), dim3(kFillThreads), lds, stream, p);
 }
 

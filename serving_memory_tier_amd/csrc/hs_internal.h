@@ -73,6 +73,29 @@ inline hipError_t allow_full_lds(const void* fn, std::atomic<uint64_t>& done) {
   return hipSuccess;
 }
 
+// Workgroups of kernel `fn` (`threads` each, `lds` bytes of dynamic LDS) that
+// the current device runs at once: compute units x workgroups per unit.  The
+// unit count is read once per device.
+inline hipError_t resident_groups(const void* fn, int threads, size_t lds, int64_t* groups) {
+  static std::atomic<int32_t> cus[64] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  int32_t n = cus[dev & 63].load(std::memory_order_acquire);
+  if (n <= 0) {
+    int v = 0;
+    err = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    n = v;
+    cus[dev & 63].store(n, std::memory_order_release);
+  }
+  int per = 0;
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, threads, lds);
+  if (err != hipSuccess) return err;
+  *groups = (int64_t)n * per;
+  return hipSuccess;
+}
+
 // Launches a kernel and returns that launch's own status (not whatever an
 // earlier runtime call left behind for hipGetLastError).
 template <typename... Args>
@@ -151,6 +174,9 @@ constexpr int kHostUnroll = HS_HOST_UNROLL;
 constexpr int kFetchHostGroups = HS_HOST_GROUPS;
 constexpr int kFetchMaxSplits = 16;        // miss workgroups per request-layer, at most
 constexpr int kFetchGatherTarget = 256;    // gather workgroups per launch to aim for
+// (unless fewer fit beside the launch's other workgroups in one round of the
+// chip; then that many, if at least this many)
+constexpr int kFetchGatherMinGroups = 64;
 constexpr int kFetchGatherMin = 64;        // entries per gather workgroup, at least
 constexpr int kFetchGatherEntries = 512;   // entries per gather workgroup, at most
 
@@ -188,7 +214,8 @@ struct FetchParams {
 size_t fetch_lds_bytes(int32_t entries, int32_t hot_capacity);
 // Completes p's launch shape; returns the number of fill workgroups and sets
 // *lds_bytes.
-int64_t prepare_fetch(FetchParams& p, size_t* lds_bytes);
+// gather_target: gather workgroups to aim for (<= 0: kFetchGatherTarget).
+int64_t prepare_fetch(FetchParams& p, size_t* lds_bytes, int64_t gather_target);
 // The fill as a kernel of its own.
 hipError_t launch_fetch(FetchParams p, hipStream_t stream);
 

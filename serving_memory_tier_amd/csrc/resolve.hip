@@ -856,11 +856,28 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
 }
 
 template <int ES, int EC, bool FILL>
-hipError_t launch_ec(const KernelArgs& a, int grid, hipStream_t stream) {
+hipError_t launch_ec(KernelArgs a, int grid, hipStream_t stream) {
   auto fn = resolve_kernel<ES, EC, FILL>;
   static std::atomic<uint64_t> raised{0};
   hipError_t err = allow_full_lds(reinterpret_cast<const void*>(fn), raised);
   if (err != hipSuccess) return err;
+  if constexpr (FILL) {
+    // as many gather workgroups as fit beside the resolver's and the miss
+    // workgroups in one round of the chip, so that no gather range waits
+    // for a CU to come free
+    int64_t resident = 0;
+    err = resident_groups(reinterpret_cast<const void*>(fn), kThreads, a.lds_bytes, &resident);
+    if (err != hipSuccess) return err;
+    const int64_t target = resident - a.n_rl - a.fill.miss_groups;
+    if (!a.fill.misses_only && target >= kFetchGatherMinGroups) {
+      size_t flds = 0;
+      const int64_t fill_groups = prepare_fetch(a.fill, &flds, target);
+      const int64_t g = a.n_rl + fill_groups;
+      if (g > INT32_MAX || flds > kMaxLdsBytes) return hipErrorInvalidValue;
+      grid = (int)g;
+      a.lds_bytes = a.plan.total > flds ? a.plan.total : (uint32_t)flds;
+    }
+  }
   return launch_kernel(fn, dim3(grid), dim3(kThreads), a.lds_bytes, stream, a);
 }
 
@@ -928,7 +945,7 @@ hipError_t launch_resolve(const ResolveParams& p, const FetchParams* fill, hipSt
   if (!fill) return launch_rounds<false>(a, a.n_rl, ES, EC, stream);
   a.fill = *fill;
   size_t flds = 0;
-  const int64_t fill_groups = prepare_fetch(a.fill, &flds);
+  const int64_t fill_groups = prepare_fetch(a.fill, &flds, 0);
   const int64_t grid = a.n_rl + fill_groups;
   if (grid > INT32_MAX || flds > kMaxLdsBytes) return hipErrorInvalidValue;
   if (flds > a.lds_bytes) a.lds_bytes = (uint32_t)flds;
