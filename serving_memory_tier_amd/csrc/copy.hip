@@ -149,7 +149,13 @@ __global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_p
   }
 }
 
-// The commit after the early fill: one wave per 64 entries of a
+// Entries per wave of the commit: few enough that a chunk full of misses is
+// copied by a wave in a few rounds of loads (64 entries of 656-byte rows would
+// be ten rounds, and a step of misses only would run on a quarter as many
+// waves).
+constexpr int kCommitEPW = 16;
+
+// The commit after the early fill: one wave per kCommitEPW entries of a
 // request-layer.  Entries holding a first-entry code copy their output row
 // into the assigned slot and record the slot's token; every code becomes the
 // slot's row id; misses left without a slot get a zero row.  Only those rows
@@ -157,16 +163,16 @@ __global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_p
 template <int PIECES>
 __global__ void __launch_bounds__(kT) commit_kernel(MoveParams p, int32_t chunks_per_rl,
                                                     int32_t total_chunks) {
-  __shared__ int32_t work_e[kWavesPerBlock][64];    // entry; -1 - entry for a zero row
-  __shared__ int32_t work_row[kWavesPerBlock][64];  // the slot's pool row
+  __shared__ int32_t work_e[kWavesPerBlock][kCommitEPW];    // entry; -1 - entry for a zero row
+  __shared__ int32_t work_row[kWavesPerBlock][kCommitEPW];  // the slot's pool row
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int32_t c = blockIdx.x * kWavesPerBlock + wv;
   if (c >= total_chunks) return;  // the whole wave leaves together
   const int32_t rl = c / chunks_per_rl;
-  const int32_t e0 = (c - rl * chunks_per_rl) * 64;
+  const int32_t e0 = (c - rl * chunks_per_rl) * kCommitEPW;
   const int32_t N = p.rows_per_rl;
-  const int32_t ne = min(64, N - e0);
+  const int32_t ne = min(kCommitEPW, N - e0);
   const int32_t r = rl / p.num_layers;
   const int32_t l0 = (rl - r * p.num_layers) * p.group;  // first layer of the group
   const int32_t layers = p.layers > 0 ? p.layers : p.num_layers;
@@ -288,7 +294,7 @@ hipError_t launch_move(const MoveParams& p, MoveMode mode, hipStream_t stream) {
   const int64_t n_rl = (int64_t)p.num_reqs * p.num_layers;
   if (n_rl == 0 || p.rows_per_rl == 0) return hipSuccess;
   if (mode == kMoveCommit) {
-    const int32_t cpr = (p.rows_per_rl + 63) / 64;
+    const int32_t cpr = (p.rows_per_rl + kCommitEPW - 1) / kCommitEPW;
     const int64_t total = n_rl * cpr;
     const uint32_t grid = (uint32_t)((total + kWavesPerBlock - 1) / kWavesPerBlock);
     auto fn = p.row_bytes == 656 ? commit_kernel<41> : commit_kernel<0>;
