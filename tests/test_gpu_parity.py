@@ -257,3 +257,39 @@ def test_plan_rows_replayed_by_gather():
                 assert torch.equal(dev.out, planned), f"forward {forward}, step {i}"
     finally:
         dev.close()
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two batches with misses resolved by calls running at the same time on
+    two streams (each with its own state and outputs): the misses' shared
+    host reads of one call never mix with the other's, and both match the
+    oracle bit for bit, every step."""
+    from serving_memory_tier_amd.runner import DeviceRun
+
+    wls = [hs_gen.mixed_decode(seed=1001 + k, steps=4, R=8) for k in range(2)]
+    devs = [DeviceRun(wl) for wl in wls]
+    oras = [OracleRun(wl) for wl in wls]
+    streams = [torch.cuda.Stream() for _ in wls]
+    try:
+        for d in devs:
+            d.upload_steps()
+        for i in range(4):
+            _say(f"[parity] two streams, step {i}")
+            for d, o, wl in zip(devs, oras, wls):
+                d.pre(i)
+                o.pre(wl.steps[i])
+            torch.cuda.synchronize()
+            for d, s in zip(devs, streams):
+                d.resolve(i, stream=s)
+            torch.cuda.synchronize()
+            for k, (d, o, wl) in enumerate(zip(devs, oras, wls)):
+                rows, stats, out = o.resolve(wl.steps[i])
+                assert int(stats[..., 2].sum()) > 0, "the step has misses"
+                assert np.array_equal(d.rows.cpu().numpy(), rows), f"row ids, batch {k}"
+                assert np.array_equal(d.stats.cpu().numpy(), stats), f"stats, batch {k}"
+                assert np.array_equal(d.out.cpu().numpy(), out), f"gathered rows, batch {k}"
+                assert np.array_equal(d.tok.cpu().numpy(), o.tok), f"slot tokens, batch {k}"
+                assert np.array_equal(d.pool.cpu().numpy(), o.pool), f"pool, batch {k}"
+    finally:
+        for d in devs:
+            d.close()
