@@ -109,7 +109,8 @@ __device__ int32_t map_find(const uint32_t* tab, int32_t n, const int32_t* keys,
 // The hot buffer's usable slots lower the slot half of their token's word.
 // The first kT * kScanUnroll slots come prefetched from the workgroup's
 // start (`pre`); for the others a slot's hot block is read only when its
-// token is in the table.  Ends with a barrier.
+// token is in the table.  Only slots whose token t has t mod S == s look
+// (the table holds only such tokens).  Ends with a barrier.
 constexpr int kScanUnroll = 4;
 
 // The first kT * kScanUnroll slots' tokens, already masked to -1 where the
@@ -135,7 +136,8 @@ __device__ __forceinline__ void prefetch_slots(const FetchParams& p, int32_t rl,
 }
 
 __device__ void scan_slots(const FetchParams& p, int32_t rl, uint32_t* tab, int32_t n,
-                           const int32_t* keys, const int32_t (&pre)[kScanUnroll]) {
+                           const int32_t* keys, const int32_t (&pre)[kScanUnroll], int32_t s = 0,
+                           int32_t S = 1) {
   const int tid = threadIdx.x;
   const int32_t C = p.hot_capacity;
   const int ps = p.page_shift;
@@ -152,7 +154,8 @@ __device__ void scan_slots(const FetchParams& p, int32_t rl, uint32_t* tab, int3
       tq[u] = first ? pre[u] : q < C ? stok[q] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < kScanUnroll; ++u) h[u] = tq[u] >= 0 ? map_find(tab, n, keys, tq[u]) : -1;
+    for (int u = 0; u < kScanUnroll; ++u)
+      h[u] = tq[u] >= 0 && (S == 1 || tq[u] % S == s) ? map_find(tab, n, keys, tq[u]) : -1;
 #pragma unroll
     for (int u = 0; u < kScanUnroll; ++u) {
       if (h[u] < 0) continue;
@@ -415,11 +418,13 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
                                   [](int32_t s) { return is_host_row(s); });
   if (any) cnt[2] = 1;  // racing writes of the same value
   HS_FILL_MARK(1);
+  // only this workgroup's tokens (t mod S == s) enter the table and are
+  // looked up by the slots
   for (int32_t e = tid; e < N; e += kT)
-    if (is_host_row(src[e])) map_insert(tab, n, keys, keys[e], e);
+    if (is_host_row(src[e]) && (S == 1 || keys[e] % S == s)) map_insert(tab, n, keys, keys[e], e);
   __syncthreads();
   if (cnt[2] == 0) return;  // nothing to read from the host
-  scan_slots(p, rl, tab, n, keys, pre);
+  scan_slots(p, rl, tab, n, keys, pre, s, S);
   HS_FILL_MARK(2);
 
   // ---- this workgroup's work lists: first entries of its miss tokens from
