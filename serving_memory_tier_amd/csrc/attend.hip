@@ -253,13 +253,15 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
     mb = fmaxf(mb, __shfl_xor(mb, 32));
     const bool grow = mb > m_run + kStaleMax;
     const float m_new = grow ? mb : m_run;
-    const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
+    // the hardware base-2 exponential: arguments here are <= kStaleMax, and
+    // results below 2^-126 (weights far below the block's largest) go to 0
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
     float pr[2][4], ls = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pr[mt][r] = m_new == -INFINITY ? 0.f : exp2f(sc[mt][r] - m_new);
+        pr[mt][r] = m_new == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[mt][r] - m_new);
         ls += pr[mt][r];
       }
     ls += __shfl_xor(ls, 16);
