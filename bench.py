@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--miss-path", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the all-miss first step of the no-residency workload "
                          "(every row over the host link)")
+    ap.add_argument("--cold-steps", type=int, default=16,
+                    help="steps after the event-timed ones, each behind an untimed 1 GiB scrub "
+                         "(cold caches: the 256 MB MALL and the L2s hold nothing of the step)")
     ap.add_argument("--event-steps", type=int, default=64,
                     help="steps launched one by one with HIP events around every kernel "
                          "(per-kernel durations), after the timed steps")
@@ -173,8 +176,9 @@ def main():
 
     W, K = args.warmup, args.steps
     KE = min(K, args.event_steps)  # eager steps timed with events, after the graph
+    NC = max(0, args.cold_steps)   # then steps behind a cache scrub, timed the same way
     t_gen = time.time()
-    wl = build_workload(args.workload, W + K + KE)
+    wl = build_workload(args.workload, W + K + KE + NC)
     print(f"[bench] workload {wl.name}: R={wl.R} L={wl.L} P={wl.P} K={wl.K} C={wl.C} "
           f"steps={len(wl.steps)} generated in {time.time() - t_gen:.1f}s", file=sys.stderr,
           flush=True)
@@ -269,9 +273,31 @@ def main():
                               "host_link_bytes": int(off_bytes),
                               "host_link_gbps": round(off_bytes / off_us / 1e3, 2)}
 
+    # cold steps: each behind an untimed write of 1 GiB, so that no cache holds
+    # the step's lists, tables, state or rows
+    cold = None
+    if NC:
+        scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cev = [[hev.new_event() for _ in range(4)] for _ in range(NC)]
+        cst = torch.zeros((NC, wl.R, wl.NG, 8), dtype=torch.int32, device="cuda")
+        for j in range(NC):
+            scrub.fill_(j & 0xFF)
+            busy.fill()
+            dev.launch_step_timed(W + K + KE + j, hev, sp0, cev[j], stats=cst[j])
+        torch.cuda.synchronize()
+        del scrub
+        sc = cst.sum(dim=(0, 1, 2)).cpu().numpy().astype(np.int64)
+        c_fused, c_commit = mean_us(0, 1, cev, NC), mean_us(1, 2, cev, NC)
+        c_host = fetch_bytes(wl, sc, NC)[0]
+        cold = {"steps": NC, "resolve_fill_us": round(c_fused, 2),
+                "commit_us": round(c_commit, 2), "step_us": round(c_fused + c_commit, 2),
+                "host_link_gbps": round(c_host / c_fused / 1e3, 2),
+                "rows_per_s": round(entries / ((c_fused + c_commit) * 1e-6)),
+                "note": "each step behind an untimed 1 GiB scrub; warm figures are 'kernels'"}
+
     # the hit-replay path: the last step's lists again with the same stamp --
     # every non-resident token hits, no host traffic, HBM-bound
-    last = W + K + KE - 1
+    last = W + K + KE + NC - 1
     NR = args.hit_replays
     rep = [[hev.new_event() for _ in range(4)] for _ in range(NR)]
     rep_stats = torch.zeros((wl.R, wl.NG, 8), dtype=torch.int32, device="cuda")
@@ -341,6 +367,7 @@ def main():
         "kernel_timing": f"HIP events on the launch stream around every kernel, over {KE} "
                          f"steps launched as hs_plan_replay's stages after the timed ones, each "
                          f"queued behind a 0.3 ms device spin so no event waits on the host",
+        "cold": cold,
         "hit_replay": hit_replay,
         "policy": policy,
         "consumer": consumer,
@@ -590,9 +617,14 @@ def policy_cost(wl, dev, n: int = 20):
     return out
 
 
-def cpu_baseline(wl, budget_s: float):
-    """The oracle as it stands, single-threaded, on the first steps of the same
-    workload (all requests, resolve + gather), until the time budget is used."""
+def _oracle_run(wl, budget_s: float, threads: int):
+    """The oracle on the first steps of the workload (all requests, resolve +
+    gather + offload), until the time budget is used: (steps done, seconds).
+    With threads > 1 each step's requests are cut into that many contiguous
+    blocks resolved at once (request-layers are independent, and the oracle's
+    C++ call runs without the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
 
@@ -605,25 +637,58 @@ def cpu_baseline(wl, budget_s: float):
     bt, hbt = wl.block_table.copy(), wl.host_block_table.copy()
     tok = np.full((wl.R, wl.L, wl.C), -1, np.int32)
     stp = np.zeros((wl.R, wl.L, wl.C), np.uint32)
+    cuts = np.linspace(0, wl.R, threads + 1).astype(int)
+    blocks = [(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    pool_ex = ThreadPoolExecutor(max_workers=threads) if threads > 1 else None
     done, spent = 0, 0.0
-    for s in wl.steps:
-        for r, p, v in s.hbt_set:
-            hbt[r, p] = v
-        for r, p, v in s.bt_set:
-            bt[r, p] = v
-        t = time.perf_counter()
-        oracle.resolve(pool, host, bt, hbt, s.ctx, wl.hot_blocks, tok, stp,
-                       np.ascontiguousarray(s.topk), s.stamp, True)
-        if s.offload.shape[0]:
-            oracle.offload(pool, host, s.offload)
-        spent += time.perf_counter() - t
-        done += 1
-        if spent >= budget_s:
-            break
+    try:
+        for s in wl.steps:
+            for r, p, v in s.hbt_set:
+                hbt[r, p] = v
+            for r, p, v in s.bt_set:
+                bt[r, p] = v
+            topk = np.ascontiguousarray(s.topk)
+            t = time.perf_counter()
+            if pool_ex is None:
+                oracle.resolve(pool, host, bt, hbt, s.ctx, wl.hot_blocks, tok, stp, topk,
+                               s.stamp, True)
+            else:
+                def part(ab):
+                    a, b = ab
+                    return oracle.resolve(pool, host, bt[a:b], hbt[a:b], s.ctx[a:b],
+                                          wl.hot_blocks[a:b], tok[a:b], stp[a:b], topk[a:b],
+                                          s.stamp, True)
+                list(pool_ex.map(part, blocks))
+            if s.offload.shape[0]:
+                oracle.offload(pool, host, s.offload)
+            spent += time.perf_counter() - t
+            done += 1
+            if spent >= budget_s:
+                break
+    finally:
+        if pool_ex is not None:
+            pool_ex.shutdown()
+    return done, spent
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle as it stands, single-threaded, on the first steps of the same
+    workload (all requests, resolve + gather), until the time budget is used;
+    then the same with one thread per host core (at most 16) over blocks of
+    requests."""
+    done, spent = _oracle_run(wl, budget_s, 1)
     rows = done * wl.R * wl.L * wl.P * wl.K
-    return {"value": round(rows / spent), "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} steps of {wl.name} ({wl.R} requests x {wl.L} layers, "
-                      f"resolve + gather + offload), {spent:.1f}s single-threaded"}
+    res = {"value": round(rows / spent), "unit": "rows/s", "cores": 1, "kind": "oracle",
+           "sample": f"first {done} steps of {wl.name} ({wl.R} requests x {wl.L} layers, "
+                     f"resolve + gather + offload), {spent:.1f}s single-threaded"}
+    threads = max(1, min(16, os.cpu_count() or 1, wl.R))
+    if threads > 1:
+        d2, s2 = _oracle_run(wl, budget_s, threads)
+        res["multi_thread"] = {"value": round(d2 * wl.R * wl.L * wl.P * wl.K / s2),
+                               "unit": "rows/s", "cores": threads,
+                               "sample": f"first {d2} steps, {s2:.1f}s, requests split "
+                                         f"into {threads} blocks"}
+    return res
 
 
 if __name__ == "__main__":
