@@ -35,6 +35,14 @@
 
 #include "hs_internal.h"
 
+// Timing hooks (per-workgroup time per phase of the block loop), empty unless
+// a profiling build defines them.
+#ifndef HS_ATTEND_MARK
+#define HS_ATTEND_DECL
+#define HS_ATTEND_MARK(i)
+#define HS_ATTEND_FLUSH
+#endif
+
 namespace hs {
 namespace {
 
@@ -200,11 +208,14 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
     s.ids[k] = id;
   }
   __syncthreads();
+  HS_ATTEND_DECL;
   BlockRegs regs;
   if (n_keys > 0) fetch_block(p, s, 0, regs);
   for (int32_t key0 = key_lo; key0 < key_end; key0 += kBlockKeys) {
+    HS_ATTEND_MARK(0);
     store_block(s, regs);
     __syncthreads();
+    HS_ATTEND_MARK(1);
     // the next block's loads are in flight while this one is computed
     if (key0 + kBlockKeys < key_end) fetch_block(p, s, key0 + kBlockKeys - key_lo, regs);
     // ---- scores of this wave's key tile: S^T[key 16 half + ..][head]
@@ -238,6 +249,7 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
       }
     }
     __syncthreads();   // both key tiles' scores are in LDS
+    HS_ATTEND_MARK(2);
     // ---- online softmax over the block's 32 keys (both halves alike)
     float sc[2][4];
 #pragma unroll
@@ -294,8 +306,12 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
       for (int d8 = 0; d8 < 8; ++d8)
         o[t2 * 8 + d8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d8], b, o[t2 * 8 + d8], 0, 0, 0);
     }
+    HS_ATTEND_MARK(3);
     __syncthreads();   // every wave is done with the block before the next store
+    HS_ATTEND_MARK(4);
   }
+  HS_ATTEND_MARK(5);
+  HS_ATTEND_FLUSH;
 
   if (!head_ok) return;
   const int64_t th = (int64_t)t * p.num_heads + head;

@@ -41,7 +41,7 @@
 #include "hs_internal.h"
 
 // Timing hooks (per-workgroup timestamps), empty unless a profiling build
-// defines them.
+// defines them; negative indices mark steps inside the miss workgroups.
 #ifndef HS_FILL_MARK
 #define HS_FILL_MARK(i)
 #endif
@@ -423,6 +423,7 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   for (int32_t e = tid; e < N; e += kT)
     if (is_host_row(src[e]) && (S == 1 || keys[e] % S == s)) map_insert(tab, n, keys, keys[e], e);
   __syncthreads();
+  HS_FILL_MARK(-1);
   if (cnt[2] == 0) return;  // nothing to read from the host
   scan_slots(p, rl, tab, n, keys, pre, s, S);
   HS_FILL_MARK(2);
@@ -463,6 +464,7 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   for (int32_t l = 0; l < v.group; ++l)
     host_rows<kHostUnroll>(p, v, list, src, v.host_l + l * v.host_stride, v.out + l * v.out_stride,
                            0, total);
+  HS_FILL_MARK(-2);
   if (n_dup == 0 || p.misses_only) return;
   __syncthreads();  // this workgroup's row writes are visible to it
 
