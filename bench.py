@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--miss-path", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the all-miss first step of the no-residency workload "
                          "(every row over the host link)")
+    ap.add_argument("--ceilings", action=argparse.BooleanOptionalAction, default=True,
+                    help="also probe the HBM copy and host-link DMA ceilings in the same job")
     ap.add_argument("--cold-steps", type=int, default=16,
                     help="steps after the event-timed ones, each behind an untimed 1 GiB scrub "
                          "(cold caches: the 256 MB MALL and the L2s hold nothing of the step)")
@@ -239,7 +241,9 @@ def main():
     torch.cuda.synchronize()
 
     def mean_us(a, b, ev=events, n=KE):
-        return 1e3 * float(np.mean([hev.elapsed_ms(ev[j][a], ev[j][b]) for j in range(n)]))
+        # the median: a launch the host enqueued late (after the device spin
+        # ahead of it ran out) would add its host delay to the mean
+        return 1e3 * float(np.median([hev.elapsed_ms(ev[j][a], ev[j][b]) for j in range(n)]))
 
     fused_us, commit_us = mean_us(0, 1), mean_us(1, 2)
     off = [(j, hev.elapsed_ms(events[j][2], events[j][3])) for j in range(KE)
@@ -267,7 +271,7 @@ def main():
         kernels.pop("offload", None)
     if off:
         page_layers = [wl.steps[W + K + j].offload.shape[0] * wl.L for j, _ in off]
-        off_us = 1e3 * float(np.mean([ms for _, ms in off]))
+        off_us = 1e3 * float(np.median([ms for _, ms in off]))
         off_bytes = float(np.mean(page_layers)) * PAGE * ROW
         kernels["offload"] = {"us": round(off_us, 2), "launches": len(off),
                               "host_link_bytes": int(off_bytes),
@@ -324,6 +328,7 @@ def main():
     if args.consumer and wl.G == 1 and wl.L == 1:
         consumer = consumer_cost(wl, hev, sp0, busy, n_steps=min(16, len(wl.steps)))
     miss_path = miss_path_cost(hev, sp0, busy) if args.miss_path else None
+    ceilings = probe_ceilings(hev, sp0, busy) if args.ceilings else None
     busy.close()
     kernels["page_touch"] = page_touch
     policy = policy_cost(wl, dev)
@@ -344,6 +349,16 @@ def main():
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                     "traffic": None}
     roofline["traffic"] = measured_traffic(roofline["kernel"], wl.name)
+    if ceilings:
+        # the same against what this chip's copies reach in this job
+        ceil = (ceilings["host_to_device_dma_gbps"] if roofline["bound"] == "host_link"
+                else ceilings["hbm_copy_gbps"])
+        roofline["probed_ceiling"] = ceil
+        roofline["frac_of_probed"] = round(roofline["achieved"] / ceil, 4)
+        if miss_path:
+            miss_path["host_link_frac_of_probed"] = round(
+                miss_path["host_link_gbps"] / ceilings["host_to_device_dma_gbps"], 4)
+        hit_replay["hbm_frac_of_probed"] = round(hit_replay["hbm_gbps"] / ceilings["hbm_copy_gbps"], 4)
     # whole steps of the timed region: algorithmic bytes per step / step time
     step_hbm_k = (decide_hbm_bytes(wl, st_all, K) + fetch_bytes(wl, st_all, K)[1] +
                   commit_bytes(wl, st_all, K))
@@ -364,14 +379,15 @@ def main():
         "per_step": {"hits": round(st_all[1] / K, 1), "misses": round(st_all[2] / K, 1),
                      "resident": round(st_all[0] / K, 1)},
         "kernels": kernels,
-        "kernel_timing": f"HIP events on the launch stream around every kernel, over {KE} "
-                         f"steps launched as hs_plan_replay's stages after the timed ones, each "
-                         f"queued behind a 0.3 ms device spin so no event waits on the host",
+        "kernel_timing": f"HIP events on the launch stream around every kernel, median over "
+                         f"{KE} steps launched as hs_plan_replay's stages after the timed ones, "
+                         f"each queued behind a 0.3 ms device spin so no event waits on the host",
         "cold": cold,
         "hit_replay": hit_replay,
         "policy": policy,
         "consumer": consumer,
         "miss_path": miss_path,
+        "ceilings": ceilings,
         "roofline": roofline,
         "cpu_baseline": None,
     }
@@ -474,9 +490,9 @@ def consumer_cost(wl, hev, stream: int, busy, n_steps: int = 16, heads: int = 12
         torch.cuda.synchronize()
         r_us = [1e3 * hev.elapsed_ms(a, b) for a, b, _ in ev]
         a_us = [1e3 * hev.elapsed_ms(b, c) for _, b, c in ev]
-        res[mode] = {"resolve_us": round(float(np.mean(r_us)), 2),
-                     "attention_us": round(float(np.mean(a_us)), 2),
-                     "step_us": round(float(np.mean(r_us) + np.mean(a_us)), 2)}
+        res[mode] = {"resolve_us": round(float(np.median(r_us)), 2),
+                     "attention_us": round(float(np.median(a_us)), 2),
+                     "step_us": round(float(np.median(r_us) + np.median(a_us)), 2)}
         dev.close()
     flops = 2.0 * T * heads * K * (576 + 512)
     for mode in res:
@@ -524,7 +540,7 @@ def miss_path_cost(hev, stream: int, busy, reps: int = 8):
     commit = np.array([1e3 * hev.elapsed_ms(e[1], e[2]) for e in ev])
     host_bytes = float(np.mean((st[:, 2] + st[:, 3]) * ROW))
     dev.close()
-    f_us, c_us = float(np.mean(fused)), float(np.mean(commit))
+    f_us, c_us = float(np.median(fused)), float(np.median(commit))
     gbps = host_bytes / f_us / 1e3
     return {"workload": "no_residency first step (8 x 2048, empty 4096-row hot buffer)",
             "calls": reps, "misses": int(np.mean(st[:, 2])),
@@ -533,6 +549,43 @@ def miss_path_cost(hev, stream: int, busy, reps: int = 8):
             "commit_us": round(c_us, 2), "step_us": round(f_us + c_us, 2),
             "host_link_gbps": round(gbps, 2), "host_link_frac": round(gbps / HOST_LINK_PEAK_GBPS, 4),
             "step_host_link_gbps": round(host_bytes / (f_us + c_us) / 1e3, 2)}
+
+
+def probe_ceilings(hev, stream: int, busy):
+    """The chip's practical ceilings in the same job: a 1 GiB device-to-device
+    copy (HBM read + write), and 256 MiB DMA copies from pinned host memory to
+    the device and back (the host link, one direction each).  HIP events
+    around each copy on the launch stream; best of three."""
+    import torch
+
+    def best(fn, nbytes, reps=3):
+        t = []
+        for _ in range(reps):
+            a, b = hev.new_event(), hev.new_event()
+            busy.fill()
+            hev.record(a, stream)
+            fn()
+            hev.record(b, stream)
+            torch.cuda.synchronize()
+            t.append(hev.elapsed_ms(a, b))
+        return nbytes / (min(t) * 1e-3) / 1e9
+
+    s = torch.cuda.current_stream()
+    d0 = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    d1 = torch.empty_like(d0)
+    d0.fill_(1)
+    hbm = best(lambda: d1.copy_(d0), 2 << 30)
+    del d0, d1
+    h = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    h2d = best(lambda: d.copy_(h, non_blocking=True), 256 << 20)
+    d2h = best(lambda: h.copy_(d, non_blocking=True), 256 << 20)
+    torch.cuda.synchronize()
+    del h, d
+    assert s.cuda_stream == stream
+    return {"hbm_copy_gbps": round(hbm, 1), "host_to_device_dma_gbps": round(h2d, 2),
+            "device_to_host_dma_gbps": round(d2h, 2),
+            "note": "read + write bytes of a 1 GiB device copy; 256 MiB pinned-host DMA each way"}
 
 
 def touch_cost(wl, dev, hev, stream: int, i: int, n: int, busy=None):
