@@ -43,6 +43,8 @@ class HipRuntime:
         hip.hipGraphDestroy.argtypes = [ct.c_void_p]
         hip.hipMemcpyAsync.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_size_t, ct.c_int,
                                        ct.c_void_p]
+        hip.hipMemcpy2DAsync.argtypes = [ct.c_void_p, ct.c_size_t, ct.c_void_p, ct.c_size_t,
+                                         ct.c_size_t, ct.c_size_t, ct.c_int, ct.c_void_p]
         self.made = []
         self.graph = self.exec = None
 
@@ -102,6 +104,15 @@ class HipRuntime:
         if self.hip.hipMemcpyAsync(ct.c_void_p(dst), ct.c_void_p(src), nbytes, _H2D,
                                    ct.c_void_p(stream)) != 0:
             raise RuntimeError("hipMemcpyAsync failed")
+
+    def memcpy2d_h2d(self, dst: int, dpitch: int, src: int, spitch: int, width: int,
+                     height: int, stream: int) -> None:
+        """`height` rows of `width` bytes, `spitch` apart in host memory and
+        `dpitch` apart on the device, as one copy."""
+        ct = self.ct
+        if self.hip.hipMemcpy2DAsync(ct.c_void_p(dst), dpitch, ct.c_void_p(src), spitch, width,
+                                     height, _H2D, ct.c_void_p(stream)) != 0:
+            raise RuntimeError("hipMemcpy2DAsync failed")
 
     def close(self) -> None:
         self.destroy_graph()

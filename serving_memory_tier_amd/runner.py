@@ -150,28 +150,57 @@ class DeviceRun:
                         for i in range(n)]
         n_vals = sum(s.hbt_set.shape[0] + s.bt_set.shape[0] for s in wl.steps)
         self.pinned_vals = torch.empty(max(1, n_vals), dtype=torch.int32, pin_memory=True)
+        # each step's updates as copies of runs, whichever of two cuts needs
+        # fewer copies: one table column (the same page of consecutive
+        # requests, max_pages * 4 bytes apart: a completed page updates every
+        # request's entry at once) or one row (consecutive pages of a request,
+        # contiguous)
         self.table_sets = []
         k = 0
         for s in wl.steps:
             sets = []
             for arr, t in ((s.hbt_set, self.hbt), (s.bt_set, self.bt)):
-                for r, p, v in arr:
-                    self.pinned_vals[k] = int(v)
-                    sets.append((t.data_ptr() + 4 * (int(r) * wl.max_pages + int(p)),
-                                 self.pinned_vals.data_ptr() + 4 * k))
-                    k += 1
+                if arr.shape[0] == 0:
+                    continue
+                assert np.unique(arr[:, :2], axis=0).shape[0] == arr.shape[0], \
+                    "one update per table entry"
+                cuts = []
+                for major, minor, pitch in ((1, 0, 4 * wl.max_pages), (0, 1, 4)):
+                    a = arr[np.lexsort((arr[:, minor], arr[:, major]))]
+                    runs = []
+                    j = 0
+                    while j < a.shape[0]:
+                        e = j + 1
+                        while (e < a.shape[0] and a[e, major] == a[j, major]
+                               and a[e, minor] == a[e - 1, minor] + 1):
+                            e += 1
+                        runs.append((j, e))
+                        j = e
+                    cuts.append((len(runs), a, runs, pitch))
+                _, a, runs, pitch = min(cuts, key=lambda c: c[0])
+                for j, e in runs:
+                    self.pinned_vals[k:k + e - j] = torch.from_numpy(a[j:e, 2].astype(np.int32))
+                    sets.append((t.data_ptr() + 4 * (int(a[j, 0]) * wl.max_pages + int(a[j, 1])),
+                                 pitch, self.pinned_vals.data_ptr() + 4 * k, e - j))
+                    k += e - j
             self.table_sets.append(sets)
+
+    def _table_updates(self, i: int, hip, stream: int) -> None:
+        for dst, pitch, src, n in self.table_sets[i]:
+            if n == 1 or pitch == 4:
+                hip.memcpy_h2d(dst, src, 4 * n, stream)
+            else:
+                hip.memcpy2d_h2d(dst, pitch, src, 4, 4, n, stream)
 
     def launch_step(self, i: int, hip, stream: int, stats=None, serial: bool = False) -> None:
         """Step ``i`` on ``stream`` with no host work: the scheduler's table
-        updates as 4-byte copies from pinned memory, then one hs_plan_replay
+        updates as copies from pinned memory, then one hs_plan_replay
         call (resolve, gather, offload of the pages the step completed).
         ``serial``: the decide and move stages one after the other instead
         (the path the library takes without a gather output, with one)."""
         wl = self.wl
         s = wl.steps[i]
-        for dst, src in self.table_sets[i]:
-            hip.memcpy_h2d(dst, src, 4, stream)
+        self._table_updates(i, hip, stream)
         st = self.stats if stats is None else stats
         n_off = s.offload.shape[0]
         if wl.G > 1:
@@ -200,8 +229,7 @@ class DeviceRun:
         launch, after it, after the commit and after the offload."""
         wl = self.wl
         s = wl.steps[i]
-        for dst, src in self.table_sets[i]:
-            hip.memcpy_h2d(dst, src, 4, stream)
+        self._table_updates(i, hip, stream)
         st = self.stats if stats is None else stats
         L, B, T = self.layout, self.batches[i], self.topk[i]
         if wl.G > 1:

@@ -73,8 +73,11 @@ def test_graph_replays_match_eager(wl_name):
     from serving_memory_tier_amd.runner import DeviceRun
 
     if wl_name == "mixed_decode":
-        wl = hs_gen.mixed_decode(R=8, steps=12)
-        warm, n_cap = 3, 8
+        # the captured steps include step 16, where a page completes and every
+        # request's host-table entry for it is set (one strided copy)
+        wl = hs_gen.mixed_decode(R=8, steps=20)
+        warm, n_cap = 12, 6
+        assert wl.steps[16].hbt_set.shape[0] == 8
     else:
         # turns with prefill, completed pages offloaded and pages leaving the tail
         wl = hs_gen.multi_layer(turns=4, R=4, L=4)
@@ -101,6 +104,14 @@ def test_graph_replays_match_eager(wl_name):
             ref.take(j, eager)
         torch.cuda.synchronize()
         ref_end = _snapshot(eager)
+        # the staged table updates leave the tables the workload prescribes
+        bt, hbt = wl.block_table.copy(), wl.host_block_table.copy()
+        for s in wl.steps[:warm + n_cap]:
+            for arr, t in ((s.hbt_set, hbt), (s.bt_set, bt)):
+                for r, p, v in arr:
+                    t[r, p] = v
+        assert np.array_equal(ref_end["bt"].cpu().numpy(), bt), "block table after the updates"
+        assert np.array_equal(ref_end["hbt"].cpu().numpy(), hbt), "host table after the updates"
 
         # capture the same steps on the second batch
         start = _snapshot(graphed)
