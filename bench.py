@@ -229,6 +229,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
+    hev.destroy_graph()
 
     # per-kernel durations: the next KE steps launched as hs_plan_replay's
     # stages on the launch stream (the fused resolve-and-fill launch, the
@@ -320,6 +321,26 @@ def main():
                   "hbm_gbps": round(rep_bytes / r_step / 1e3, 1),
                   "hbm_frac": round(rep_bytes / r_step / 1e3 / HBM_PEAK_GBPS, 4),
                   "resolve_fill_hbm_gbps": round(r_fused_bytes / r_fused / 1e3, 1)}
+    if graph and NR:
+        # the same replays captured once and replayed as one graph, timed like
+        # the decode steps (no event pairs between the launches): a hit
+        # replay leaves the state as it found it, so replaying it is exact
+        hev.begin_capture(cap.cuda_stream)
+        try:
+            for j in range(NR):
+                dev.launch_step(last, hev, cap.cuda_stream, stats=rep_stats)
+        finally:
+            hev.end_capture(cap.cuda_stream)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        hev.launch(cap.cuda_stream)
+        torch.cuda.synchronize()
+        g_step = (time.perf_counter() - t2) / NR * 1e6
+        hev.destroy_graph()
+        hit_replay["graph_step_us"] = round(g_step, 2)
+        hit_replay["graph_rows_per_s"] = round(entries / (g_step * 1e-6))
+        hit_replay["graph_hbm_gbps"] = round(rep_bytes / g_step / 1e3, 1)
+        hit_replay["graph_hbm_frac"] = round(rep_bytes / g_step / 1e3 / HBM_PEAK_GBPS, 4)
 
     # page coldness for the residency policy: hs_page_touch over the last
     # step's lists, HIP events around each launch
@@ -359,6 +380,9 @@ def main():
             miss_path["host_link_frac_of_probed"] = round(
                 miss_path["host_link_gbps"] / ceilings["host_to_device_dma_gbps"], 4)
         hit_replay["hbm_frac_of_probed"] = round(hit_replay["hbm_gbps"] / ceilings["hbm_copy_gbps"], 4)
+        if "graph_hbm_gbps" in hit_replay:
+            hit_replay["graph_hbm_frac_of_probed"] = round(
+                hit_replay["graph_hbm_gbps"] / ceilings["hbm_copy_gbps"], 4)
     # whole steps of the timed region: algorithmic bytes per step / step time
     step_hbm_k = (decide_hbm_bytes(wl, st_all, K) + fetch_bytes(wl, st_all, K)[1] +
                   commit_bytes(wl, st_all, K))
@@ -391,7 +415,6 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    hev.destroy_graph()
     hev.close()
     dev.close()
     if args.calibrate_copy:
