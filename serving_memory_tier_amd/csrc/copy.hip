@@ -154,6 +154,8 @@ __global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_p
 // be ten rounds, and a step of misses only would run on a quarter as many
 // waves).
 constexpr int kCommitEPW = 16;
+// The C ABI bounds a launch's waves by kMoveEntriesPerWave entries a wave.
+static_assert(kCommitEPW >= kMoveEntriesPerWave, "commit waves within the validated bound");
 
 // The commit after the early fill: one wave per kCommitEPW entries of a
 // request-layer.  Entries holding a first-entry code copy their output row
