@@ -593,7 +593,8 @@ def probe_ceilings(hev, stream: int, busy):
             t.append(hev.elapsed_ms(a, b))
         return nbytes / (min(t) * 1e-3) / 1e9
 
-    s = torch.cuda.current_stream()
+    # the copies go to torch's current stream, which must be the timed one
+    assert torch.cuda.current_stream().cuda_stream == stream
     d0 = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     d1 = torch.empty_like(d0)
     d0.fill_(1)
@@ -605,7 +606,6 @@ def probe_ceilings(hev, stream: int, busy):
     d2h = best(lambda: h.copy_(d, non_blocking=True), 256 << 20)
     torch.cuda.synchronize()
     del h, d
-    assert s.cuda_stream == stream
     return {"hbm_copy_gbps": round(hbm, 1), "host_to_device_dma_gbps": round(h2d, 2),
             "device_to_host_dma_gbps": round(d2h, 2),
             "note": "read + write bytes of a 1 GiB device copy; 256 MiB pinned-host DMA each way"}
