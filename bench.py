@@ -474,7 +474,8 @@ def consumer_cost(wl, hev, stream: int, busy, n_steps: int = 16, heads: int = 12
 
     import serving_memory_tier_amd as hs
     from serving_memory_tier_amd.runner import DeviceRun
-    T, K = wl.R * wl.P, wl.P * wl.K
+    # one query token per (request, position), each attending to its own K rows
+    T, K = wl.R * wl.P, wl.K
     q = (torch.randn((T, heads, 576), device="cuda") * 0.5).to(torch.bfloat16).view(torch.int16)
     out = torch.empty((T, heads, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((T, heads), dtype=torch.float32, device="cuda")
@@ -486,6 +487,10 @@ def consumer_cost(wl, hev, stream: int, busy, n_steps: int = 16, heads: int = 12
     for mode in ("gathered", "in_place"):
         dev = DeviceRun(wl)
         dev.upload_steps()
+        # the kernel reads T x K row ids, and in the gathered mode T x K rows
+        assert dev.rows.numel() == T * K and dev.out.shape[:-1].numel() == T * K, \
+            "consumer shapes must match the batch's row ids and gathered rows"
+        assert dev.out.shape[-1] == ROW
         lay_kv = hs.layout_of(1, ROW, 1, 64, wl.pool_rows if mode == "in_place" else T * K, 0)
         ev = [(hev.new_event(), hev.new_event(), hev.new_event()) for _ in range(n_steps)]
         for i in range(n_steps):
