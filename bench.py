@@ -328,7 +328,7 @@ def main():
         hev.begin_capture(cap.cuda_stream)
         try:
             for j in range(NR):
-                dev.launch_step(last, hev, cap.cuda_stream, stats=rep_stats)
+                dev.launch_step(last, hev, cap.cuda_stream, stats=rep_stats, offload=False)
         finally:
             hev.end_capture(cap.cuda_stream)
         torch.cuda.synchronize()

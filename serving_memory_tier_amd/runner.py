@@ -192,17 +192,19 @@ class DeviceRun:
             else:
                 hip.memcpy2d_h2d(dst, pitch, src, 4, 4, n, stream)
 
-    def launch_step(self, i: int, hip, stream: int, stats=None, serial: bool = False) -> None:
+    def launch_step(self, i: int, hip, stream: int, stats=None, serial: bool = False,
+                    offload: bool = True) -> None:
         """Step ``i`` on ``stream`` with no host work: the scheduler's table
         updates as copies from pinned memory, then one hs_plan_replay
         call (resolve, gather, offload of the pages the step completed).
         ``serial``: the decide and move stages one after the other instead
-        (the path the library takes without a gather output, with one)."""
+        (the path the library takes without a gather output, with one).
+        ``offload``: False leaves out the step's prefix-page offload."""
         wl = self.wl
         s = wl.steps[i]
         self._table_updates(i, hip, stream)
         st = self.stats if stats is None else stats
-        n_off = s.offload.shape[0]
+        n_off = s.offload.shape[0] if offload else 0
         if wl.G > 1:
             assert not serial, "layer groups have no serial staged form"
             hs_resolve_grouped(self.layout, self.batches[i], wl.G, self.topk[i], wl.P, wl.K,
