@@ -25,6 +25,32 @@ PAGE = 64
 ROW = 656
 
 
+def update_runs(arr: np.ndarray):
+    """A step's table updates (rows of (request, page, value), one per entry) as
+    runs that one copy each can write: whichever of two cuts gives fewer runs --
+    columns (the same page of consecutive requests, max_pages entries apart: a
+    completed page updates every request's entry at once) or rows (consecutive
+    pages of one request, contiguous).  Yields (request, page, along_pages,
+    int32 values) for the run starting at (request, page)."""
+    if arr.shape[0] == 0:
+        return []
+    assert np.unique(arr[:, :2], axis=0).shape[0] == arr.shape[0], "one update per table entry"
+    cuts = []
+    for major, minor in ((1, 0), (0, 1)):   # columns, then rows
+        a = arr[np.lexsort((arr[:, minor], arr[:, major]))]
+        runs = []
+        j = 0
+        while j < a.shape[0]:
+            e = j + 1
+            while (e < a.shape[0] and a[e, major] == a[j, major]
+                   and a[e, minor] == a[e - 1, minor] + 1):
+                e += 1
+            runs.append((int(a[j, 0]), int(a[j, 1]), minor == 1, a[j:e, 2].astype(np.int32)))
+            j = e
+        cuts.append(runs)
+    return min(cuts, key=len)
+
+
 class DeviceRun:
     def __init__(self, wl, device: str = "cuda", content_device: str | None = None):
         self.wl = wl
@@ -150,39 +176,19 @@ class DeviceRun:
                         for i in range(n)]
         n_vals = sum(s.hbt_set.shape[0] + s.bt_set.shape[0] for s in wl.steps)
         self.pinned_vals = torch.empty(max(1, n_vals), dtype=torch.int32, pin_memory=True)
-        # each step's updates as copies of runs, whichever of two cuts needs
-        # fewer copies: one table column (the same page of consecutive
-        # requests, max_pages * 4 bytes apart: a completed page updates every
-        # request's entry at once) or one row (consecutive pages of a request,
-        # contiguous)
+        # each step's updates as copies of runs (update_runs), one copy a run
         self.table_sets = []
         k = 0
         for s in wl.steps:
             sets = []
             for arr, t in ((s.hbt_set, self.hbt), (s.bt_set, self.bt)):
-                if arr.shape[0] == 0:
-                    continue
-                assert np.unique(arr[:, :2], axis=0).shape[0] == arr.shape[0], \
-                    "one update per table entry"
-                cuts = []
-                for major, minor, pitch in ((1, 0, 4 * wl.max_pages), (0, 1, 4)):
-                    a = arr[np.lexsort((arr[:, minor], arr[:, major]))]
-                    runs = []
-                    j = 0
-                    while j < a.shape[0]:
-                        e = j + 1
-                        while (e < a.shape[0] and a[e, major] == a[j, major]
-                               and a[e, minor] == a[e - 1, minor] + 1):
-                            e += 1
-                        runs.append((j, e))
-                        j = e
-                    cuts.append((len(runs), a, runs, pitch))
-                _, a, runs, pitch = min(cuts, key=lambda c: c[0])
-                for j, e in runs:
-                    self.pinned_vals[k:k + e - j] = torch.from_numpy(a[j:e, 2].astype(np.int32))
-                    sets.append((t.data_ptr() + 4 * (int(a[j, 0]) * wl.max_pages + int(a[j, 1])),
-                                 pitch, self.pinned_vals.data_ptr() + 4 * k, e - j))
-                    k += e - j
+                for r, p, along_pages, vals in update_runs(arr):
+                    n_run = vals.shape[0]
+                    self.pinned_vals[k:k + n_run] = torch.from_numpy(vals)
+                    pitch = 4 if along_pages else 4 * wl.max_pages
+                    sets.append((t.data_ptr() + 4 * (r * wl.max_pages + p), pitch,
+                                 self.pinned_vals.data_ptr() + 4 * k, n_run))
+                    k += n_run
             self.table_sets.append(sets)
 
     def _table_updates(self, i: int, hip, stream: int) -> None:
