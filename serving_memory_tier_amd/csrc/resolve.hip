@@ -671,15 +671,18 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
     bool predC[EC];
     int posC[EC];
     // the least-recent stamp among the usable non-hit slots, its group size,
-    // and the number of such slots; non-candidates carry stamp ~0 and are
-    // never taken (every candidate group is found before them)
+    // and the number of such slots.  Candidacy is a bit per slot round, not a
+    // stamp value: every uint32 is a legal stamp, 0xffffffff included, so no
+    // stamp can mark a hit or unusable slot.
     uint32_t v = 0xffffffffu;
     int c = 0, nv = 0;
+    uint32_t candm = 0;  // bit j: this thread's slot j * kThreads + tid is a candidate
+    static_assert(EC <= 32, "candidate bits");
 #pragma unroll
     for (int j = 0; j < EC; ++j) {
       const int q = j * kThreads + tid;
       const bool cand = q < C && sflag[q] == 0;
-      if (!cand) cst[j] = 0xffffffffu;
+      candm |= cand ? (1u << j) : 0u;
       nv += cand ? 1 : 0;
       if (cand) {
         if (cst[j] < v) {
@@ -701,7 +704,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
       const int take = c < A - taken ? c : A - taken;
       const uint32_t gv = v;
 #pragma unroll
-      for (int j = 0; j < EC; ++j) predC[j] = cst[j] == gv && (j * kThreads + tid) < C;
+      for (int j = 0; j < EC; ++j) predC[j] = ((candm >> j) & 1u) && cst[j] == gv;
       block_compact<EC>(predC, posC, red);
 #pragma unroll
       for (int j = 0; j < EC; ++j)
@@ -717,7 +720,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
 #pragma unroll
       for (int j = 0; j < EC; ++j) {
         const uint32_t st = cst[j];
-        if (st > gv && st != 0xffffffffu) {
+        if (((candm >> j) & 1u) && st > gv) {
           if (st < v2) {
             v2 = st;
             c2 = 1;
@@ -739,7 +742,7 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
 #pragma unroll
       for (int j = 0; j < EC; ++j) {
         const int q = j * kThreads + tid;
-        predC[j] = q < C && sflag[q] == 0;
+        predC[j] = ((candm >> j) & 1u) != 0;
         if (predC[j]) {
           mn = min(mn, cst[j]);
           mx = max(mx, cst[j]);

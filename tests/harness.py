@@ -23,17 +23,20 @@ class OracleRun:
     tables, state, top-K lists and offload pairs are cut to the subset.
     """
 
-    def __init__(self, wl: hs_gen.Workload, requests=None):
+    def __init__(self, wl: hs_gen.Workload, requests=None, content_device=None, threads=1):
         self.wl = wl
+        self.threads = threads
         if requests is not None and wl.dynamic:
             raise ValueError("blocks move between requests: simulate the whole batch")
         self.req = np.arange(wl.R) if requests is None else np.asarray(requests, dtype=np.int64)
         R = self.req.size
         self.pool = np.zeros((wl.L, wl.pool_rows, ROW), dtype=np.uint8)
         self.host = np.zeros((wl.L, wl.host_rows, ROW), dtype=np.uint8)
-        wl.fill_device_pool(torch.from_numpy(self.pool),
+        # the generator's rows, computed where the caller says (its torch and
+        # numpy forms are pinned bit-identical)
+        wl.fill_device_pool(torch.from_numpy(self.pool), compute_device=content_device,
                             requests=None if requests is None else self.req)
-        wl.fill_host_pool(torch.from_numpy(self.host))
+        wl.fill_host_pool(torch.from_numpy(self.host), compute_device=content_device)
         self.bt = np.ascontiguousarray(wl.block_table[self.req])
         self.hbt = np.ascontiguousarray(wl.host_block_table[self.req])
         self.hot = np.ascontiguousarray(wl.hot_blocks[self.req])
@@ -67,14 +70,31 @@ class OracleRun:
         self.ctx = np.ascontiguousarray(step.ctx[self.req])
 
     def resolve(self, step: hs_gen.Step, gather: bool = True, topk=None, stamp=None):
-        topk = step.topk[self.req] if topk is None else topk
+        topk = np.ascontiguousarray(step.topk[self.req] if topk is None else topk)
         stamp = step.stamp if stamp is None else stamp
+        R = self.req.size
+        if self.threads <= 1 or R < 2:
+            return self._resolve_block(0, R, topk, stamp, gather)
+        # request-layers are independent and their hot blocks disjoint, so
+        # blocks of requests resolve on threads of their own (the oracle
+        # releases the GIL); each block's state and lists are contiguous
+        # slices of the batch's arrays
+        from concurrent.futures import ThreadPoolExecutor
+        n = min(self.threads, R)
+        cuts = [R * i // n for i in range(n + 1)]
+        with ThreadPoolExecutor(n) as ex:
+            parts = list(ex.map(lambda i: self._resolve_block(cuts[i], cuts[i + 1], topk, stamp,
+                                                              gather), range(n)))
+        rows = np.concatenate([p[0] for p in parts])
+        stats = np.concatenate([p[1] for p in parts])
+        out = np.concatenate([p[2] for p in parts]) if gather else None
+        return rows, stats, out
+
+    def _resolve_block(self, r0, r1, topk, stamp, gather):
+        a = [x[r0:r1] for x in (self.bt, self.hbt, self.ctx, self.hot, self.tok, self.stp, topk)]
         if self.wl.G > 1:
-            return oracle.resolve_grouped(self.pool, self.host, self.bt, self.hbt, self.ctx,
-                                          self.hot, self.tok, self.stp, np.ascontiguousarray(topk),
-                                          stamp, self.wl.G, gather)
-        return oracle.resolve(self.pool, self.host, self.bt, self.hbt, self.ctx, self.hot,
-                              self.tok, self.stp, np.ascontiguousarray(topk), stamp, gather)
+            return oracle.resolve_grouped(self.pool, self.host, *a, stamp, self.wl.G, gather)
+        return oracle.resolve(self.pool, self.host, *a, stamp, gather)
 
     def pairs(self, step: hs_gen.Step) -> np.ndarray:
         if self.req.size == self.wl.R:

@@ -213,6 +213,9 @@ CASES = [
     # a 4-position plan, and the largest capacity the resolver takes
     ("mtp_capacity", 2, 1, 4, 2048, 10240, 64, 656, 400, False),
     ("max_capacity_12k", 2, 1, 1, 2048, 12288, 64, 656, 400, False),
+    # the resolver's largest LDS plan: 4 x 2048 entries with 12,288 slots
+    ("max_plan_12k", 2, 1, 4, 2048, 12288, 64, 656, 500, False),
+    ("max_plan_12k_hostile", 2, 1, 4, 2048, 12288, 64, 656, 500, True),
     ("hostile_c9216", 3, 1, 2, 900, 9216, 64, 656, 300, True),
     ("min_capacity", 5, 1, 1, 300, 64, 64, 656, 40, False),
     ("page16", 3, 2, 2, 700, 1024, 16, 656, 900, False),
@@ -397,5 +400,116 @@ def test_victims_across_many_stamp_groups(C, mode):
         _say(f"[edges] stamp groups C={C} {mode} step 2")
         _, st = _compare(case, a, second, C + 9, mode=mode)
         assert (st[..., 1] == K // 2).all()
+    finally:
+        case.close()
+
+
+def _max_stamp_instance(rs, R, L, C, page, n_pages, n_resident):
+    """Slots 0..page-1 sit in an unusable hot block (outside the pool) and hold
+    stamp 5; slots page..2*page-1 hold tokens the lists will ask for (hits)
+    at stamp 7; every other slot holds a token nobody asks for at the largest
+    stamp, 0xffffffff.  Pages below n_pages - n_resident are host-only."""
+    rb = 656
+    n_blocks = R * (C // page) + R * n_resident + 4
+    pool = rs.integers(0, 256, size=(L, n_blocks * page, rb), dtype=np.uint8)
+    host = rs.integers(0, 256, size=(L, R * n_pages * page, rb), dtype=np.uint8)
+    perm = rs.permutation(n_blocks)
+    hot = perm[:R * (C // page)].reshape(R, C // page).astype(np.int32)
+    hot[:, 0] = n_blocks + 5                                    # unusable
+    rest = perm[R * (C // page):]
+    bt = np.full((R, n_pages), -1, np.int32)
+    bt[:, n_pages - n_resident:] = rest[:R * n_resident].reshape(R, n_resident)
+    hbt = np.stack([rs.permutation(n_pages) + r * n_pages for r in range(R)]).astype(np.int32)
+    ctx = np.full(R, n_pages * page, np.int32)
+    n_nonres = (n_pages - n_resident) * page
+    tok = np.empty((R, L, C), np.int32)
+    stp = np.full((R, L, C), 0xFFFFFFFF, np.uint32)
+    stp[:, :, :page] = 5
+    stp[:, :, page:2 * page] = 7
+    order = np.empty((R, L, n_nonres), np.int64)
+    for r in range(R):
+        for layer in range(L):
+            order[r, layer] = rs.permutation(n_nonres)
+            tok[r, layer] = order[r, layer, :C]
+    return dict(pool=pool, host=host, bt=bt, hbt=hbt, ctx=ctx, hot=hot, tok=tok, stp=stp), order
+
+
+@pytest.mark.parametrize("mode", stages.MODES)
+@pytest.mark.parametrize("more_misses", [False, True], ids=["fewer_misses", "more_misses"])
+def test_victims_at_the_largest_stamp(more_misses, mode):
+    """The LRU slot of "How it works" is chosen among usable non-hit slots
+    only, whatever their stamps: here every candidate holds the largest
+    stamp, 0xffffffff, while hit slots and an unusable hot block sit at the
+    lowest slot indices.  With fewer misses than candidates every miss gets a
+    slot; with more, the extra misses overflow.  A second call, itself at
+    stamp 0xffffffff, evicts the first call's victims before the rest."""
+    rs = np.random.default_rng(zlib.crc32(f"maxstamp{more_misses}".encode()))
+    page, R, L, C = 64, 2, 2, 512
+    n_pages, n_resident = 40, 10
+    a, order = _max_stamp_instance(rs, R, L, C, page, n_pages, n_resident)
+    case = GpuCase(page, a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"], a["hot"],
+                   a["tok"].copy(), a["stp"].copy(), C)
+    n_fresh = 400 if more_misses else 100
+    P, K = (2, 256) if more_misses else (1, 256)
+    res0 = (n_pages - n_resident) * page
+    try:
+        for step, stamp in enumerate((9, 0xFFFFFFFF)):
+            lists = np.empty((R, L, P * K), np.int32)
+            for r in range(R):
+                for layer in range(L):
+                    o = order[r, layer]
+                    hits = o[page:2 * page]                        # hit slots' tokens
+                    unusable = o[:20]                              # held by unusable slots: misses
+                    fresh = o[C + step * n_fresh:C + (step + 1) * n_fresh]
+                    n_res = P * K - hits.size - unusable.size - fresh.size
+                    resident = rs.integers(res0, n_pages * page, size=n_res)
+                    v = np.concatenate([hits, unusable, fresh, resident])
+                    lists[r, layer] = rs.permutation(v)
+            topk = lists if P == 1 else lists.reshape(R, L, P, K)
+            _say(f"[edges] largest stamp more_misses={more_misses} {mode} step {step}")
+            _, st = _compare(case, a, np.ascontiguousarray(topk), stamp, mode=mode)
+            if step == 0:
+                assert (st[..., 1] == page).all()                 # every hit slot hit
+                m = 20 + n_fresh
+                cand = C - 2 * page
+                assert (st[..., 2] == min(m, cand)).all()
+                assert (st[..., 3] == max(0, m - cand)).all()
+                # no hit slot and no unusable slot was taken
+                assert (a["stp"][:, :, :page] == 5).all()
+                assert (a["stp"][:, :, page:2 * page] == 9).all()
+    finally:
+        case.close()
+
+
+@pytest.mark.parametrize("mode", stages.MODES)
+def test_overflow_at_size(mode):
+    """A 4-position plan of 2048 entries per position over a host-only context:
+    more distinct misses than the 4096 slots hold, so the largest ones
+    overflow (row -2, nothing copied for them), at the workload size."""
+    rs = np.random.default_rng(zlib.crc32(b"overflow_at_size"))
+    page, rb, R, L, P, K, C = 64, 656, 4, 1, 4, 2048, 4096
+    n_pages = 400
+    n_blocks = R * (C // page) + 4
+    pool = rs.integers(0, 256, size=(L, n_blocks * page, rb), dtype=np.uint8)
+    host = rs.integers(0, 256, size=(L, R * n_pages * page, rb), dtype=np.uint8)
+    hot = rs.permutation(n_blocks)[:R * (C // page)].reshape(R, C // page).astype(np.int32)
+    bt = np.full((R, n_pages), -1, np.int32)                     # nothing resident
+    hbt = np.stack([rs.permutation(n_pages) + r * n_pages for r in range(R)]).astype(np.int32)
+    ctx = np.full(R, n_pages * page, np.int32)
+    tok = np.full((R, L, C), -1, np.int32)
+    stp = np.zeros((R, L, C), np.uint32)
+    a = dict(pool=pool, host=host, bt=bt, hbt=hbt, ctx=ctx, hot=hot, tok=tok, stp=stp)
+    case = GpuCase(page, pool, host, bt, hbt, ctx, hot, tok.copy(), stp.copy(), C)
+    try:
+        prev = None
+        for step in range(3):
+            lists = rs.integers(0, n_pages * page, size=(R, L, P, K)).astype(np.int32)
+            if prev is not None:     # half of the first position repeats the last step's
+                lists[:, :, 0, :K // 2] = prev[:, :, 0, :K // 2]
+            prev = lists
+            _say(f"[edges] overflow at size {mode} step {step}")
+            _, st = _compare(case, a, lists, 3 + step, mode=mode)
+            assert (st[..., 3] > 1000).all()
+            assert (st.sum(axis=-1) == P * K).all()
     finally:
         case.close()

@@ -3,9 +3,10 @@
 Every comparison is element by element on the same seeded inputs: row ids,
 stats, hot-buffer tokens and stamps, every byte of the hot-slot rows, every
 gathered byte, and the host pool after each prefix offload.  The five
-workloads run at their full sizes; the two largest (64 x 16 request-layers,
-128 requests x 4 positions) are checked on a sample of requests the oracle
-simulates exactly (request-layers are independent).
+workloads run at their full sizes with every request compared; quicker
+sampled forms of the two largest (64 x 16 request-layers, 128 requests x 4
+positions) add content checks and the staged paths (request-layers are
+independent, so a subset of requests resolves exactly as inside the batch).
 """
 
 from __future__ import annotations
@@ -43,13 +44,25 @@ def _say(msg: str) -> None:
     print(msg, flush=True)
 
 
+def _equal_by_layer(dev_pool, ora_pool, rows=None) -> bool:
+    """Pool planes compared one layer at a time (the largest batches hold
+    tens of GB), optionally only the given rows."""
+    idx = None if rows is None else torch.from_numpy(rows).cuda()
+    for layer in range(ora_pool.shape[0]):
+        d = dev_pool[layer] if idx is None else dev_pool[layer, idx]
+        o = ora_pool[layer] if rows is None else ora_pool[layer, rows]
+        if not np.array_equal(d.cpu().numpy(), o):
+            return False
+    return True
+
+
 def run_parity(wl, requests=None, n_steps=None, hit_replay=False, fused_plan=False,
-               check_content=True, mode="call", gather=True):
+               check_content=True, mode="call", gather=True, threads=8):
     from serving_memory_tier_amd.runner import DeviceRun
 
     dev = DeviceRun(wl)
     dev.upload_steps()
-    ora = OracleRun(wl, requests)
+    ora = OracleRun(wl, requests, content_device="cuda", threads=threads)
     req = torch.from_numpy(ora.req).cuda()
     steps = wl.steps if n_steps is None else wl.steps[:n_steps]
     totals = np.zeros(8, dtype=np.int64)
@@ -81,8 +94,7 @@ def run_parity(wl, requests=None, n_steps=None, hit_replay=False, fused_plan=Fal
                                                               ora.req)), f"content, step {i}"
             # the hot slots' rows (leases can move between steps)
             hot_rows = _hot_rows(ora.hot[ora.hot >= 0])
-            assert np.array_equal(dev.pool[:, torch.from_numpy(hot_rows).cuda()].cpu().numpy(),
-                                  ora.pool[:, hot_rows]), f"hot rows, step {i}"
+            assert _equal_by_layer(dev.pool, ora.pool, hot_rows), f"hot rows, step {i}"
             if hit_replay:
                 # the same lists with the same stamp: every non-resident token
                 # is now a hit, nothing is copied, the state does not move
@@ -107,7 +119,7 @@ def run_parity(wl, requests=None, n_steps=None, hit_replay=False, fused_plan=Fal
                     f"host pool after offload, step {i}"
         torch.cuda.synchronize()
         if requests is None:
-            assert np.array_equal(dev.pool.cpu().numpy(), ora.pool), "final pool"
+            assert _equal_by_layer(dev.pool, ora.pool), "final pool"
             assert np.array_equal(dev.host.numpy(), ora.host), "final host pool"
     finally:
         dev.close()
@@ -135,6 +147,29 @@ def test_no_residency_full():
     totals = run_parity(hs_gen.no_residency())
     _say(f"[parity] no_residency totals {totals.tolist()}")
     assert totals[2] >= 8 * 2048 * 0.99
+
+
+@pytest.mark.timeout(900)
+def test_mixed_state_full():
+    """The mixed-state batch in full: all 128 requests (full, mixed and
+    no residency), 4 positions x 2048 per step resolved as one plan with its
+    gather and the offload of the pages each step completes, 16 steps; the
+    final pool and host pool compared whole."""
+    totals = run_parity(hs_gen.mixed_state(), fused_plan=True, check_content=False, threads=16)
+    _say(f"[parity] mixed_state totals {totals.tolist()}")
+    assert totals[0] > 0 and totals[1] > 0 and totals[2] > 0
+
+
+@pytest.mark.timeout(900)
+def test_multi_layer_full():
+    """The multi-layer batch in full: 64 requests x 16 layers in one launch,
+    13 turns of +753 tokens with the tail moving, and after every turn the
+    offload of the completed pages of all 16 layers in one launch; every
+    request's rows, state and gathered bytes per turn, the host pool after
+    each offload, and the final pool and host pool whole."""
+    totals = run_parity(hs_gen.multi_layer(), check_content=False, threads=16)
+    _say(f"[parity] multi_layer totals {totals.tolist()}")
+    assert totals[0] > 0 and totals[1] > 0 and totals[2] > 0
 
 
 def test_mixed_state_full_sampled():

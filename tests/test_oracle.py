@@ -380,6 +380,30 @@ def test_mixed_decode_reduced_invariants_and_offload():
     assert sum(s.offload.shape[0] for s in wl.steps) == 3
 
 
+@pytest.mark.parametrize("G", [1, 2])
+def test_blocked_oracle_run_equals_whole_batch(G):
+    """The tests' threaded driver of the oracle (blocks of requests on threads
+    of their own, for the full-size batches) gives the whole batch's result:
+    request-layers are independent and their hot blocks disjoint."""
+    spec = hs_gen.Spec(name="blocked", seed=21, R=7, L=2, K=256, C=512, steps=3,
+                       ctx0=np.array([9000, 20000, 5000, 7000, 12000, 3000, 16000]),
+                       classes=np.array([1, 2, 0, 1, 1, 2, 1], np.int8), append=70, P=2, pos_keep=160,
+                       group=G)
+    wl = hs_gen.build(spec)
+    whole, blocked = OracleRun(wl), OracleRun(wl, threads=3)
+    for step in wl.steps:
+        for run in (whole, blocked):
+            run.pre(step)
+        a, b = whole.resolve(step), blocked.resolve(step)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+        for run in (whole, blocked):
+            run.post(step)
+        assert np.array_equal(whole.tok, blocked.tok) and np.array_equal(whole.stp, blocked.stp)
+        assert np.array_equal(whole.pool, blocked.pool)
+        assert np.array_equal(whole.host, blocked.host)
+
+
 def test_plan_equals_resolve_of_concatenation():
     wl = hs_gen.build(hs_gen.Spec(name="plan", seed=11, R=3, L=2, K=128, C=512, steps=3,
                                   ctx0=np.array([9000, 20000, 5000]),
