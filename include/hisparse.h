@@ -338,6 +338,36 @@ hs_status hs_sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
  * needs none, or for non-positive sizes). */
 size_t hs_sparse_mla_workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t top_k);
 
+/*
+ * hs_sparse_mla_decode_noalloc -- hs_sparse_mla_decode for callers that
+ * cannot allocate device memory at all (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation and
+ * results, with the key splits' partial outputs in a workspace the library
+ * holds in device memory instead of a caller buffer.  It calls no
+ * allocating routine of any kind.
+ * Workspace: one array of hs_sparse_mla_noalloc_max_workspace() bytes
+ * (64 MiB) per device, a static part of the library's code object that each
+ * GPU the library runs on holds until the process ends; its device address
+ * is looked up once per device, on the first call that needs it.  Calls whose
+ * hs_sparse_mla_workspace_bytes(num_tokens, num_heads, top_k) exceeds it
+ * return HS_ERR_UNSUPPORTED before enqueuing anything (the decode shape, 32
+ * tokens x 128 heads x 2048 rows, needs about 34 MB).
+ * Concurrency: every call on one device shares that device's array and
+ * overwrites it; calls that overlap in time on one device (other streams,
+ * other threads) race and must be ordered by the caller.  Nothing in the
+ * array needs to start at zero: each call writes every part it reads.
+ * Arguments, precision and other errors: as hs_sparse_mla_decode; a failed
+ * address lookup is HS_ERR_HIP.
+ */
+hs_status hs_sparse_mla_decode_noalloc(const hs_layout* layout, const uint8_t* kv_layer,
+                                       const int32_t* row_ids, int32_t num_tokens,
+                                       int32_t top_k, const uint16_t* q, int32_t num_heads,
+                                       float sm_scale, float* out, float* lse,
+                                       hipStream_t stream);
+
+/* The size of hs_sparse_mla_decode_noalloc's per-device workspace, bytes. */
+size_t hs_sparse_mla_noalloc_max_workspace(void);
+
 /* A static English description of a status code. */
 const char* hs_status_string(hs_status status);
 

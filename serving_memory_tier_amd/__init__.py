@@ -17,8 +17,8 @@ from .api import (HostPool, batch_of, hs_gather, hs_host_alloc, hs_host_device_p
                   hs_host_free, hs_offload_prefix_pages, hs_plan_replay, hs_resolve,
                   hs_resolve_commit, hs_resolve_decide, hs_resolve_fetch, hs_resolve_grouped,
                   hs_resolve_move, hs_page_touch, hs_resolve_in_place, hs_sparse_mla_decode,
-                  hs_sparse_mla_workspace_bytes,
-                  hs_status_string, layout_of)
+                  hs_sparse_mla_workspace_bytes, hs_sparse_mla_decode_noalloc,
+                  hs_sparse_mla_noalloc_max_workspace, hs_status_string, layout_of)
 
 __all__ = [
     "EXPORTS", "HS_OK", "HS_ERR_INVALID_ARGUMENT", "HS_ERR_UNSUPPORTED", "HS_ERR_LAUNCH",
@@ -29,6 +29,6 @@ __all__ = [
     "hs_resolve_fetch",
     "hs_resolve_move", "hs_resolve_commit", "hs_page_touch",
     "hs_resolve_in_place", "hs_sparse_mla_decode", "hs_sparse_mla_workspace_bytes",
-    "hs_status_string", "hs_host_alloc",
+    "hs_sparse_mla_decode_noalloc", "hs_sparse_mla_noalloc_max_workspace", "hs_status_string", "hs_host_alloc",
     "hs_host_free", "hs_host_device_pointer",
 ]

@@ -20,6 +20,7 @@ EXPORTS = ("hs_resolve", "hs_gather", "hs_offload_prefix_pages", "hs_plan_replay
            "hs_resolve_grouped",
            "hs_resolve_decide", "hs_resolve_fetch", "hs_resolve_move", "hs_resolve_commit",
            "hs_page_touch", "hs_resolve_in_place", "hs_sparse_mla_decode", "hs_sparse_mla_workspace_bytes",
+           "hs_sparse_mla_decode_noalloc", "hs_sparse_mla_noalloc_max_workspace",
            "hs_status_string", "hs_last_error", "hs_host_alloc", "hs_host_free",
            "hs_host_device_pointer")
 
@@ -72,6 +73,9 @@ def lib():
         L.hs_sparse_mla_decode.argtypes = [lay, vp, vp, i32, i32, vp, i32, ctypes.c_float, vp,
                                            vp, vp, sz, vp]
         L.hs_sparse_mla_workspace_bytes.argtypes = [i32, i32, i32]
+        L.hs_sparse_mla_decode_noalloc.argtypes = [lay, vp, vp, i32, i32, vp, i32,
+                                                   ctypes.c_float, vp, vp, vp]
+        L.hs_sparse_mla_noalloc_max_workspace.argtypes = []
         L.hs_status_string.argtypes = [i32]
         L.hs_status_string.restype = ctypes.c_char_p
         L.hs_last_error.argtypes = []
@@ -84,5 +88,6 @@ def lib():
                 continue
             getattr(L, name).restype = i32
         L.hs_sparse_mla_workspace_bytes.restype = sz
+        L.hs_sparse_mla_noalloc_max_workspace.restype = sz
         _lib = L
     return _lib

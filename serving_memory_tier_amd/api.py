@@ -164,6 +164,21 @@ def hs_sparse_mla_decode(layout: HsLayout, kv_layer, row_ids, num_tokens: int, t
            "hs_sparse_mla_decode")
 
 
+def hs_sparse_mla_decode_noalloc(layout: HsLayout, kv_layer, row_ids, num_tokens: int,
+                                 top_k: int, q, num_heads: int, sm_scale: float, out, lse,
+                                 stream=None) -> None:
+    """hs_sparse_mla_decode with the library's per-device workspace."""
+    kv = kv_layer if isinstance(kv_layer, int) else _ptr(kv_layer)
+    _check(lib().hs_sparse_mla_decode_noalloc(ctypes.byref(layout), kv, _ptr(row_ids), num_tokens,
+                                              top_k, _ptr(q), num_heads, sm_scale, _ptr(out),
+                                              _ptr(lse), _stream(stream)),
+           "hs_sparse_mla_decode_noalloc")
+
+
+def hs_sparse_mla_noalloc_max_workspace() -> int:
+    return int(lib().hs_sparse_mla_noalloc_max_workspace())
+
+
 def hs_host_alloc(nbytes: int) -> int:
     p = ctypes.c_void_p()
     _check(lib().hs_host_alloc(nbytes, ctypes.byref(p)), "hs_host_alloc")

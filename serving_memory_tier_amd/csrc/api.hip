@@ -440,11 +440,16 @@ size_t hs_sparse_mla_workspace_bytes(int32_t num_tokens, int32_t num_heads, int3
   return ws;
 }
 
-hs_status hs_sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
-                               const int32_t* row_ids, int32_t num_tokens, int32_t top_k,
-                               const uint16_t* q, int32_t num_heads, float sm_scale, float* out,
-                               float* lse, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
+namespace {
+
+// Shared body of hs_sparse_mla_decode and its allocation-free form; with
+// `noalloc` the workspace is the library's per-device array instead of the
+// caller's.
+hs_status sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
+                            const int32_t* row_ids, int32_t num_tokens, int32_t top_k,
+                            const uint16_t* q, int32_t num_heads, float sm_scale, float* out,
+                            float* lse, void* workspace, size_t workspace_bytes, bool noalloc,
+                            hipStream_t stream) {
   hs_status s = check_layout(layout);
   if (s != HS_OK) return s;
   if (layout->row_bytes != 656) return HS_ERR_UNSUPPORTED;
@@ -459,6 +464,13 @@ hs_status hs_sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
     return HS_ERR_INVALID_ARGUMENT;
   size_t need = 0;
   hs::AttendParams p = attend_plan(num_tokens, num_heads, top_k, &need);
+  if (noalloc) {
+    if (need > hs::kAttendScratchBytes) return HS_ERR_UNSUPPORTED;
+    workspace = nullptr;
+    if (need > 0 && !hip_ok(hs::attend_scratch(&workspace), "workspace symbol lookup"))
+      return HS_ERR_HIP;
+    workspace_bytes = hs::kAttendScratchBytes;
+  }
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return HS_ERR_INVALID_ARGUMENT;
   p.kv = kv_layer;
@@ -472,6 +484,28 @@ hs_status hs_sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
   p.part_ml = need > 0 ? p.part_o + (size_t)num_tokens * p.splits * num_heads * 512 : nullptr;
   return from_hip(hs::launch_attend(p, stream), "sparse MLA launch");
 }
+
+}  // namespace
+
+hs_status hs_sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
+                               const int32_t* row_ids, int32_t num_tokens, int32_t top_k,
+                               const uint16_t* q, int32_t num_heads, float sm_scale, float* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return sparse_mla_decode(layout, kv_layer, row_ids, num_tokens, top_k, q, num_heads, sm_scale,
+                           out, lse, workspace, workspace_bytes, false, stream);
+}
+
+hs_status hs_sparse_mla_decode_noalloc(const hs_layout* layout, const uint8_t* kv_layer,
+                                       const int32_t* row_ids, int32_t num_tokens,
+                                       int32_t top_k, const uint16_t* q, int32_t num_heads,
+                                       float sm_scale, float* out, float* lse,
+                                       hipStream_t stream) {
+  return sparse_mla_decode(layout, kv_layer, row_ids, num_tokens, top_k, q, num_heads, sm_scale,
+                           out, lse, nullptr, 0, true, stream);
+}
+
+size_t hs_sparse_mla_noalloc_max_workspace(void) { return hs::kAttendScratchBytes; }
 
 const char* hs_last_error(void) { return g_last_error; }
 

@@ -32,6 +32,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "hs_internal.h"
 
@@ -360,7 +361,33 @@ __global__ void __launch_bounds__(128) attend_combine_kernel(AttendParams p) {
   if (threadIdx.x == 0) p.lse[th] = L > 0.f ? (M + log2f(L)) / kLog2e : -INFINITY;
 }
 
+// The workspace of the allocation-free entry point: one array per device
+// that holds the key splits' partial outputs of whichever call runs, kept
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it only names the symbol); the device address comes
+// from hipGetSymbolAddress, once per device, on that device.
+static __device__ __align__(256) unsigned char scratch[kAttendScratchBytes];
+
 }  // namespace
+
+hipError_t attend_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t attend_lds_bytes() { return sizeof(AttendLds); }
 

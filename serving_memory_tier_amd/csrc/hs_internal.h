@@ -281,6 +281,12 @@ struct AttendParams {
   int32_t keys_per_split;   // a multiple of 32
 };
 
+// Bytes of the per-device workspace of hs_sparse_mla_decode_noalloc.
+constexpr size_t kAttendScratchBytes = size_t(64) << 20;
+// That workspace's device address on the current device (looked up once per
+// device; no allocation).
+hipError_t attend_scratch(void** ptr);
+
 size_t attend_lds_bytes();
 // Sets splits and keys_per_split for about target_groups workgroups.
 void plan_attend(AttendParams& p, int64_t target_groups);

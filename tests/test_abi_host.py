@@ -217,3 +217,22 @@ def test_sparse_mla_rejects(lib):
     assert f(lay, P, P, 1, 64 * 2048 + 1, P, 16, P, P, P, 1 << 40) == 2   # top_k over the bound
     assert f(lay, P, P, 0, 64, None, 16, None, None, None, 0) == 0   # nothing to do
     assert lib.hs_sparse_mla_workspace_bytes(0, 16, 64) == 0
+
+
+def test_sparse_mla_noalloc_rejects(lib):
+    """The allocation-free form checks like hs_sparse_mla_decode and refuses,
+    before any GPU work, sizes whose workspace exceeds its per-device array."""
+    lay = _layout()
+    P = 0x1000
+    f = lambda lay_, kv, ids, T, K, q, H, out, lse: lib.hs_sparse_mla_decode_noalloc(
+        ctypes.byref(lay_), kv, ids, T, K, q, H, 0.1, out, lse, None)
+    cap = lib.hs_sparse_mla_noalloc_max_workspace()
+    assert cap == hs.hs_sparse_mla_noalloc_max_workspace() == 64 << 20
+    assert lib.hs_sparse_mla_workspace_bytes(32, 128, 2048) <= cap    # the decode shape fits
+    assert lib.hs_sparse_mla_workspace_bytes(16, 128, 131072) > cap  # 64 key splits
+    assert f(lay, P, P, 16, 131072, P, 128, P, P) == 2               # beyond the array
+    assert f(_layout(row_bytes=512), P, P, 1, 64, P, 16, P, P) == 2
+    assert f(lay, P, P, 1, 64, P, 24, P, P) == 1
+    assert f(lay, None, P, 1, 64, P, 16, P, P) == 1
+    assert f(lay, P, P, 1, 64, P + 4, 16, P, P) == 1
+    assert f(lay, P, P, 0, 64, None, 16, None, None) == 0            # nothing to do
