@@ -33,20 +33,46 @@ def build_policy() -> str:
     return POLICY_LIB
 
 
-def build(verbose: bool = False) -> str:
-    build_policy()
-    out = os.path.join(HERE, "libhisparse.so")
-    tmp = out + ".tmp"
-    cmd = (["hipcc"] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp] +
-           [os.path.join(HERE, "csrc", s) for s in SOURCES])
-    res = subprocess.run(cmd, capture_output=True, text=True)
+PROBE_SRC = "probe.hip"
+PROBE_LIB = os.path.join(HERE, "libhs_probe.so")
+
+
+def _hipcc(args, what):
+    res = subprocess.run(["hipcc"] + args, capture_output=True, text=True)
     noise = "packed-fp32-ops' is not a recognized feature"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+        raise RuntimeError(f"hipcc failed ({what}):\n" + "\n".join(msgs))
+    return msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source to an object (in parallel), links the library,
+    and builds the measurement library beside it."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    build_policy()
+    out = os.path.join(HERE, "libhisparse.so")
+    tmp = out + ".tmp"
+    inc = ["-I", os.path.join(ROOT, "include")]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="hs_build_") as objdir:
+        def compile_one(src):
+            obj = os.path.join(objdir, src.replace(".hip", ".o"))
+            return _hipcc(compile_flags + inc + ["-c", os.path.join(HERE, "csrc", src), "-o", obj],
+                          src), obj
+        jobs = min(len(SOURCES) + 1, max(1, os.cpu_count() or 1))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(compile_one, SOURCES + [PROBE_SRC]))
+        msgs = [m for r in results for m in r[0]]
+        objs = [r[1] for r in results]
+        msgs += _hipcc(FLAGS + ["-o", tmp] + objs[:-1], "link")
+        msgs += _hipcc(FLAGS + ["-o", PROBE_LIB + ".tmp", objs[-1]], "link probe")
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, out)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return out
 
 
