@@ -603,7 +603,19 @@ def probe_ceilings(hev, stream: int, busy):
     d0 = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     d1 = torch.empty_like(d0)
     d0.fill_(1)
-    hbm = best(lambda: d1.copy_(d0), 2 << 30)
+    torch_copy = best(lambda: d1.copy_(d0), 2 << 30)
+    # a plain streaming-copy kernel (libhs_probe.so), its best launch shape
+    probe = _probe_lib()
+    kern, kern_shape = 0.0, None
+    for variant, grid in ((1, 256), (0, 256), (2, 256), (3, 4096), (1, 512)):
+        rc = []
+        r = best(lambda: rc.append(probe.hs_probe_copy(d0.data_ptr(), d1.data_ptr(), 1 << 30,
+                                                       grid, variant, stream)), 2 << 30)
+        assert all(x == 0 for x in rc), "copy probe launch failed"
+        if r > kern:
+            kern, kern_shape = r, f"variant {variant}, {grid} workgroups of 256"
+    assert torch.equal(d0[:1 << 20], d1[:1 << 20])
+    hbm = max(torch_copy, kern)
     del d0, d1
     h = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
     d = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -611,9 +623,25 @@ def probe_ceilings(hev, stream: int, busy):
     d2h = best(lambda: h.copy_(d, non_blocking=True), 256 << 20)
     torch.cuda.synchronize()
     del h, d
-    return {"hbm_copy_gbps": round(hbm, 1), "host_to_device_dma_gbps": round(h2d, 2),
+    return {"hbm_copy_gbps": round(hbm, 1), "hbm_copy_kernel_gbps": round(kern, 1),
+            "hbm_copy_kernel_shape": kern_shape, "torch_copy_gbps": round(torch_copy, 1),
+            "host_to_device_dma_gbps": round(h2d, 2),
             "device_to_host_dma_gbps": round(d2h, 2),
-            "note": "read + write bytes of a 1 GiB device copy; 256 MiB pinned-host DMA each way"}
+            "note": "read + write bytes of a 1 GiB device copy, the better of a plain streaming "
+                    "copy kernel and torch's copy; 256 MiB pinned-host DMA each way"}
+
+
+def _probe_lib():
+    """The measurement library built beside the hot-path library."""
+    import ctypes
+    from serving_memory_tier_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        raise RuntimeError(f"{build.PROBE_LIB} is missing; build with __graft_entry__.build()")
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    lib.hs_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.hs_probe_copy.restype = ctypes.c_int
+    return lib
 
 
 def touch_cost(wl, dev, hev, stream: int, i: int, n: int, busy=None):
@@ -626,16 +654,27 @@ def touch_cost(wl, dev, hev, stream: int, i: int, n: int, busy=None):
     from serving_memory_tier_amd import hs_page_touch
     use = torch.zeros((wl.R, wl.max_pages), dtype=torch.int32, device="cuda")
     E = wl.NG * wl.P * wl.K
-    # a launch takes a few microseconds, less than an event pair's own cost:
-    # time n launches back to back between one pair
+    # a launch takes a few microseconds, less than an event pair's own cost
+    # and less than the host's enqueue of one call: the n launches are
+    # captured once and the graph's replay is timed between one event pair
+    cap = torch.cuda.Stream()
+    hev.begin_capture(cap.cuda_stream)
+    try:
+        for j in range(n):
+            hs_page_touch(dev.layout, dev.batches[i], dev.topk[i], E, wl.steps[i].stamp, use,
+                          cap.cuda_stream)
+    finally:
+        hev.end_capture(cap.cuda_stream)
     a, b = hev.new_event(), hev.new_event()
+    hev.launch(stream)                    # warm replay
+    torch.cuda.synchronize()
     if busy is not None:
         busy.fill()
     hev.record(a, stream)
-    for j in range(n):
-        hs_page_touch(dev.layout, dev.batches[i], dev.topk[i], E, wl.steps[i].stamp, use, stream)
+    hev.launch(stream)
     hev.record(b, stream)
     torch.cuda.synchronize()
+    hev.destroy_graph()
     us = 1e3 * hev.elapsed_ms(a, b) / n
     pages = int((use != 0).sum().item())
     nbytes = wl.R * E * 4 + pages * 4

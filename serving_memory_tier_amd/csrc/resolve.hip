@@ -741,7 +741,6 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
       uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
       for (int j = 0; j < EC; ++j) {
-        const int q = j * kThreads + tid;
         predC[j] = ((candm >> j) & 1u) != 0;
         if (predC[j]) {
           mn = min(mn, cst[j]);

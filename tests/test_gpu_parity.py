@@ -244,6 +244,45 @@ def test_determinism_repeat():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("block", [1, 5, 8])
+def test_launch_shape_independence(block):
+    """No byte depends on the launch shape: the fused launch sizes its gather
+    workgroups (and so every gather range) from the request-layers it holds
+    and the chip's occupancy.  The same mixed-decode steps resolved as one
+    batch of 32 requests and as consecutive sub-batches of ``block``
+    requests (leading slices of the same tables, state and outputs, so every
+    launch has another shape) give identical rows, stats, gathered bytes,
+    state and pool, step after step, hit replays included."""
+    import serving_memory_tier_amd as hs
+    from serving_memory_tier_amd.runner import DeviceRun
+
+    wl = hs_gen.mixed_decode(steps=5)
+    a, b = DeviceRun(wl), DeviceRun(wl)
+    try:
+        for d in (a, b):
+            d.upload_steps()
+        for i, step in enumerate(wl.steps):
+            _say(f"[parity] launch shapes, block {block}, step {i}")
+            for stamp in (step.stamp, step.stamp):         # the step, then its hit replay
+                a.pre(i)
+                a.resolve(i, stamp=stamp)
+                b.pre(i)
+                for r0 in range(0, wl.R, block):
+                    r1 = min(wl.R, r0 + block)
+                    sub = hs.batch_of(r1 - r0, wl.max_pages, b.pool, b.host_pool, b.bt[r0:r1],
+                                      b.hbt[r0:r1], b.ctx[r0:r1], b.hot[r0:r1], b.tok[r0:r1],
+                                      b.stp[r0:r1])
+                    hs.hs_resolve(b.layout, sub, b.topk[i][r0:r1], wl.K, stamp, b.rows[r0:r1],
+                                  b.out[r0:r1], b.stats[r0:r1])
+                torch.cuda.synchronize()
+                for x, y in ((a.rows, b.rows), (a.stats, b.stats), (a.tok, b.tok),
+                             (a.stp, b.stp), (a.out, b.out), (a.pool, b.pool)):
+                    assert torch.equal(x, y), f"step {i}"
+    finally:
+        a.close()
+        b.close()
+
+
 @pytest.mark.parametrize("group", [1, 2])
 def test_policy_driven_small(group):
     """Residency decided step by step by the host policy: blocks freed by
