@@ -10,8 +10,10 @@
 // scaled latent values (512).
 //
 // Work split: one workgroup of 8 waves per (query token, 64 heads, key
-// split).  Per block of 32 selected rows the workgroup loads the rows by id
-// (one block ahead, into registers), converts the latent bytes exactly to
+// split); the two head groups of a (token, split) run side by side on one
+// XCD, so each selected row comes from HBM about once.  Per block of 32
+// selected rows the workgroup loads the rows by id (one block ahead, into
+// registers), converts the latent bytes exactly to
 // bfloat16 (FP8 E4M3 fits bfloat16) into LDS twice -- key-major for the
 // scores, dimension-major for the values -- and wave w takes 16 heads (w & 3)
 // and one half (w >> 2), which picks its 16 keys for the scores and its 256
@@ -176,7 +178,15 @@ __device__ __forceinline__ void store_block(AttendLds& s, const BlockRegs& b) {
 __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   AttendLds& s = *reinterpret_cast<AttendLds*>(lds_raw);
-  const int split = blockIdx.x, hg = blockIdx.y, t = blockIdx.z;
+  // workgroup -> (token, split, head group): the head groups of one (token,
+  // split) are 8 workgroups apart -- the XCD stride -- and dispatched
+  // together, so the rows one of them fetches are in that XCD's L2 when the
+  // other reads them
+  const int32_t L = blockIdx.x;
+  const int hg = (L >> 3) % p.head_groups;
+  const int32_t pair = (L / (8 * p.head_groups)) * 8 + (L & 7);
+  if (pair >= p.num_tokens * p.splits) return;   // the grid's rounding: the whole workgroup
+  const int t = pair % p.num_tokens, split = pair / p.num_tokens;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 15, g = l >> 4;
   const int ht = w & 3, half = w >> 2;
@@ -403,6 +413,7 @@ void plan_attend(AttendParams& p, int64_t target_groups) {
   if (s > kAttendMaxSplits) s = kAttendMaxSplits;   // top_k is validated against this bound
   if (s < 1) s = 1;
   const int32_t per = (int32_t)(((blocks + s - 1) / s) * kBlockKeys);
+  p.head_groups = hg;
   p.keys_per_split = per;
   p.splits = per > 0 ? (p.top_k + per - 1) / per : 1;
   if (p.splits < 1) p.splits = 1;
@@ -415,9 +426,11 @@ hipError_t launch_attend(const AttendParams& p, hipStream_t stream) {
   static std::atomic<uint64_t> raised{0};
   hipError_t e = allow_full_lds(reinterpret_cast<const void*>(fn), raised);
   if (e != hipSuccess) return e;
-  const uint32_t hg = (uint32_t)((p.num_heads + kAttendHeadsPerGroup - 1) / kAttendHeadsPerGroup);
-  e = launch_kernel(fn, dim3((uint32_t)p.splits, hg, (uint32_t)p.num_tokens), dim3(kT),
-                    sizeof(AttendLds), stream, p);
+  // (token, split) pairs in rounds of 8, each round once per head group
+  const int64_t pairs = (int64_t)p.num_tokens * p.splits;
+  const int64_t grid = (pairs + 7) / 8 * 8 * p.head_groups;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  e = launch_kernel(fn, dim3((uint32_t)grid), dim3(kT), sizeof(AttendLds), stream, p);
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_kernel(attend_combine_kernel, dim3((uint32_t)p.num_heads, (uint32_t)p.num_tokens),
                        dim3(128), 0, stream, p);

@@ -279,6 +279,7 @@ struct AttendParams {
   float* part_ml;           // workspace: [tokens][splits][heads][2]
   int32_t splits;
   int32_t keys_per_split;   // a multiple of 32
+  int32_t head_groups;      // ceil(num_heads / kAttendHeadsPerGroup)
 };
 
 // Bytes of the per-device workspace of hs_sparse_mla_decode_noalloc.
