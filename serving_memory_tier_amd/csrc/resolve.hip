@@ -8,11 +8,14 @@
 // on a miss, dotted = reuse without copy); section "Integration with the rest
 // of vLLM" (a per-step replayable plan shares the request's hot state).
 //
-// One workgroup (8 wave64s) decides one request-layer; the row movement --
-// the host-link copies of the misses and the gather -- is left to the wide
-// streaming kernel in copy.hip, which runs next on the same stream, so that
-// the host link and HBM are driven by the whole chip instead of one CU per
-// request-layer.  Phases:
+// One workgroup (16 wave64s, 1024 threads) decides one request-layer.  The
+// row movement is not done here: with a gather output the same launch also
+// carries the early fill's workgroups (fill.h: every output row, the misses'
+// host-link reads included, written from the pre-call state while this
+// decides), and the commit kernel in copy.hip then copies each assigned
+// miss's row into its slot; without one, the row mover in copy.hip runs
+// next on the same stream.  Either way the host link and HBM are driven by
+// the whole chip instead of one CU per request-layer.  Phases:
 //   A  load the N top-K entries in sort layout, classify each (pad / invalid
 //      / resident / non-resident), write the final row of every entry that
 //      does not need the hot buffer;
