@@ -219,6 +219,8 @@ def main():
             print(f"[bench] graph capture failed ({exc}); timing eager launches",
                   file=sys.stderr, flush=True)
             graph = False
+    if graph:
+        hev.upload(cap.cuda_stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if graph:
@@ -331,6 +333,9 @@ def main():
                 dev.launch_step(last, hev, cap.cuda_stream, stats=rep_stats, offload=False)
         finally:
             hev.end_capture(cap.cuda_stream)
+        torch.cuda.synchronize()
+        # one untimed launch first: a graph's first launch also uploads it
+        hev.launch(cap.cuda_stream)
         torch.cuda.synchronize()
         t2 = time.perf_counter()
         hev.launch(cap.cuda_stream)

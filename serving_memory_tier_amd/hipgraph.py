@@ -39,6 +39,7 @@ class HipRuntime:
         hip.hipGraphInstantiate.argtypes = [ct.POINTER(ct.c_void_p), ct.c_void_p, ct.c_void_p,
                                             ct.c_void_p, ct.c_size_t]
         hip.hipGraphLaunch.argtypes = [ct.c_void_p, ct.c_void_p]
+        hip.hipGraphUpload.argtypes = [ct.c_void_p, ct.c_void_p]
         hip.hipGraphExecDestroy.argtypes = [ct.c_void_p]
         hip.hipGraphDestroy.argtypes = [ct.c_void_p]
         hip.hipMemcpyAsync.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_size_t, ct.c_int,
@@ -87,6 +88,12 @@ class HipRuntime:
             self.hip.hipGraphDestroy(g)
             raise RuntimeError("hipGraphInstantiate failed")
         self.graph, self.exec = g, ge
+
+    def upload(self, stream: int) -> None:
+        """Move the graph's launch resources to the device ahead of its first
+        launch, which otherwise pays for that itself."""
+        if self.hip.hipGraphUpload(self.exec, self.ct.c_void_p(stream)) != 0:
+            raise RuntimeError("hipGraphUpload failed")
 
     def launch(self, stream: int) -> None:
         if self.hip.hipGraphLaunch(self.exec, self.ct.c_void_p(stream)) != 0:
