@@ -11,22 +11,26 @@
 //
 // Work split: one workgroup of 8 waves per (query token, 64 heads, key
 // split); the two head groups of a (token, split) run side by side on one
-// XCD, so each selected row comes from HBM about once.  Per block of 32
-// selected rows the workgroup loads the rows by id (one block ahead, into
-// registers), converts the latent bytes exactly to
-// bfloat16 (FP8 E4M3 fits bfloat16) into LDS twice -- key-major for the
-// scores, dimension-major for the values -- and wave w takes 16 heads (w & 3)
-// and one half (w >> 2), which picks its 16 keys for the scores and its 256
-// value dimensions:
-//   S^T (16 keys x 16 heads) = K Q^T with 16x16x32 bf16 MFMAs, one
-//     accumulator per 128-value latent tile and one for the rope, so the
-//     per-row scales are applied in float32 after the products; the two
-//     halves swap their scores through LDS;
+// XCD, so each selected row comes from HBM about once.  Blocks of 32
+// selected rows stream through LDS as they are in the pool (FP8 latent
+// bytes, scales, bf16 rope), three blocks resident: the block computed, the
+// next one being stored from registers, and the one before, which every wave
+// is done with; the block after next is loaded by row id into registers.
+// One barrier a block.  Wave w takes 16 heads (w & 3) and one half (w >> 2),
+// which picks its 16 keys for the scores and its 256 value dimensions:
+//   S^T (16 keys x 16 heads) = K Q^T with 16x16x32 bf16 MFMAs, the key
+//     operand read from LDS as FP8 and converted exactly to bf16 (every E4M3
+//     value is a bf16 value), one accumulator per 128-value latent tile and
+//     one for the rope, so the per-row scales are applied in float32 after
+//     the products; the two halves swap their scores through LDS;
 //   online softmax per head over the 32 keys (each lane owns one head column);
 //   O^T (256 dims x 16 heads) += V^T P'^T, where P' = p * scale of the latent
-//     tile: the probabilities are the B operand straight from registers.
-// Half the value dimensions per wave keep a wave under 256 registers, so two
-// waves share each SIMD.
+//     tile: the probabilities are the B operand straight from registers, and
+//     the value operand comes from the row-major block through the
+//     transposing LDS read (ds_read_b64_tr_b8), converted to bf16 likewise.
+// Reading FP8 from LDS and converting per use halves the LDS bytes against
+// converting once into bf16 copies; half the value dimensions per wave keep
+// a wave under 256 registers, so two waves share each SIMD.
 // Key splits write unnormalised partial outputs with their running max and
 // sum to the caller's workspace; a combine kernel merges them.
 
@@ -56,10 +60,7 @@ constexpr int kRope = 64;
 constexpr int kDim = kLatent + kRope;       // 576
 constexpr int kRowBytes = 656;
 constexpr int kPieces = kRowBytes / 16;     // 41
-constexpr int kKdStride = kDim + 8;         // bf16 per key row in LDS (padded)
-constexpr int kVtStride = kBlockKeys + 4;   // bf16 per dimension row in LDS (padded: the
-                                            // transposing writes and the value reads spread
-                                            // over the banks, 8-byte aligned)
+constexpr int kBufs = 3;                    // blocks resident in LDS: computed, stored, free
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kStaleMax = 8.f;            // log2 of the largest unnormalised probability
 
@@ -68,13 +69,19 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
+// A block's rows as they are in the pool, 656 bytes each; key k of the
+// block sits in row slot(k), which spreads both the key-fragment reads and the
+// transposing value reads over distinct banks.
+struct AttendBlock {
+  uint8_t rows[kBlockKeys * kRowBytes];
+};
+
+__device__ __forceinline__ int slot(int k) { return k ^ ((k >> 4) << 3); }
+
 struct AttendLds {
-  uint16_t kd[kBlockKeys * kKdStride];      // keys, key-major, bf16 bits
-  uint16_t vt[kLatent * kVtStride];         // latent values, dimension-major
-  float scale[kBlockKeys][4];
-  int32_t valid[kBlockKeys];
+  AttendBlock blk[kBufs];
   int32_t ids[kAttendMaxSplitKeys];         // the split's row ids, -1 where nothing is selected
-  float xs[4][kBlockKeys][16];              // scores per (head tile, key, head) for the exchange
+  float xs[2][4][kBlockKeys][16];           // scores per (head tile, key, head) for the exchange
 };
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -86,20 +93,36 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// A block's rows are moved in pairs (rows 2 jp and 2 jp + 1, the same
-// 16-byte piece pc of both), 16 pairs x 41 pieces over the workgroup: the
-// loads are issued for the next block before the current one is computed.
-constexpr int kPairPieces = (kBlockKeys / 2) * kPieces;          // 656
-constexpr int kFetchRounds = (kPairPieces + kT - 1) / kT;        // 2
+// ds_read_b64_tr_b8: within each group of 16 lanes, lane c receives byte
+// c % 8 of the 8-byte vectors at the addresses of lanes 2 j + c / 8 of its
+// group, j = 0..7 (an 8-byte-aligned LDS address a lane).
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+__device__ __forceinline__ u32x2 tr8_read(const uint8_t* p) {
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(const_cast<uint8_t*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Eight FP8 E4M3 bytes to eight bf16, exactly, in byte order.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 w) {
+  return __builtin_bit_cast(bf16x8, u32x4{fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
+                                          fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])});
+}
+
+// A block's rows are moved one 16-byte piece a thread (41 consecutive
+// threads read one row): the loads are issued two blocks ahead of the
+// block computed, into registers, and stored one block ahead.
+constexpr int kBlockPieces = kBlockKeys * kPieces;                // 1312
+constexpr int kFetchRounds = (kBlockPieces + kT - 1) / kT;        // 3
 
 struct BlockRegs {
-  u32x4 v[kFetchRounds][2];
-  int32_t id[kFetchRounds][2];
+  u32x4 v[kFetchRounds];
+  int32_t id[kFetchRounds];
 };
 
 // Global loads of the rows of keys [k0, k0 + 32) of the split (row ids from
 // LDS) into registers.  Loads are unconditional where the pool has rows (an
-// unselected key reads row 0 and is masked when stored), so nothing waits
+// unselected key reads row 0 and is stored as zeros), so nothing waits
 // between issuing them.
 __device__ __forceinline__ void fetch_block(const AttendParams& p, const AttendLds& s,
                                             int32_t k0, BlockRegs& b) {
@@ -107,67 +130,27 @@ __device__ __forceinline__ void fetch_block(const AttendParams& p, const AttendL
 #pragma unroll
   for (int i = 0; i < kFetchRounds; ++i) {
     const int q = tid + kT * i;
-    const int jp = q & 15, pc = q >> 4;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int32_t id = q < kPairPieces ? s.ids[k0 + 2 * jp + h] : -1;
-      b.id[i][h] = id;
-      if (p.pool_rows > 0 && q < kPairPieces)
-        b.v[i][h] = *reinterpret_cast<const u32x4*>(p.kv + (int64_t)(id >= 0 ? id : 0) * kRowBytes +
-                                                    pc * 16);
-      else
-        b.v[i][h] = u32x4{0u, 0u, 0u, 0u};
-    }
+    const int k = q / kPieces, pc = q - k * kPieces;
+    const int32_t id = q < kBlockPieces ? s.ids[k0 + k] : -1;
+    b.id[i] = id;
+    if (p.pool_rows > 0 && q < kBlockPieces)
+      b.v[i] = *reinterpret_cast<const u32x4*>(p.kv + (int64_t)(id >= 0 ? id : 0) * kRowBytes +
+                                               pc * 16);
+    else
+      b.v[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-// The fetched rows into LDS: latent values converted exactly to bf16, key-major
-// and dimension-major; scales; rope values; which keys are selected.
-__device__ __forceinline__ void store_block(AttendLds& s, const BlockRegs& b) {
+// The fetched rows into an LDS block as they are (zeros for unselected keys).
+__device__ __forceinline__ void store_block(AttendBlock& s, const BlockRegs& b) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kFetchRounds; ++i) {
     const int q = tid + kT * i;
-    if (q >= kPairPieces) continue;
-    const int jp = q & 15, pc = q >> 4;
-    const int j0 = 2 * jp;
-    if (pc == 0) {
-      s.valid[j0] = b.id[i][0];
-      s.valid[j0 + 1] = b.id[i][1];
-    }
-    u32x4 v[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) v[h] = b.id[i][h] >= 0 ? b.v[i][h] : u32x4{0u, 0u, 0u, 0u};
-    if (pc < kLatent / 16) {
-      uint32_t w[2][8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[h][2 * e] = fp8x2_to_bf16x2<false>(v[h][e]);
-          w[h][2 * e + 1] = fp8x2_to_bf16x2<true>(v[h][e]);
-        }
-        uint16_t* kd = s.kd + (j0 + h) * kKdStride + pc * 16;
-        *reinterpret_cast<u32x4*>(kd) = u32x4{w[h][0], w[h][1], w[h][2], w[h][3]};
-        *reinterpret_cast<u32x4*>(kd + 8) = u32x4{w[h][4], w[h][5], w[h][6], w[h][7]};
-      }
-      // dimension-major: one word holds the dimension of both rows (the low
-      // or high halves of the two rows' words, one byte permute)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        *reinterpret_cast<uint32_t*>(s.vt + (pc * 16 + 2 * k) * kVtStride + j0) =
-            __builtin_amdgcn_perm(w[1][k], w[0][k], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(s.vt + (pc * 16 + 2 * k + 1) * kVtStride + j0) =
-            __builtin_amdgcn_perm(w[1][k], w[0][k], 0x07060302u);
-      }
-    } else if (pc == kLatent / 16) {
-      *reinterpret_cast<u32x4*>(&s.scale[j0][0]) = v[0];       // four float32 scales
-      *reinterpret_cast<u32x4*>(&s.scale[j0 + 1][0]) = v[1];
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)                                     // rope
-        *reinterpret_cast<u32x4*>(s.kd + (j0 + h) * kKdStride + kLatent + (pc - 33) * 8) = v[h];
-    }
+    if (q >= kBlockPieces) continue;
+    const int k = q / kPieces, pc = q - k * kPieces;
+    *reinterpret_cast<u32x4*>(s.rows + slot(k) * kRowBytes + pc * 16) =
+        b.id[i] >= 0 ? b.v[i] : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -220,21 +203,32 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
   }
   __syncthreads();
   HS_ATTEND_DECL;
+  const int32_t nblk = n_pad / kBlockKeys;
   BlockRegs regs;
-  if (n_keys > 0) fetch_block(p, s, 0, regs);
-  for (int32_t key0 = key_lo; key0 < key_end; key0 += kBlockKeys) {
+  if (nblk > 0) {
+    fetch_block(p, s, 0, regs);
+    store_block(s.blk[0], regs);
+    if (nblk > 1) fetch_block(p, s, kBlockKeys, regs);
+  }
+  __syncthreads();
+  // Block i is computed from buffer i % 3 while block i + 1 is stored into
+  // buffer (i + 1) % 3 and block i + 2 is loaded into registers.  One barrier
+  // a block: past it, block i's scores and block i + 1's rows are complete,
+  // and every wave is done with block i - 1, whose buffer is stored next.
+  int cur = 0;
+  for (int32_t bi = 0; bi < nblk; ++bi) {
     HS_ATTEND_MARK(0);
-    store_block(s, regs);
-    __syncthreads();
-    HS_ATTEND_MARK(1);
-    // the next block's loads are in flight while this one is computed
-    if (key0 + kBlockKeys < key_end) fetch_block(p, s, key0 + kBlockKeys - key_lo, regs);
+    const AttendBlock& cb = s.blk[cur];
+    const int nxt = cur == kBufs - 1 ? 0 : cur + 1;
+    float (*xs)[kBlockKeys][16] = s.xs[bi & 1];
     // ---- scores of this wave's key tile: S^T[key 16 half + ..][head]
     {
       f32x4 acc[5];
 #pragma unroll
       for (int tl = 0; tl < 5; ++tl) acc[tl] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = s.kd + (half * 16 + col) * kKdStride + 8 * g;
+      // key half * 16 + col: latent bytes 128 tl + 32 kk + 8 g .. converted
+      // to bf16, rope values 32 kk + 8 g .. as they are
+      const uint8_t* krow = cb.rows + slot(half * 16 + col) * kRowBytes;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int nt = kk < 2 ? 5 : 4;
@@ -242,8 +236,10 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
 #pragma unroll
         for (int tl = 0; tl < 5; ++tl)
           if (tl < nt)
-            ka[tl] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(krow + (tl * 4 + kk) * 32));
+            ka[tl] = tl < 4 ? fp8x8_to_bf16x8(*reinterpret_cast<const u32x2*>(
+                                  krow + tl * 128 + kk * 32 + 8 * g))
+                            : __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                  krow + kLatent + 16 + kk * 64 + 16 * g));
 #pragma unroll
         for (int tl = 0; tl < 5; ++tl)
           if (tl < nt)
@@ -253,20 +249,28 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = half * 16 + 4 * g + r;
+        const f32x4 sc4 = *reinterpret_cast<const f32x4*>(cb.rows + slot(key) * kRowBytes + kLatent);
         float v = acc[4][r];
 #pragma unroll
-        for (int tl = 0; tl < 4; ++tl) v += s.scale[key][tl] * acc[tl][r];
-        s.xs[ht][key][col] = s.valid[key] >= 0 ? v * qk_scale : -INFINITY;
+        for (int tl = 0; tl < 4; ++tl) v += sc4[tl] * acc[tl][r];
+        xs[ht][key][col] = s.ids[bi * kBlockKeys + key] >= 0 ? v * qk_scale : -INFINITY;
       }
     }
-    __syncthreads();   // both key tiles' scores are in LDS
+    HS_ATTEND_MARK(1);
+    // ---- the next block into the next buffer, the one after into registers
+    if (bi + 1 < nblk) {
+      store_block(s.blk[nxt], regs);
+      if (bi + 2 < nblk) fetch_block(p, s, (bi + 2) * kBlockKeys, regs);
+    }
     HS_ATTEND_MARK(2);
+    __syncthreads();
+    HS_ATTEND_MARK(3);
     // ---- online softmax over the block's 32 keys (both halves alike)
     float sc[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[mt][r] = s.xs[ht][mt * 16 + 4 * g + r][col];
+      for (int r = 0; r < 4; ++r) sc[mt][r] = xs[ht][mt * 16 + 4 * g + r][col];
     float mb = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -295,7 +299,11 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) o[dt] *= alpha;
     }
-    // ---- O^T += V^T P'^T for this wave's two latent tiles
+    // ---- O^T += V^T P'^T for this wave's two latent tiles.  The value
+    // operand is read transposed from the key-major rows: in each 16-lane
+    // group g, lane c supplies the address of key 4 g + c / 4 (and 16 more),
+    // dimensions 4 (c % 4) ..; the transposing read hands lane c dimension c
+    // of keys 4 g .. 4 g + 3
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int tl = half * 2 + t2;
@@ -304,22 +312,25 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          b[4 * mt + r] = (__bf16)(pr[mt][r] * s.scale[mt * 16 + 4 * g + r][tl]);
+          b[4 * mt + r] = (__bf16)(pr[mt][r] * *reinterpret_cast<const float*>(
+                                        cb.rows + slot(mt * 16 + 4 * g + r) * kRowBytes +
+                                        kLatent + 4 * tl));
       bf16x8 va[8];
+      // lane c of group g supplies key kv(c / 2) (4 g + j, then 16 + 4 g + j)
+      // at dimensions 8 (c % 2) ..; the transposing read hands lane c
+      // dimension c of the group's eight keys
+      const int j = col >> 1;
+      const int kv = (j < 4 ? 0 : 12) + 4 * g + j;
+      const uint8_t* vbase = cb.rows + slot(kv) * kRowBytes + 8 * (col & 1);
 #pragma unroll
-      for (int d8 = 0; d8 < 8; ++d8) {
-        const uint16_t* vrow = s.vt + ((tl * 8 + d8) * 16 + col) * kVtStride;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 4 * g);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 + 4 * g);
-        va[d8] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-      }
+      for (int d8 = 0; d8 < 8; ++d8)
+        va[d8] = fp8x8_to_bf16x8(tr8_read(vbase + (tl * 8 + d8) * 16));
 #pragma unroll
       for (int d8 = 0; d8 < 8; ++d8)
         o[t2 * 8 + d8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d8], b, o[t2 * 8 + d8], 0, 0, 0);
     }
-    HS_ATTEND_MARK(3);
-    __syncthreads();   // every wave is done with the block before the next store
     HS_ATTEND_MARK(4);
+    cur = nxt;
   }
   HS_ATTEND_MARK(5);
   HS_ATTEND_FLUSH;
