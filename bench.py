@@ -346,6 +346,32 @@ def main():
         hit_replay["graph_rows_per_s"] = round(entries / (g_step * 1e-6))
         hit_replay["graph_hbm_gbps"] = round(rep_bytes / g_step / 1e3, 1)
         hit_replay["graph_hbm_frac"] = round(rep_bytes / g_step / 1e3 / HBM_PEAK_GBPS, 4)
+    regather = None
+    if graph and NR and wl.G == 1:
+        # the plan's rows gathered again for a further forward pass
+        # (hs_gather over the last step's row ids), NR launches captured once
+        # and timed like the hit replays
+        valid = int(((dev.rows >= 0) & (dev.rows < wl.pool_rows)).sum().item())
+        g_bytes = entries * 4 + entries * ROW + valid * ROW
+        hev.begin_capture(cap.cuda_stream)
+        try:
+            for j in range(NR):
+                dev.gather(cap.cuda_stream)
+        finally:
+            hev.end_capture(cap.cuda_stream)
+        torch.cuda.synchronize()
+        hev.launch(cap.cuda_stream)          # untimed first launch
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        hev.launch(cap.cuda_stream)
+        torch.cuda.synchronize()
+        g_us = (time.perf_counter() - t2) / NR * 1e6
+        hev.destroy_graph()
+        regather = {"graph_us": round(g_us, 2), "hbm_bytes": g_bytes,
+                    "hbm_gbps": round(g_bytes / g_us / 1e3, 1),
+                    "hbm_frac": round(g_bytes / g_us / 1e3 / HBM_PEAK_GBPS, 4),
+                    "note": "hs_gather of the last step's row ids (the multi-forward replay of a "
+                            "resolved plan), graph replay"}
 
     # page coldness for the residency policy: hs_page_touch over the last
     # step's lists, HIP events around each launch
@@ -413,6 +439,7 @@ def main():
                          f"each queued behind a 0.3 ms device spin so no event waits on the host",
         "cold": cold,
         "hit_replay": hit_replay,
+        "plan_regather": regather,
         "policy": policy,
         "consumer": consumer,
         "miss_path": miss_path,
