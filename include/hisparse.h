@@ -321,7 +321,9 @@ hs_status hs_resolve_in_place(const hs_layout* layout, const hs_batch* batch, co
  * Precision: keys and values are used exactly (E4M3 values are bfloat16
  * values; the scales are applied in float32), products accumulate in
  * float32, the probabilities times the value scales are rounded to bfloat16
- * for the value products.
+ * for the value products; where the rows are split across workgroups, each
+ * split's normalised output is kept in half precision (a relative 2^-11)
+ * until the splits are merged in float32.
  * Execution: all on `stream`; calls sharing a workspace must not overlap.
  * Errors: HS_ERR_INVALID_ARGUMENT (null or misaligned pointers with work to
  * do, a short workspace, num_heads not a positive multiple of 16, negative
@@ -351,7 +353,7 @@ size_t hs_sparse_mla_workspace_bytes(int32_t num_tokens, int32_t num_heads, int3
  * is looked up once per device, on the first call that needs it.  Calls whose
  * hs_sparse_mla_workspace_bytes(num_tokens, num_heads, top_k) exceeds it
  * return HS_ERR_UNSUPPORTED before enqueuing anything (the decode shape, 32
- * tokens x 128 heads x 2048 rows, needs about 34 MB).
+ * tokens x 128 heads x 2048 rows, needs about 17 MB).
  * Concurrency: every call on one device shares that device's array and
  * overwrites it; calls that overlap in time on one device (other streams,
  * other threads) race and must be ordered by the caller.  Nothing in the

@@ -425,7 +425,8 @@ hs::AttendParams attend_plan(int32_t num_tokens, int32_t num_heads, int32_t top_
   p.num_heads = num_heads;
   p.top_k = top_k;
   hs::plan_attend(p, hs::kAttendTargetGroups);
-  *workspace = p.splits > 1 ? (size_t)num_tokens * p.splits * num_heads * (512 + 2) * 4 : 0;
+  // per (token, split, head): 512 half-precision outputs and two floats
+  *workspace = p.splits > 1 ? (size_t)num_tokens * p.splits * num_heads * (512 * 2 + 2 * 4) : 0;
   return p;
 }
 
@@ -480,8 +481,10 @@ hs_status sparse_mla_decode(const hs_layout* layout, const uint8_t* kv_layer,
   p.sm_scale = sm_scale;
   p.out = out;
   p.lse = lse;
-  p.part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  p.part_ml = need > 0 ? p.part_o + (size_t)num_tokens * p.splits * num_heads * 512 : nullptr;
+  p.part_o = need > 0 ? static_cast<uint16_t*>(workspace) : nullptr;
+  p.part_ml = need > 0 ? reinterpret_cast<float*>(p.part_o + (size_t)num_tokens * p.splits *
+                                                                 num_heads * 512)
+                       : nullptr;
   return from_hip(hs::launch_attend(p, stream), "sparse MLA launch");
 }
 

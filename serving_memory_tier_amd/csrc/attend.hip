@@ -66,6 +66,7 @@ constexpr float kStaleMax = 8.f;            // log2 of the largest unnormalised 
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
@@ -348,19 +349,27 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
       p.lse[th] = l_run > 0.f ? (m_run + log2f(l_run)) / kLog2e : -INFINITY;
     return;
   }
+  // the split's output divided by its own sum, in half precision: values
+  // within the rows' range, a relative 2^-11 each, half the bytes of float32
+  // for the merge to read back
   const int64_t ps = ((int64_t)t * p.splits + split) * p.num_heads + head;
-  float* po = p.part_o + ps * kLatent + d0;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  uint16_t* po = p.part_o + ps * kLatent + d0;
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt)
-    *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * g) = o[dt];
+  for (int dt = 0; dt < 16; ++dt) {
+    const f32x4 v = o[dt] * inv;
+    const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *reinterpret_cast<f16x4*>(po + dt * 16 + 4 * g) = h;
+  }
   if (g == 0 && half == 0) {
     p.part_ml[2 * ps] = m_run;
     p.part_ml[2 * ps + 1] = l_run;
   }
 }
 
-// Merges the key splits of one (token, head): out = sum_s 2^(m_s - M) O_s /
-// sum_s 2^(m_s - M) l_s, lse = (M + log2 L) / log2 e.
+// Merges the key splits of one (token, head): with w_s = 2^(m_s - M) l_s and
+// the splits' normalised outputs O_s / l_s, out = sum_s w_s (O_s / l_s) /
+// sum_s w_s, lse = (M + log2 L) / log2 e, L = sum_s w_s.
 __global__ void __launch_bounds__(128) attend_combine_kernel(AttendParams p) {
   const int t = blockIdx.y, head = blockIdx.x;
   const int64_t th = (int64_t)t * p.num_heads + head;
@@ -373,9 +382,10 @@ __global__ void __launch_bounds__(128) attend_combine_kernel(AttendParams p) {
     const int64_t ps = ((int64_t)t * p.splits + sp) * p.num_heads + head;
     const float m = p.part_ml[2 * ps];
     if (m == -INFINITY) continue;
-    const float f = exp2f(m - M);
-    L += f * p.part_ml[2 * ps + 1];
-    acc += f * *reinterpret_cast<const f32x4*>(p.part_o + ps * kLatent + 4 * threadIdx.x);
+    const float wgt = exp2f(m - M) * p.part_ml[2 * ps + 1];
+    L += wgt;
+    const f16x4 h = *reinterpret_cast<const f16x4*>(p.part_o + ps * kLatent + 4 * threadIdx.x);
+    acc += wgt * f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   *reinterpret_cast<f32x4*>(p.out + th * kLatent + 4 * threadIdx.x) = acc * inv;

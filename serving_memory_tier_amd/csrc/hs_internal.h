@@ -275,8 +275,9 @@ struct AttendParams {
   float sm_scale;
   float* out;               // [tokens][heads][512]
   float* lse;               // [tokens][heads]
-  float* part_o;            // workspace: [tokens][splits][heads][512]
-  float* part_ml;           // workspace: [tokens][splits][heads][2]
+  uint16_t* part_o;         // workspace: [tokens][splits][heads][512] IEEE half bits, each
+                            // split's output already divided by its sum
+  float* part_ml;           // workspace: [tokens][splits][heads][2] (running max, sum)
   int32_t splits;
   int32_t keys_per_split;   // a multiple of 32
   int32_t head_groups;      // ceil(num_heads / kAttendHeadsPerGroup)
