@@ -91,14 +91,21 @@ def build_workload(name: str, n_steps: int):
 
 
 def kernel_source_hash() -> str:
-    """First 16 hex digits of the SHA-256 over the kernel sources, in name order."""
+    """First 16 hex digits of the SHA-256 over the kernel sources, in name
+    order, with comments and blank space taken out (so a comment edit leaves
+    measured figures valid; any change to the code does not)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "serving_memory_tier_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                text = fh.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update(f.encode())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

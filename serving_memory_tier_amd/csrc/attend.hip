@@ -31,8 +31,9 @@
 // Reading FP8 from LDS and converting per use halves the LDS bytes against
 // converting once into bf16 copies; half the value dimensions per wave keep
 // a wave under 256 registers, so two waves share each SIMD.
-// Key splits write unnormalised partial outputs with their running max and
-// sum to the caller's workspace; a combine kernel merges them.
+// Key splits write their outputs divided by their own sums, in half
+// precision, with their running max and sum to the workspace; a combine
+// kernel merges them in float32.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
