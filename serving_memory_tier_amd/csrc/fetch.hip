@@ -67,7 +67,20 @@ int64_t prepare_fetch(FetchParams& p, size_t* lds_bytes, int64_t gather_target) 
   const int64_t n_rl = (int64_t)p.num_reqs * p.num_layers;
   p.lds_n = ((p.entries + 3) / 4) * 4;
   p.gather_e = gather_entries(p.entries, n_rl, gather_target);
-  *lds_bytes = 4 * fetch_lds_words(p.entries, p.gather_e, &p.miss_tab_n, &p.gather_tab_n);
+  size_t words = fetch_lds_words(p.entries, p.gather_e, &p.miss_tab_n, &p.gather_tab_n);
+  // the miss workgroups' bitmap of the tokens the usable slots hold (one bit
+  // per token of the block table's span), where the slots all come with the
+  // workgroup's first loads and the bitmap fits beside the rest of its LDS
+  p.slot_bits_words = 0;
+  if (p.hot_capacity <= kFillThreads * fill::kScanUnroll) {
+    const int64_t nb = (((int64_t)p.max_pages << p.page_shift) + 31) / 32;
+    const int64_t need = 3 * (int64_t)p.lds_n + p.miss_tab_n + 4 + nb;
+    if (nb > 0 && need <= (int64_t)(kMaxLdsBytes / 4)) {
+      p.slot_bits_words = (int32_t)nb;
+      if ((size_t)need > words) words = (size_t)need;
+    }
+  }
+  *lds_bytes = 4 * words;
   const uint32_t pieces = (uint32_t)(p.row_bytes >> 4);
   p.piece_magic = (uint32_t)(((1ull << 32) + pieces - 1) / pieces);
   // miss workgroups: kFetchHostGroups in all (the host reads in flight that

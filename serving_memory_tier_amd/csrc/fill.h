@@ -403,7 +403,7 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   const int tid = threadIdx.x;
   const Rl v = rl_view(p, rl);
   const int32_t N = v.N;
-  // LDS: keys[N] | src[N] | list[N] | tab[n] | counters[4]
+  // LDS: keys[N] | src[N] | list[N] | tab[n] | counters[4] (| slot bitmap)
   int32_t* keys = lds;
   int32_t* src = keys + p.lds_n;
   int32_t* list = src + p.lds_n;
@@ -414,18 +414,51 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   prefetch_slots(p, rl, pre);
   for (int32_t h = tid; h < n; h += kT) tab[h] = kEmptyWord;
   if (tid < 4) cnt[tid] = 0;
+  // with a slot bitmap (after the counters): bit t set when a usable slot
+  // holds token t; only the misses then enter the table, and no slot probes it
+  const int32_t nb = p.slot_bits_words;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(cnt + 4);
+  for (int32_t h = tid; h < nb; h += kT) bits[h] = 0u;
   const bool any = classify_range(p, v, 0, N, keys, src,
                                   [](int32_t s) { return is_host_row(s); });
   if (any) cnt[2] = 1;  // racing writes of the same value
   HS_FILL_MARK(1);
-  // only this workgroup's tokens (t mod S == s) enter the table and are
-  // looked up by the slots
-  for (int32_t e = tid; e < N; e += kT)
-    if (is_host_row(src[e]) && (S == 1 || keys[e] % S == s)) map_insert(tab, n, keys, keys[e], e);
-  __syncthreads();
-  HS_FILL_MARK(-1);
-  if (cnt[2] == 0) return;  // nothing to read from the host
-  scan_slots(p, rl, tab, n, keys, pre, s, S);
+  if (nb > 0) {
+    // every usable slot came with the first loads (pre); the bitmap was
+    // cleared before classify_range's barrier
+    const int32_t lim = nb * 32;
+#pragma unroll
+    for (int u = 0; u < kScanUnroll; ++u) {
+      const int32_t t = pre[u];
+      if (t >= 0 && t < lim && (S == 1 || t % S == s)) atomicOr(&bits[t >> 5], 1u << (t & 31));
+    }
+    __syncthreads();
+    // a host row whose token a slot holds is a hit, which the gather
+    // workgroups write; the others of this workgroup's tokens enter the table
+    for (int32_t e = tid; e < N; e += kT) {
+      if (!is_host_row(src[e])) continue;
+      const int32_t t = keys[e];
+      if (S != 1 && t % S != s) continue;
+      if ((bits[t >> 5] >> (t & 31)) & 1u) {
+        src[e] = kSkip;
+      } else {
+        map_insert(tab, n, keys, t, e);
+        cnt[3] = 1;  // racing writes of the same value
+      }
+    }
+    __syncthreads();
+    HS_FILL_MARK(-1);
+    if (cnt[3] == 0) return;  // no miss among this workgroup's tokens
+  } else {
+    // only this workgroup's tokens (t mod S == s) enter the table and are
+    // looked up by the slots
+    for (int32_t e = tid; e < N; e += kT)
+      if (is_host_row(src[e]) && (S == 1 || keys[e] % S == s)) map_insert(tab, n, keys, keys[e], e);
+    __syncthreads();
+    HS_FILL_MARK(-1);
+    if (cnt[2] == 0) return;  // nothing to read from the host
+    scan_slots(p, rl, tab, n, keys, pre, s, S);
+  }
   HS_FILL_MARK(2);
 
   // ---- this workgroup's work lists: first entries of its miss tokens from

@@ -208,6 +208,9 @@ struct FetchParams {
   // 1: no gather workgroups; the misses' host rows go to their first entries
   // only (a staging buffer for callers that read rows in place)
   int32_t misses_only = 0;
+  // > 0 (set by prepare_fetch where it fits): the miss workgroups mark the
+  // tokens the usable slots hold in a bitmap of this many words
+  int32_t slot_bits_words = 0;
 };
 
 // Bytes of dynamic LDS a fill workgroup needs for N entries.
