@@ -24,7 +24,8 @@
  *     Data-dependent outcomes are reported per entry (sentinel row ids) and
  *     per request-layer (the stats record), never through the return value.
  *   - Calls on disjoint state may run concurrently; calls that share state
- *     (slot_token / slot_stamp / pool rows) must be ordered by the caller.
+ *     (slot_token / slot_stamp / pool rows / fill_sync) must be ordered by
+ *     the caller.
  *
  * Data layout (all little-endian, all row ids int32):
  *   kv_pool    uint8 [L][pool_rows][row_bytes], layer l at l * pool_layer_stride
@@ -93,7 +94,22 @@ typedef struct {
   const int32_t* hot_blocks;        /* device [R][C / page_size] */
   int32_t* slot_token;              /* device [R][L][C], read and updated */
   uint32_t* slot_stamp;             /* device [R][L][C], read and updated */
+  int32_t* fill_sync;               /* device [HS_FILL_SYNC_WORDS], or NULL (see below) */
 } hs_batch;
+
+/*
+ * fill_sync -- optional work counters of the early fill's miss workgroups.
+ * With more (request-layer, split) items than miss workgroups, a non-NULL
+ * fill_sync lets each workgroup take its next item from a counter as it
+ * finishes the last one (the host link serves the chip's XCDs at different
+ * rates, so a fixed share per workgroup ends with the slowest); NULL keeps
+ * the fixed share.  The words must be zero before the first call that uses
+ * them; every call leaves them zero again (the last miss workgroup to finish
+ * clears them), so one zeroed allocation serves a batch's calls for good.
+ * They are state like slot_token: calls that share a fill_sync must be
+ * ordered by the caller.  Results do not depend on fill_sync.
+ */
+#define HS_FILL_SYNC_WORDS 64
 
 /*
  * hs_resolve -- the fused top-K resolver ("How it works": mixed residency;

@@ -15,6 +15,7 @@ HS_ERR_LAUNCH = 3
 HS_ERR_HIP = 4
 HS_MAX_ENTRIES = 8192
 HS_MAX_HOT_CAPACITY = 12288
+HS_FILL_SYNC_WORDS = 64
 
 EXPORTS = ("hs_resolve", "hs_gather", "hs_offload_prefix_pages", "hs_plan_replay",
            "hs_resolve_grouped",
@@ -43,7 +44,8 @@ class HsBatch(ctypes.Structure):
                 ("kv_pool", ctypes.c_void_p), ("host_pool", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("host_block_table", ctypes.c_void_p),
                 ("ctx_len", ctypes.c_void_p), ("hot_blocks", ctypes.c_void_p),
-                ("slot_token", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p)]
+                ("slot_token", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
+                ("fill_sync", ctypes.c_void_p)]
 
 
 _lib = None

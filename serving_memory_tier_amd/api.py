@@ -55,13 +55,14 @@ def layout_of(page_size: int, row_bytes: int, num_layers: int, hot_capacity: int
 
 
 def batch_of(num_reqs: int, max_pages: int, kv_pool, host_pool, block_table, host_block_table,
-             ctx_len, hot_blocks, slot_token, slot_stamp) -> HsBatch:
+             ctx_len, hot_blocks, slot_token, slot_stamp, fill_sync=None) -> HsBatch:
     """kv_pool and the tables are CUDA tensors; host_pool is a HostPool, a
-    device-visible address (int), or None when host_rows is 0."""
+    device-visible address (int), or None when host_rows is 0; fill_sync is
+    None or a zeroed int32 CUDA tensor of HS_FILL_SYNC_WORDS elements."""
     hp = host_pool.device_ptr if isinstance(host_pool, HostPool) else _ptr(host_pool)
     return HsBatch(num_reqs, max_pages, _ptr(kv_pool), hp, _ptr(block_table),
                    _ptr(host_block_table), _ptr(ctx_len), _ptr(hot_blocks), _ptr(slot_token),
-                   _ptr(slot_stamp))
+                   _ptr(slot_stamp), _ptr(fill_sync))
 
 
 def hs_resolve(layout: HsLayout, batch: HsBatch, topk, top_k: int, stamp: int, row_ids,

@@ -222,6 +222,7 @@ hs::FetchParams fetch_params(const hs_layout* lay, const hs_batch* b, const int3
   f.ctx_len = b->ctx_len;
   f.hot_blocks = b->hot_blocks;
   f.slot_token = b->slot_token;
+  f.sync = b->fill_sync;
   f.topk = topk;
   f.entries = N;
   f.out = gather_out;

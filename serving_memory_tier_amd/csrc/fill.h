@@ -95,6 +95,19 @@ __device__ void map_insert(uint32_t* tab, int32_t n, const int32_t* keys, int32_
   }
 }
 
+// Claims token t's word for entry e: -1 when e claimed it, otherwise the
+// entry that did (the word is not lowered afterwards).
+__device__ int32_t map_claim(uint32_t* tab, int32_t n, const int32_t* keys, int32_t t, int32_t e) {
+  const uint32_t w = ((uint32_t)e << 16) | kNoSlot;
+  int32_t h = home((uint32_t)t, n);
+  while (true) {
+    const uint32_t old = atomicCAS(&tab[h], kEmptyWord, w);
+    if (old == kEmptyWord) return -1;
+    if (keys[old >> 16] == t) return (int32_t)(old >> 16);
+    h = next(h, n);
+  }
+}
+
 // The table index holding token t, or -1.
 __device__ int32_t map_find(const uint32_t* tab, int32_t n, const int32_t* keys, int32_t t) {
   int32_t h = home((uint32_t)t, n);
@@ -276,17 +289,23 @@ __device__ __forceinline__ void classify_tokens(const Rl& v, const int32_t* bt,
 }
 
 // Classifies entries [lo, hi) into keys[e - lo] (the token) and src[e - lo];
-// returns whether this thread saw an entry for which `want` holds.  Ends
-// with a barrier.
+// returns whether this thread saw an entry for which `want` holds.  The
+// first kT * kU entries' tokens come loaded (t0, from load_tokens at lo).
+// Ends with a barrier.
 template <typename Want>
 __device__ __forceinline__ bool classify_range(const FetchParams& p, const Rl& v, int32_t lo,
                                                int32_t hi, int32_t* keys, int32_t* src,
-                                               Want want) {
+                                               const int32_t (&t0)[kU], Want want) {
   const int tid = threadIdx.x;
   bool any = false;
   for (int32_t e0 = lo; e0 < hi; e0 += kT * kU) {
     int32_t t[kU], sv[kU];
-    load_tokens(p, v, e0, hi, t);
+    if (e0 == lo) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) t[u] = t0[u];
+    } else {
+      load_tokens(p, v, e0, hi, t);
+    }
     classify_tokens(v, v.bt, v.hbt, t, sv);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -315,11 +334,15 @@ __device__ void fill_gather(const FetchParams& p, int32_t* lds, int32_t rl, int3
   uint32_t* tab = reinterpret_cast<uint32_t*>(src + p.gather_e);
   const int32_t n = p.gather_tab_n;
   int32_t* flag = reinterpret_cast<int32_t*>(tab + n);
+  // the first entries' tokens are loaded before the slots, so that their
+  // block-table loads need not wait for the slots' loads
+  int32_t t0[kU];
+  load_tokens(p, v, lo, hi, t0);
   int32_t pre[kScanUnroll];
   prefetch_slots(p, rl, pre);
   for (int32_t h = tid; h < n; h += kT) tab[h] = kEmptyWord;
   if (tid == 0) *flag = 0;
-  const bool any = classify_range(p, v, lo, hi, keys, src,
+  const bool any = classify_range(p, v, lo, hi, keys, src, t0,
                                   [](int32_t s) { return non_resident(s); });
   if (any) *flag = 1;
   for (int32_t el = tid; el < E; el += kT)
@@ -410,6 +433,9 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   uint32_t* tab = reinterpret_cast<uint32_t*>(list + p.lds_n);
   const int32_t n = p.miss_tab_n;
   int32_t* cnt = reinterpret_cast<int32_t*>(tab + n);
+  // the first entries' tokens before the slots (as in fill_gather)
+  int32_t t0[kU];
+  load_tokens(p, v, 0, N, t0);
   int32_t pre[kScanUnroll];
   prefetch_slots(p, rl, pre);
   for (int32_t h = tid; h < n; h += kT) tab[h] = kEmptyWord;
@@ -419,10 +445,11 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
   const int32_t nb = p.slot_bits_words;
   uint32_t* bits = reinterpret_cast<uint32_t*>(cnt + 4);
   for (int32_t h = tid; h < nb; h += kT) bits[h] = 0u;
-  const bool any = classify_range(p, v, 0, N, keys, src,
+  const bool any = classify_range(p, v, 0, N, keys, src, t0,
                                   [](int32_t s) { return is_host_row(s); });
   if (any) cnt[2] = 1;  // racing writes of the same value
   HS_FILL_MARK(1);
+  bool listed = false;  // the work lists below are already built
   if (nb > 0) {
     // every usable slot came with the first loads (pre); the bitmap was
     // cleared before classify_range's barrier
@@ -434,21 +461,56 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
     }
     __syncthreads();
     // a host row whose token a slot holds is a hit, which the gather
-    // workgroups write; the others of this workgroup's tokens enter the table
-    for (int32_t e = tid; e < N; e += kT) {
-      if (!is_host_row(src[e])) continue;
-      const int32_t t = keys[e];
-      if (S != 1 && t % S != s) continue;
-      if ((bits[t >> 5] >> (t & 31)) & 1u) {
-        src[e] = kSkip;
-      } else {
-        map_insert(tab, n, keys, t, e);
-        cnt[3] = 1;  // racing writes of the same value
+    // workgroups write; the others of this workgroup's tokens are misses
+    if (!p.misses_only) {
+      // the entry that claims a miss token's word reads its row; the token's
+      // other entries copy that row (every entry ends with the same bytes,
+      // whichever entry reads)
+      for (int32_t e0 = 0; e0 < N; e0 += kT) {
+        const int32_t e = e0 + tid;
+        const int32_t sv = e < N ? src[e] : kZeroRow;
+        const int32_t t = e < N ? keys[e] : -1;
+        bool first = false, dup = false;
+        int32_t f = -1;
+        if (is_host_row(sv) && (S == 1 || t % S == s)) {
+          if ((bits[t >> 5] >> (t & 31)) & 1u) {
+            src[e] = kSkip;
+          } else {
+            f = map_claim(tab, n, keys, t, e);
+            first = f < 0;
+            dup = !first;
+          }
+        }
+        const int32_t i = wave_append(&cnt[0], first);
+        if (first) list[i] = e;
+        const int32_t j = wave_append(&cnt[1], dup);
+        if (dup) {
+          list[p.lds_n - 1 - j] = e;
+          src[e] = f;  // a later entry copies the reading entry's output row
+        }
       }
+      __syncthreads();
+      listed = true;
+      HS_FILL_MARK(-1);
+      if (cnt[0] == 0) return;  // no miss among this workgroup's tokens
+    } else {
+      // the staging rows are the first entries' only: the smallest entry of
+      // each miss token reads its row (the table keeps the smallest)
+      for (int32_t e = tid; e < N; e += kT) {
+        if (!is_host_row(src[e])) continue;
+        const int32_t t = keys[e];
+        if (S != 1 && t % S != s) continue;
+        if ((bits[t >> 5] >> (t & 31)) & 1u) {
+          src[e] = kSkip;
+        } else {
+          map_insert(tab, n, keys, t, e);
+          cnt[3] = 1;  // racing writes of the same value
+        }
+      }
+      __syncthreads();
+      HS_FILL_MARK(-1);
+      if (cnt[3] == 0) return;  // no miss among this workgroup's tokens
     }
-    __syncthreads();
-    HS_FILL_MARK(-1);
-    if (cnt[3] == 0) return;  // no miss among this workgroup's tokens
   } else {
     // only this workgroup's tokens (t mod S == s) enter the table and are
     // looked up by the slots
@@ -463,29 +525,31 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
 
   // ---- this workgroup's work lists: first entries of its miss tokens from
   // the front of list[], their later entries from the back ----------------
-  for (int32_t e0 = 0; e0 < N; e0 += kT) {
-    const int32_t e = e0 + tid;
-    const int32_t sv = e < N ? src[e] : kZeroRow;
-    const int32_t t = e < N ? keys[e] : -1;
-    bool first = false, dup = false;
-    int32_t f = -1;
-    if (is_host_row(sv) && (t % S) == s) {
-      const uint32_t w = tab[map_find(tab, n, keys, t)];
-      if ((w & 0xFFFFu) == kNoSlot) {  // not in the hot buffer: a miss
-        f = (int32_t)(w >> 16);
-        first = f == e;
-        dup = !first;
+  if (!listed) {
+    for (int32_t e0 = 0; e0 < N; e0 += kT) {
+      const int32_t e = e0 + tid;
+      const int32_t sv = e < N ? src[e] : kZeroRow;
+      const int32_t t = e < N ? keys[e] : -1;
+      bool first = false, dup = false;
+      int32_t f = -1;
+      if (is_host_row(sv) && (t % S) == s) {
+        const uint32_t w = tab[map_find(tab, n, keys, t)];
+        if ((w & 0xFFFFu) == kNoSlot) {  // not in the hot buffer: a miss
+          f = (int32_t)(w >> 16);
+          first = f == e;
+          dup = !first;
+        }
+      }
+      const int32_t i = wave_append(&cnt[0], first);
+      if (first) list[i] = e;
+      const int32_t j = wave_append(&cnt[1], dup);
+      if (dup) {
+        list[p.lds_n - 1 - j] = e;
+        src[e] = f;  // a later entry copies the first entry's output row
       }
     }
-    const int32_t i = wave_append(&cnt[0], first);
-    if (first) list[i] = e;
-    const int32_t j = wave_append(&cnt[1], dup);
-    if (dup) {
-      list[p.lds_n - 1 - j] = e;
-      src[e] = f;  // a later entry copies the first entry's output row
-    }
+    __syncthreads();
   }
-  __syncthreads();
   const int32_t n_first = cnt[0];
   const int32_t n_dup = cnt[1];
   HS_FILL_MARK(3);
@@ -529,17 +593,44 @@ __device__ void fill_misses(const FetchParams& p, int32_t* lds, int32_t rl, int3
 }
 
 // Fill block b of the launch's fill blocks: [0, miss_groups) are miss
-// workgroups (group g handles the (request-layer, split) pairs g,
-// g + miss_groups, ...), the rest gather workgroups, gather_splits per
-// request-layer.
+// workgroups, the rest gather workgroups, gather_splits per request-layer.
+// Miss workgroup g takes the (request-layer, split) item g first, then, with
+// fill_sync and more items than miss workgroups, the next item not yet taken
+// (a counter in fill_sync; the host link serves the XCDs at different rates,
+// so fixed shares end with the slowest), otherwise items g + miss_groups, ...
 __device__ void fill_block(const FetchParams& p, int32_t* lds, int32_t b) {
   HS_FILL_MARK(0);
   const int32_t n_rl = p.num_reqs * p.num_layers;
   if (b < p.miss_groups) {
+    const int tid = threadIdx.x;
     const int32_t S = p.miss_splits;
-    for (int32_t w = b; w < n_rl * S; w += p.miss_groups) {
-      if (w != b) __syncthreads();  // the previous pair's LDS reads are done
-      fill_misses(p, lds, w / S, w % S, S);
+    const int32_t items = n_rl * S;
+    const bool dyn = p.sync != nullptr && items > p.miss_groups;
+    // the fourth counter word of fill_misses carries the next item between
+    // its calls (it clears the word only after the barrier that starts a
+    // call)
+    int32_t* next = lds + 3 * p.lds_n + p.miss_tab_n + 3;
+    int32_t it = b;
+    for (int32_t round = 0; it < items && round < items; ++round) {
+      if (round > 0) __syncthreads();  // the previous item's LDS reads are done
+      fill_misses(p, lds, it / S, it % S, S);
+      if (dyn) {
+        __syncthreads();
+        if (tid == 0) *next = atomicAdd(&p.sync[kSyncItems], 1) + p.miss_groups;
+        __syncthreads();
+        it = *next;
+      } else {
+        it += p.miss_groups;
+      }
+    }
+    if (dyn && tid == 0) {
+      // every take of this workgroup precedes its count; the last workgroup
+      // counted clears both words for the next launch
+      __threadfence();
+      if (atomicAdd(&p.sync[kSyncDone], 1) == p.miss_groups - 1) {
+        __hip_atomic_store(&p.sync[kSyncItems], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.sync[kSyncDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     HS_FILL_MARK(5);
     return;

@@ -211,7 +211,14 @@ struct FetchParams {
   // > 0 (set by prepare_fetch where it fits): the miss workgroups mark the
   // tokens the usable slots hold in a bitmap of this many words
   int32_t slot_bits_words = 0;
+  // the batch's fill_sync words (zero between launches), or null: with more
+  // items than miss workgroups, each takes its next item from a counter
+  int32_t* sync = nullptr;
 };
+
+// fill_sync words: workgroups done, items taken (on separate 128-byte lines)
+constexpr int kSyncDone = 0;
+constexpr int kSyncItems = 32;
 
 // Bytes of dynamic LDS a fill workgroup needs for N entries.
 size_t fetch_lds_bytes(int32_t entries, int32_t hot_capacity);

@@ -17,6 +17,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+from ._lib import HS_FILL_SYNC_WORDS
 from .api import (HostPool, batch_of, hs_gather, hs_offload_prefix_pages, hs_plan_replay,
                   hs_resolve, hs_resolve_commit, hs_resolve_decide, hs_resolve_grouped,
                   hs_resolve_move, layout_of)
@@ -52,7 +53,8 @@ def update_runs(arr: np.ndarray):
 
 
 class DeviceRun:
-    def __init__(self, wl, device: str = "cuda", content_device: str | None = None):
+    def __init__(self, wl, device: str = "cuda", content_device: str | None = None,
+                 fill_sync: bool = True):
         self.wl = wl
         dev = torch.device(device)
         self.device = dev
@@ -80,8 +82,11 @@ class DeviceRun:
         self.stats = torch.empty((wl.R, NG, 8), dtype=i32, device=dev)
         self.out = torch.empty((wl.R, wl.L, wl.P, wl.K, ROW), dtype=torch.uint8, device=dev)
         self.layout = layout_of(PAGE, ROW, wl.L, wl.C, wl.pool_rows, wl.host_rows)
+        # the miss workgroups' item counters (zero between calls)
+        self.fill_sync = (torch.zeros(HS_FILL_SYNC_WORDS, dtype=i32, device=dev)
+                          if fill_sync else None)
         self.batch = batch_of(wl.R, wl.max_pages, self.pool, self.host_pool, self.bt, self.hbt,
-                              self.ctx, self.hot, self.tok, self.stp)
+                              self.ctx, self.hot, self.tok, self.stp, self.fill_sync)
         self.entries = N
         self.topk = [None] * len(wl.steps)
         self.pairs = [None] * len(wl.steps)
@@ -172,7 +177,8 @@ class DeviceRun:
         self.ctx_all = torch.from_numpy(
             np.stack([s.ctx for s in wl.steps]).astype(np.int32)).to(self.device)
         self.batches = [batch_of(wl.R, wl.max_pages, self.pool, self.host_pool, self.bt,
-                                 self.hbt, self.ctx_all[i], self.hot, self.tok, self.stp)
+                                 self.hbt, self.ctx_all[i], self.hot, self.tok, self.stp,
+                                 self.fill_sync)
                         for i in range(n)]
         n_vals = sum(s.hbt_set.shape[0] + s.bt_set.shape[0] for s in wl.steps)
         self.pinned_vals = torch.empty(max(1, n_vals), dtype=torch.int32, pin_memory=True)

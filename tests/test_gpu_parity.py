@@ -333,14 +333,16 @@ def test_plan_rows_replayed_by_gather():
         dev.close()
 
 
-def test_concurrent_calls_on_two_streams():
+@pytest.mark.parametrize("R", [8, 48])
+def test_concurrent_calls_on_two_streams(R):
     """Two batches with misses resolved by calls running at the same time on
-    two streams (each with its own state and outputs): the misses' shared
-    host reads of one call never mix with the other's, and both match the
-    oracle bit for bit, every step."""
+    two streams (each with its own state, outputs and fill_sync counters):
+    the misses' shared host reads of one call never mix with the other's,
+    and both match the oracle bit for bit, every step.  With 48 requests the
+    miss workgroups take their items from the counters."""
     from serving_memory_tier_amd.runner import DeviceRun
 
-    wls = [hs_gen.mixed_decode(seed=1001 + k, steps=4, R=8) for k in range(2)]
+    wls = [hs_gen.mixed_decode(seed=1001 + k, steps=4, R=R) for k in range(2)]
     devs = [DeviceRun(wl) for wl in wls]
     oras = [OracleRun(wl) for wl in wls]
     streams = [torch.cuda.Stream() for _ in wls]
@@ -367,3 +369,44 @@ def test_concurrent_calls_on_two_streams():
     finally:
         for d in devs:
             d.close()
+
+
+@pytest.mark.parametrize("make", ["mixed_state", "multi_layer"])
+def test_fill_sync_items(make):
+    """More (request-layer, split) items than miss workgroups: with the
+    batch's fill_sync each miss workgroup takes its next item from a counter,
+    without it each takes a fixed share.  Both give identical row ids, stats,
+    gathered bytes, state and pool, step after step and on the hit replay of
+    each step, and every call leaves the counters zero."""
+    from serving_memory_tier_amd.runner import DeviceRun
+
+    wl = (hs_gen.mixed_state(R=48, steps=4) if make == "mixed_state"
+          else hs_gen.multi_layer(R=4, L=16, turns=3))
+    a, b = DeviceRun(wl), DeviceRun(wl, fill_sync=False)
+    assert a.fill_sync is not None and b.fill_sync is None
+    misses = 0
+    try:
+        for d in (a, b):
+            d.upload_steps()
+        for i in range(len(wl.steps)):
+            _say(f"[parity] fill_sync {make} step {i}")
+            for d in (a, b):
+                d.pre(i)
+            for rep in range(2):  # the step, then its hit replay
+                for d in (a, b):
+                    d.resolve(i)
+                torch.cuda.synchronize()
+                if rep == 0:
+                    misses += int(a.stats[..., 2].sum())
+                assert int(torch.count_nonzero(a.fill_sync)) == 0, f"counters, step {i}"
+                for x, y in ((a.rows, b.rows), (a.stats, b.stats), (a.out, b.out),
+                             (a.tok, b.tok), (a.stp, b.stp), (a.pool, b.pool)):
+                    assert torch.equal(x, y), f"step {i}, replay {rep}"
+            for d in (a, b):
+                d.post(i)
+        torch.cuda.synchronize()
+        assert torch.equal(a.host, b.host)
+        assert misses > 0
+    finally:
+        a.close()
+        b.close()
