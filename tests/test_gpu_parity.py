@@ -371,19 +371,22 @@ def test_concurrent_calls_on_two_streams(R):
             d.close()
 
 
-@pytest.mark.parametrize("make", ["mixed_state", "multi_layer"])
+@pytest.mark.parametrize("make", ["mixed_state", "multi_layer", "in_place"])
 def test_fill_sync_items(make):
     """More (request-layer, split) items than miss workgroups: with the
     batch's fill_sync each miss workgroup takes its next item from a counter,
     without it each takes a fixed share.  Both give identical row ids, stats,
     gathered bytes, state and pool, step after step and on the hit replay of
-    each step, and every call leaves the counters zero."""
+    each step, and every call leaves the counters zero.  ``in_place``: the
+    misses-only fill with its staging rows (hs_resolve_in_place)."""
     from serving_memory_tier_amd.runner import DeviceRun
 
     wl = (hs_gen.mixed_state(R=48, steps=4) if make == "mixed_state"
-          else hs_gen.multi_layer(R=4, L=16, turns=3))
+          else hs_gen.multi_layer(R=4, L=16, turns=3) if make == "multi_layer"
+          else hs_gen.mixed_decode(R=40, steps=4))
     a, b = DeviceRun(wl), DeviceRun(wl, fill_sync=False)
     assert a.fill_sync is not None and b.fill_sync is None
+    mode = "in_place" if make == "in_place" else "call"
     misses = 0
     try:
         for d in (a, b):
@@ -394,13 +397,20 @@ def test_fill_sync_items(make):
                 d.pre(i)
             for rep in range(2):  # the step, then its hit replay
                 for d in (a, b):
-                    d.resolve(i)
+                    if mode == "call":
+                        d.resolve(i)
+                    else:
+                        stages.run(mode, d.layout, d.batch, d.topk[i], wl.P, wl.K,
+                                   wl.steps[i].stamp, d.rows, d.out, d.stats)
                 torch.cuda.synchronize()
                 if rep == 0:
                     misses += int(a.stats[..., 2].sum())
                 assert int(torch.count_nonzero(a.fill_sync)) == 0, f"counters, step {i}"
-                for x, y in ((a.rows, b.rows), (a.stats, b.stats), (a.out, b.out),
-                             (a.tok, b.tok), (a.stp, b.stp), (a.pool, b.pool)):
+                pairs = [(a.rows, b.rows), (a.stats, b.stats), (a.tok, b.tok), (a.stp, b.stp),
+                         (a.pool, b.pool)]
+                if mode == "call":  # in place, the output holds staging rows only
+                    pairs.append((a.out, b.out))
+                for x, y in pairs:
                     assert torch.equal(x, y), f"step {i}, replay {rep}"
             for d in (a, b):
                 d.post(i)
