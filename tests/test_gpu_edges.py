@@ -155,7 +155,8 @@ def random_arrays(rs: np.random.Generator, R, L, C, page, rb, n_pages, n_blocks,
                   hostile=False):
     """A random batch.  Hot blocks of different requests are disjoint (a
     caller precondition); with ``hostile`` the tables also point outside the
-    pools, some hot blocks are unusable and stamps are non-monotone."""
+    pools, some hot blocks are unusable, stamps are non-monotone and some
+    slots hold stale tokens past the tables' span."""
     pool = rs.integers(0, 256, size=(L, n_blocks * page, rb), dtype=np.uint8)
     host = rs.integers(0, 256, size=(L, n_host * page, rb), dtype=np.uint8)
     hb_per = C // page
@@ -184,6 +185,11 @@ def random_arrays(rs: np.random.Generator, R, L, C, page, rb, n_pages, n_blocks,
             if hostile:
                 stp[r, layer, rs.choice(C, size=C // 8, replace=False)] = \
                     rs.integers(1, 1 << 32, size=C // 8, dtype=np.uint64).astype(np.uint32)
+                # stale tokens no list can hold: past the tables' span (the
+                # fill's slot bitmap covers the span only) and far past it
+                g = rs.choice(C, size=max(1, C // 64), replace=False)
+                tok[r, layer, g] = n_pages * page + rs.choice(4 * C, size=g.size, replace=False)
+                tok[r, layer, g[0]] = (1 << 30) + layer
     return dict(pool=pool, host=host, bt=bt, hbt=hbt, ctx=ctx, hot=hot, tok=tok, stp=stp)
 
 
