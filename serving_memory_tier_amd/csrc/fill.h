@@ -15,17 +15,22 @@
 // token, turns the codes into row ids and zeroes the rows of misses left
 // without a slot.
 //
-// Two kinds of fill workgroup classify entries the same way (an LDS map of
-// the non-resident entries' tokens that the hot buffer's slots probe gives
-// the hits; the block tables give the rest):
+// Two kinds of fill workgroup classify entries the same way (the block
+// tables, then whether a usable hot slot holds the token):
 //   * gather workgroups (several per request-layer, a range of entries each)
 //     write every row but the misses': resident and hot rows from the pool,
-//     zero rows for padded and invalid entries and tokens without a host copy;
+//     zero rows for padded and invalid entries and tokens without a host copy
+//     (an LDS map of the range's non-resident tokens, probed by every slot,
+//     gives each hit its slot);
 //   * miss workgroups (a fixed few for the whole launch) classify every entry
 //     of a request-layer, deduplicate the misses and read each distinct
-//     missed token's row once from the host into its first entry, then copy
-//     it to the token's later entries.  With several per request-layer,
-//     workgroup s owns the tokens t with t mod S == s.
+//     missed token's row once from the host into one of its entries, then
+//     copy it to the token's other entries (the hits come from a bitmap of
+//     the slots' tokens where it fits, else from the slots probing an LDS map
+//     of the host-backed entries).  With several per request-layer,
+//     workgroup s owns the tokens t with t mod S == s; with the batch's
+//     fill_sync counters, a workgroup done with its (request-layer, split)
+//     item takes the next one not yet taken.
 // Keeping the host reads to a few workgroups bounds how many are in flight:
 // the link saturates with a few tens of thousands of 16-byte reads
 // outstanding, and more only hold back the HBM reads of the rest of the
