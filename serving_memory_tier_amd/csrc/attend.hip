@@ -19,10 +19,14 @@
 // One barrier a block.  Wave w takes 16 heads (w & 3) and one half (w >> 2),
 // which picks its 16 keys for the scores and its 256 value dimensions:
 //   S^T (16 keys x 16 heads) = K Q^T with 16x16x32 bf16 MFMAs, the key
-//     operand read from LDS as FP8 and converted exactly to bf16 (every E4M3
-//     value is a bf16 value), one accumulator per 128-value latent tile and
-//     one for the rope, so the per-row scales are applied in float32 after
-//     the products; the two halves swap their scores through LDS;
+//     operand read from LDS as FP8, 16 bytes a lane for two steps (within
+//     each 64-value chunk the contraction runs over lane g's 16 values, 8 a
+//     step, and the queries are loaded in that order), and converted exactly
+//     to bf16 (every E4M3 value is a bf16 value), one accumulator per
+//     128-value latent tile and one for the rope, so the per-row scales are
+//     applied in float32 after the products; the two halves swap their
+//     scores through LDS (rows of 20 floats for 16 heads: the four lane
+//     groups of a write or read land on distinct banks);
 //   online softmax per head over the 32 keys (each lane owns one head column);
 //   O^T (256 dims x 16 heads) += V^T P'^T, where P' = p * scale of the latent
 //     tile: the probabilities are the B operand straight from registers, and
@@ -83,7 +87,7 @@ __device__ __forceinline__ int slot(int k) { return k ^ ((k >> 4) << 3); }
 struct AttendLds {
   AttendBlock blk[kBufs];
   int32_t ids[kAttendMaxSplitKeys];         // the split's row ids, -1 where nothing is selected
-  float xs[2][4][kBlockKeys][16];           // scores per (head tile, key, head) for the exchange
+  float xs[2][4][kBlockKeys][20];           // scores per (head tile, key, head) for the exchange
 };
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -186,7 +190,11 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
     const uint16_t* qh = p.q + ((int64_t)t * p.num_heads + (head_ok ? head : 0)) * kDim;
 #pragma unroll
     for (int ks = 0; ks < kDim / 32; ++ks) {
-      u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qh + ks * 32 + 8 * g) : u32x4{0, 0, 0, 0};
+      // latent steps in the keys' read order: step kk of tile tl takes
+      // values 128 tl + 64 (kk / 2) + 16 g + 8 (kk % 2) ..; rope as it is
+      const int off = ks < 16 ? (ks / 4) * 128 + 64 * ((ks % 4) >> 1) + 16 * g + 8 * (ks & 1)
+                              : ks * 32 + 8 * g;
+      u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qh + off) : u32x4{0, 0, 0, 0};
       qb[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -222,7 +230,7 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
     HS_ATTEND_MARK(0);
     const AttendBlock& cb = s.blk[cur];
     const int nxt = cur == kBufs - 1 ? 0 : cur + 1;
-    float (*xs)[kBlockKeys][16] = s.xs[bi & 1];
+    float (*xs)[kBlockKeys][20] = s.xs[bi & 1];
     // ---- scores of this wave's key tile: S^T[key 16 half + ..][head]
     {
       f32x4 acc[5];
@@ -231,22 +239,33 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
       // key half * 16 + col: latent bytes 128 tl + 32 kk + 8 g .. converted
       // to bf16, rope values 32 kk + 8 g .. as they are
       const uint8_t* krow = cb.rows + slot(half * 16 + col) * kRowBytes;
+      // latent: one 16-byte read a tile covers two steps (the contraction's
+      // order within a 64-value chunk is lane g's 16 values, 8 a step; the
+      // queries were loaded in the same order)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int nt = kk < 2 ? 5 : 4;
-        bf16x8 ka[5];
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        u32x4 kr[4];
 #pragma unroll
-        for (int tl = 0; tl < 5; ++tl)
-          if (tl < nt)
-            ka[tl] = tl < 4 ? fp8x8_to_bf16x8(*reinterpret_cast<const u32x2*>(
-                                  krow + tl * 128 + kk * 32 + 8 * g))
-                            : __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                  krow + kLatent + 16 + kk * 64 + 16 * g));
+        for (int tl = 0; tl < 4; ++tl)
+          kr[tl] = *reinterpret_cast<const u32x4*>(krow + tl * 128 + kk2 * 64 + 16 * g);
+        bf16x8 rp[2];
+        if (kk2 == 0) {
 #pragma unroll
-        for (int tl = 0; tl < 5; ++tl)
-          if (tl < nt)
-            acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tl], qb[tl * 4 + kk], acc[tl],
-                                                              0, 0, 0);
+          for (int h = 0; h < 2; ++h)
+            rp[h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                        krow + kLatent + 16 + h * 64 + 16 * g));
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kk = 2 * kk2 + h;
+#pragma unroll
+          for (int tl = 0; tl < 4; ++tl)
+            acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                fp8x8_to_bf16x8(u32x2{kr[tl][2 * h], kr[tl][2 * h + 1]}), qb[tl * 4 + kk], acc[tl],
+                0, 0, 0);
+          if (kk2 == 0)
+            acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp[h], qb[16 + h], acc[4], 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
