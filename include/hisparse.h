@@ -94,7 +94,8 @@ typedef struct {
   const int32_t* hot_blocks;        /* device [R][C / page_size] */
   int32_t* slot_token;              /* device [R][L][C], read and updated */
   uint32_t* slot_stamp;             /* device [R][L][C], read and updated */
-  int32_t* fill_sync;               /* device [HS_FILL_SYNC_WORDS], or NULL (see below) */
+  int32_t* fill_sync;               /* device [fill_sync_words], or NULL (see below) */
+  int32_t fill_sync_words;          /* int32 words at fill_sync: >= HS_FILL_SYNC_WORDS, 0 with NULL */
 } hs_batch;
 
 /*
@@ -106,6 +107,8 @@ typedef struct {
  * the fixed share.  The words must be zero before the first call that uses
  * them; every call leaves them zero again (the last miss workgroup to finish
  * clears them), so one zeroed allocation serves a batch's calls for good.
+ * fill_sync_words gives the allocation's size, which the call checks (fewer
+ * than HS_FILL_SYNC_WORDS, or words without a pointer: invalid argument).
  * They are state like slot_token: calls that share a fill_sync must be
  * ordered by the caller.  Results do not depend on fill_sync.
  */

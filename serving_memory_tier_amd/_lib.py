@@ -45,7 +45,7 @@ class HsBatch(ctypes.Structure):
                 ("block_table", ctypes.c_void_p), ("host_block_table", ctypes.c_void_p),
                 ("ctx_len", ctypes.c_void_p), ("hot_blocks", ctypes.c_void_p),
                 ("slot_token", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
-                ("fill_sync", ctypes.c_void_p)]
+                ("fill_sync", ctypes.c_void_p), ("fill_sync_words", ctypes.c_int32)]
 
 
 _lib = None

@@ -55,14 +55,21 @@ def layout_of(page_size: int, row_bytes: int, num_layers: int, hot_capacity: int
 
 
 def batch_of(num_reqs: int, max_pages: int, kv_pool, host_pool, block_table, host_block_table,
-             ctx_len, hot_blocks, slot_token, slot_stamp, fill_sync=None) -> HsBatch:
+             ctx_len, hot_blocks, slot_token, slot_stamp, fill_sync=None,
+             fill_sync_words: int | None = None) -> HsBatch:
     """kv_pool and the tables are CUDA tensors; host_pool is a HostPool, a
     device-visible address (int), or None when host_rows is 0; fill_sync is
-    None or a zeroed int32 CUDA tensor of HS_FILL_SYNC_WORDS elements."""
+    None or zeroed int32 device words (at least HS_FILL_SYNC_WORDS): a CUDA
+    tensor, whose length is the word count unless fill_sync_words says
+    otherwise, or an address with fill_sync_words."""
     hp = host_pool.device_ptr if isinstance(host_pool, HostPool) else _ptr(host_pool)
+    if isinstance(fill_sync, torch.Tensor) and fill_sync.dtype != torch.int32:
+        raise TypeError(f"fill_sync must be int32, not {fill_sync.dtype}")
+    if fill_sync_words is None:
+        fill_sync_words = fill_sync.numel() if isinstance(fill_sync, torch.Tensor) else 0
     return HsBatch(num_reqs, max_pages, _ptr(kv_pool), hp, _ptr(block_table),
                    _ptr(host_block_table), _ptr(ctx_len), _ptr(hot_blocks), _ptr(slot_token),
-                   _ptr(slot_stamp), _ptr(fill_sync))
+                   _ptr(slot_stamp), _ptr(fill_sync), fill_sync_words)
 
 
 def hs_resolve(layout: HsLayout, batch: HsBatch, topk, top_k: int, stamp: int, row_ids,

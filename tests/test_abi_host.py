@@ -101,6 +101,16 @@ def test_resolve_rejects_bad_call(lib):
     assert _resolve(lib, lay, bad) == 1
     bad = _batch(R=-1)
     assert _resolve(lib, lay, bad) == 1
+    # fill_sync: words without a pointer, a pointer with too few words
+    bad = _batch()
+    bad.fill_sync_words = 64
+    assert _resolve(lib, lay, bad) == 1
+    bad = _batch()
+    bad.fill_sync = 0x1000
+    bad.fill_sync_words = 63
+    assert _resolve(lib, lay, bad) == 1
+    bad.fill_sync_words = -1
+    assert _resolve(lib, lay, bad) == 1
 
 
 def test_plan_rejects_bad_call(lib):

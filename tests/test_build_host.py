@@ -27,8 +27,9 @@ def _c_layout():
 #include "hisparse.h"
 int main(void) {
   printf("%zu %zu\n", sizeof(hs_layout), sizeof(hs_batch));
-  printf("%zu %zu %zu %zu\n", offsetof(hs_batch, slot_token), offsetof(hs_batch, slot_stamp),
-         offsetof(hs_batch, fill_sync), offsetof(hs_layout, host_layer_stride));
+  printf("%zu %zu %zu %zu %zu\n", offsetof(hs_batch, slot_token), offsetof(hs_batch, slot_stamp),
+         offsetof(hs_batch, fill_sync), offsetof(hs_batch, fill_sync_words),
+         offsetof(hs_layout, host_layer_stride));
   printf("%d\n", HS_FILL_SYNC_WORDS);
   return 0;
 }
@@ -48,12 +49,13 @@ int main(void) {
 def test_struct_mirrors_match_header():
     from serving_memory_tier_amd._lib import HS_FILL_SYNC_WORDS, HsBatch, HsLayout
 
-    lay, bat, o_tok, o_stp, o_sync, o_hls, words = _c_layout()
+    lay, bat, o_tok, o_stp, o_sync, o_words, o_hls, words = _c_layout()
     assert ctypes.sizeof(HsLayout) == lay
     assert ctypes.sizeof(HsBatch) == bat
     assert HsBatch.slot_token.offset == o_tok
     assert HsBatch.slot_stamp.offset == o_stp
     assert HsBatch.fill_sync.offset == o_sync
+    assert HsBatch.fill_sync_words.offset == o_words
     assert HsLayout.host_layer_stride.offset == o_hls
     assert HS_FILL_SYNC_WORDS == words
 
@@ -62,9 +64,10 @@ def test_batch_of_leaves_fill_sync_null_by_default():
     from serving_memory_tier_amd.api import batch_of
 
     b = batch_of(2, 4, None, None, None, None, None, None, None, None)
-    assert b.fill_sync is None
-    b2 = batch_of(2, 4, None, None, None, None, None, None, None, None, fill_sync=0x1000)
-    assert b2.fill_sync == 0x1000
+    assert b.fill_sync is None and b.fill_sync_words == 0
+    b2 = batch_of(2, 4, None, None, None, None, None, None, None, None, fill_sync=0x1000,
+                  fill_sync_words=64)
+    assert b2.fill_sync == 0x1000 and b2.fill_sync_words == 64
 
 
 def test_scratch_guard_reads_resource_remarks():
