@@ -71,10 +71,12 @@ typedef int32_t hs_status;
 /* Limits of the resolver kernel (one workgroup per request-layer, state in LDS). */
 #define HS_MAX_ENTRIES 8192       /* P * K per request-layer */
 #define HS_MAX_HOT_CAPACITY 12288 /* C: up to (speculative tokens + 2) x 2048 for 4 tokens */
+#define HS_MAX_ROW_BYTES 4096     /* row_bytes for the resolving calls (656 here) */
 
 typedef struct {
   int32_t page_size;          /* tokens per page: a power of two, 1..4096 (64 here) */
-  int32_t row_bytes;          /* bytes per KV row: a positive multiple of 16 (656 here) */
+  int32_t row_bytes;          /* bytes per KV row: a positive multiple of 16 (656 here);
+                                 the resolving calls take at most HS_MAX_ROW_BYTES */
   int32_t num_layers;         /* L >= 1 */
   int32_t hot_capacity;       /* C: hot slots per request-layer, a multiple of page_size */
   int64_t pool_rows;          /* rows per layer in kv_pool: multiple of page_size, < 2^31 */

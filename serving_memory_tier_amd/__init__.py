@@ -12,6 +12,7 @@ missing or fails to load, every call raises.
 
 from ._lib import (EXPORTS, HS_ERR_HIP, HS_ERR_INVALID_ARGUMENT, HS_ERR_LAUNCH,
                    HS_ERR_UNSUPPORTED, HS_FILL_SYNC_WORDS, HS_MAX_ENTRIES, HS_MAX_HOT_CAPACITY,
+                   HS_MAX_ROW_BYTES,
                    HS_OK, LIB_PATH, HsBatch, HsError, HsLayout, lib)
 from .api import (HostPool, batch_of, hs_gather, hs_host_alloc, hs_host_device_pointer,
                   hs_host_free, hs_offload_prefix_pages, hs_plan_replay, hs_resolve,
@@ -22,7 +23,7 @@ from .api import (HostPool, batch_of, hs_gather, hs_host_alloc, hs_host_device_p
 
 __all__ = [
     "EXPORTS", "HS_OK", "HS_ERR_INVALID_ARGUMENT", "HS_ERR_UNSUPPORTED", "HS_ERR_LAUNCH",
-    "HS_ERR_HIP", "HS_MAX_ENTRIES", "HS_MAX_HOT_CAPACITY", "HS_FILL_SYNC_WORDS", "LIB_PATH",
+    "HS_ERR_HIP", "HS_MAX_ENTRIES", "HS_MAX_HOT_CAPACITY", "HS_MAX_ROW_BYTES", "HS_FILL_SYNC_WORDS", "LIB_PATH",
     "HsLayout", "HsBatch",
     "HsError", "HostPool", "lib", "layout_of", "batch_of", "hs_resolve", "hs_gather",
     "hs_offload_prefix_pages", "hs_plan_replay", "hs_resolve_grouped", "hs_resolve_decide",

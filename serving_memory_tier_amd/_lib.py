@@ -15,6 +15,7 @@ HS_ERR_LAUNCH = 3
 HS_ERR_HIP = 4
 HS_MAX_ENTRIES = 8192
 HS_MAX_HOT_CAPACITY = 12288
+HS_MAX_ROW_BYTES = 4096
 HS_FILL_SYNC_WORDS = 64
 
 EXPORTS = ("hs_resolve", "hs_gather", "hs_offload_prefix_pages", "hs_plan_replay",

@@ -120,6 +120,7 @@ hs_status check_resolve(const hs_layout* lay, const hs_batch* b, const int32_t* 
   if ((s = check_hot(lay)) != HS_OK) return s;
   if (!b || !topk || !row_ids) return HS_ERR_INVALID_ARGUMENT;
   if (b->num_reqs < 0 || b->max_pages < 1) return HS_ERR_INVALID_ARGUMENT;
+  if (lay->row_bytes > HS_MAX_ROW_BYTES) return HS_ERR_UNSUPPORTED;
   if (b->fill_sync ? b->fill_sync_words < HS_FILL_SYNC_WORDS : b->fill_sync_words != 0)
     return HS_ERR_INVALID_ARGUMENT;
   if (num_pos < 1 || top_k < 1) return HS_ERR_INVALID_ARGUMENT;

@@ -61,8 +61,10 @@ constexpr int kT = kFillThreads;
 constexpr int kU = kCopyUnroll;
 
 // n / pieces for the piece counters of one row size: (n * magic) >> 32 with
-// magic = ceil(2^32 / pieces) is exact for n < 2^32 / pieces, far above any
-// piece count here (entries <= 8192, pieces <= 2^12).
+// magic = ceil(2^32 / pieces) is exact for n < 2^32 / pieces (magic * pieces
+// exceeds 2^32 by less than pieces), above any piece count here: entries
+// <= 8192 and pieces <= 256 (rows of at most 4096 bytes) give n < 2^21,
+// against a bound of 2^24.
 __device__ __forceinline__ int32_t pdiv(int32_t n, uint32_t magic) {
   return (int32_t)(((uint64_t)(uint32_t)n * magic) >> 32);
 }

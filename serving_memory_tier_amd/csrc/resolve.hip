@@ -454,6 +454,7 @@ struct KernelArgs {
   FetchParams fill;  // the fused fill's workgroups (FILL launches)
   int32_t n_rl;
   uint32_t lds_bytes;
+  int32_t interleave;  // FILL: resolvers and gathers alternate in groups of 8 (see below)
 };
 
 // ES: sort elements per thread (kThreads * ES >= N); EC: slots per thread
@@ -464,7 +465,14 @@ struct KernelArgs {
 // miss workgroups first, so that the host-link reads start at once, then one
 // resolver workgroup per request-layer, then the fill's gather workgroups.
 // The two kinds never wait on each other; they share the launch so that the
-// step needs no second stream and no cross-queue join.
+// step needs no second stream and no cross-queue join.  When the resolvers
+// alone would hold more than half of one round of the chip (many
+// request-layers), the resolvers and the gathers alternate in groups of 8
+// workgroups (one a XCD) instead, so that HBM is busy from the start rather
+// than after rounds of resolvers, whose time is latency, not bytes: position
+// j after the miss workgroups is the resolver of rank (resolvers before it)
+// when j % 16 < 8 and resolvers remain, otherwise gather j - (resolvers
+// before it).
 template <int ES, int EC, bool FILL>
 __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -472,11 +480,22 @@ __global__ void __launch_bounds__(kThreads) resolve_kernel(KernelArgs args) {
   if constexpr (FILL) {
     const int32_t b = blockIdx.x;
     const int32_t mg = args.fill.miss_groups;
-    if (b < mg || b >= mg + args.n_rl) {
-      fill::fill_block(args.fill, reinterpret_cast<int32_t*>(lds), b < mg ? b : b - args.n_rl);
+    int32_t fi = b;  // the fill's workgroup index, or -1 for a resolver
+    if (b >= mg) {
+      const int32_t j = b - mg;
+      if (args.interleave) {
+        const int32_t before = min(args.n_rl, (j >> 4) * 8 + min(j & 15, 8));
+        fi = (j & 15) < 8 && before < args.n_rl ? -1 : mg + j - before;
+        rl = before;
+      } else {
+        fi = j < args.n_rl ? -1 : b - args.n_rl;
+        rl = j;
+      }
+    }
+    if (fi >= 0) {
+      fill::fill_block(args.fill, reinterpret_cast<int32_t*>(lds), fi);
       return;
     }
-    rl = b - mg;
   }
   const ResolveParams& p = args.p;
   const LdsPlan& plan = args.plan;
@@ -882,6 +901,13 @@ hipError_t launch_ec(KernelArgs a, int grid, hipStream_t stream) {
       grid = (int)g;
       a.lds_bytes = a.plan.total > flds ? a.plan.total : (uint32_t)flds;
     }
+    // interleave where the resolvers alone would hold more than half a
+    // round of the chip.  Every resolver then has its place: the last one
+    // sits at position 16 * ((n_rl - 1) / 8) + (n_rl - 1) % 8, behind
+    // ((n_rl - 1) / 8) * 8 < n_rl gathers, and there is at least one gather
+    // a request-layer.
+    a.interleave = !a.fill.misses_only && a.fill.gather_splits > 0 &&
+                   2 * (int64_t)a.n_rl > resident ? 1 : 0;
   }
   return launch_kernel(fn, dim3(grid), dim3(kThreads), a.lds_bytes, stream, a);
 }
@@ -946,6 +972,7 @@ hipError_t launch_resolve(const ResolveParams& p, const FetchParams* fill, hipSt
   a.plan = make_plan(p.entries, p.hot_capacity, ES);
   a.n_rl = p.num_reqs * p.num_layers;
   a.lds_bytes = a.plan.total;
+  a.interleave = 0;
   if (a.n_rl == 0) return hipSuccess;
   if (!fill) return launch_rounds<false>(a, a.n_rl, ES, EC, stream);
   a.fill = *fill;

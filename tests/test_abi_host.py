@@ -73,6 +73,7 @@ def _resolve(lib, lay, bat, topk=0x1000, K=2048, stamp=1, rows=0x1000, stats=0x1
 @pytest.mark.parametrize("kw,code", [
     (dict(page_size=48), 1), (dict(page_size=0), 1), (dict(page_size=8192), 1),
     (dict(row_bytes=650), 1), (dict(row_bytes=0), 1), (dict(num_layers=0), 1),
+    (dict(row_bytes=4096 + 16), 2),
     (dict(hot_capacity=100), 1), (dict(hot_capacity=0), 1), (dict(hot_capacity=16384), 2),
     (dict(hot_capacity=12288 + 64), 2),
     (dict(pool_rows=0), 1), (dict(pool_rows=100), 1), (dict(host_rows=-64), 1),

@@ -1,7 +1,8 @@
 """Host checks of the build and of the binding's struct mirrors (no GPU).
 
 - The ctypes mirrors of hs_layout and hs_batch have the sizes and field
-  offsets a C compiler gives the header's structs.
+  offsets a C compiler gives the header's structs, and the binding's limits
+  are the header's.
 - The build's scratch-memory guard reads hipcc's resource remarks: a kernel
   reporting scratch per lane is named, one without is not.
 """
@@ -30,7 +31,7 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu\n", offsetof(hs_batch, slot_token), offsetof(hs_batch, slot_stamp),
          offsetof(hs_batch, fill_sync), offsetof(hs_batch, fill_sync_words),
          offsetof(hs_layout, host_layer_stride));
-  printf("%d\n", HS_FILL_SYNC_WORDS);
+  printf("%d %d %d %d\n", HS_FILL_SYNC_WORDS, HS_MAX_ENTRIES, HS_MAX_HOT_CAPACITY, HS_MAX_ROW_BYTES);
   return 0;
 }
 """
@@ -47,9 +48,10 @@ int main(void) {
 
 
 def test_struct_mirrors_match_header():
-    from serving_memory_tier_amd._lib import HS_FILL_SYNC_WORDS, HsBatch, HsLayout
+    from serving_memory_tier_amd import _lib
 
-    lay, bat, o_tok, o_stp, o_sync, o_words, o_hls, words = _c_layout()
+    HsBatch, HsLayout = _lib.HsBatch, _lib.HsLayout
+    lay, bat, o_tok, o_stp, o_sync, o_words, o_hls, words, n_max, c_max, row_max = _c_layout()
     assert ctypes.sizeof(HsLayout) == lay
     assert ctypes.sizeof(HsBatch) == bat
     assert HsBatch.slot_token.offset == o_tok
@@ -57,7 +59,9 @@ def test_struct_mirrors_match_header():
     assert HsBatch.fill_sync.offset == o_sync
     assert HsBatch.fill_sync_words.offset == o_words
     assert HsLayout.host_layer_stride.offset == o_hls
-    assert HS_FILL_SYNC_WORDS == words
+    assert _lib.HS_FILL_SYNC_WORDS == words
+    assert (_lib.HS_MAX_ENTRIES, _lib.HS_MAX_HOT_CAPACITY, _lib.HS_MAX_ROW_BYTES) == (
+        n_max, c_max, row_max)
 
 
 def test_batch_of_leaves_fill_sync_null_by_default():

@@ -229,6 +229,9 @@ CASES = [
     ("rb1024", 2, 3, 1, 513, 512, 64, 1024, 50, False),
     ("hostile", 4, 2, 3, 600, 2048, 64, 656, 100, True),
     ("hostile_small", 6, 1, 1, 37, 128, 32, 656, 12, True),
+    # more request-layers than CUs: the fused launch interleaves its resolver
+    # and gather workgroups (260 is not a multiple of their groups of 8)
+    ("many_request_layers", 130, 2, 1, 300, 512, 64, 656, 40, False),
 ]
 
 
