@@ -82,7 +82,8 @@ int64_t prepare_fetch(FetchParams& p, size_t* lds_bytes, int64_t gather_target) 
   }
   *lds_bytes = 4 * words;
   const uint32_t pieces = (uint32_t)(p.row_bytes >> 4);
-  p.piece_magic = (uint32_t)(((1ull << 32) + pieces - 1) / pieces);
+  // ceil(2^32 / pieces); 0 for one piece a row, where it would be 2^32
+  p.piece_magic = pieces > 1 ? (uint32_t)(((1ull << 32) + pieces - 1) / pieces) : 0u;
   // miss workgroups: kFetchHostGroups in all (the host reads in flight that
   // saturate the link), split by token when there are few request-layers
   int64_t S = (kFetchHostGroups + n_rl - 1) / n_rl;

@@ -64,9 +64,10 @@ constexpr int kU = kCopyUnroll;
 // magic = ceil(2^32 / pieces) is exact for n < 2^32 / pieces (magic * pieces
 // exceeds 2^32 by less than pieces), above any piece count here: entries
 // <= 8192 and pieces <= 256 (rows of at most 4096 bytes) give n < 2^21,
-// against a bound of 2^24.
+// against a bound of 2^24.  One piece a row (16-byte rows) would need magic
+// 2^32, which a 32-bit word does not hold: magic 0 stands for it.
 __device__ __forceinline__ int32_t pdiv(int32_t n, uint32_t magic) {
-  return (int32_t)(((uint64_t)(uint32_t)n * magic) >> 32);
+  return magic == 0 ? n : (int32_t)(((uint64_t)(uint32_t)n * magic) >> 32);
 }
 
 // The token map: an open-addressing table (linear probing) over the tokens

@@ -227,6 +227,8 @@ CASES = [
     ("page16", 3, 2, 2, 700, 1024, 16, 656, 900, False),
     ("page128_rb64", 3, 1, 1, 1500, 2048, 128, 64, 80, False),
     ("rb1024", 2, 3, 1, 513, 512, 64, 1024, 50, False),
+    # rows of one 16-byte piece (the fill's piece division has no multiplier)
+    ("rb16", 4, 2, 2, 431, 352, 32, 16, 193, True),
     ("hostile", 4, 2, 3, 600, 2048, 64, 656, 100, True),
     ("hostile_small", 6, 1, 1, 37, 128, 32, 656, 12, True),
     # more request-layers than CUs: the fused launch interleaves its resolver
@@ -257,6 +259,52 @@ def test_random_cases(name, R, L, P, K, C, page, rb, n_pages, hostile, mode):
                     pairs[0, 0] = n_blocks + 1
                     pairs[1, 1] = -2
             _compare(case, a, topk, 10 + 3 * step - (step == 3) * 7, pairs=pairs, mode=mode)
+    finally:
+        case.close()
+
+
+def _sweep_shape(seed):
+    """Shape of sweep case ``seed``: page, capacity, batch, positions, list
+    length and row size drawn from the seed, the pools kept under ~48 MB."""
+    rs = np.random.default_rng(1000 + seed)
+    page = int(rs.choice([16, 32, 64, 128]))
+    C = page * int(rs.integers(1, 4096 // page + 1))
+    R = int(rs.integers(1, 13))
+    L = int(rs.integers(1, 4))
+    P = int(rs.choice([1, 1, 2, 3, 4]))
+    K = int(rs.integers(1, min(1500, 8192 // P) + 1))
+    rb = int(rs.choice([656, 656, 16, 48, 1024]))
+    n_pages = max(int(rs.integers(4, 301)), C // page + 1)  # slot tokens come from the span
+    while R > 1 and L * (R * (C // page) + n_pages * R // 2 + 8 + n_pages) * page * rb > 48 << 20:
+        R -= 1
+    return rs, R, L, P, K, C, page, rb, n_pages, bool(seed % 2)
+
+
+SWEEP = list(range(48))
+
+
+@pytest.mark.parametrize("seed", SWEEP)
+def test_random_shapes_sweep(seed):
+    """Random shapes, one stage mode each (the modes in turn), three steps
+    with an offload in the second, hostile tables on odd seeds."""
+    rs, R, L, P, K, C, page, rb, n_pages, hostile = _sweep_shape(seed)
+    mode = stages.MODES[seed % len(stages.MODES)]
+    n_blocks = R * (C // page) + n_pages * R // 2 + 8
+    a = random_arrays(rs, R, L, C, page, rb, n_pages, n_blocks, n_pages, hostile)
+    case = GpuCase(page, a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"], a["hot"],
+                   a["tok"].copy(), a["stp"].copy(), C)
+    try:
+        for step in range(3):
+            _say(f"[edges] sweep {seed} R={R} L={L} P={P} K={K} C={C} page={page} rb={rb} "
+                 f"pages={n_pages} hostile={hostile} {mode} step {step}")
+            lists = random_lists(rs, R, L, P, K, a["ctx"])
+            topk = lists[:, :, 0] if P == 1 else lists
+            pairs = None
+            if step == 1:
+                n = min(4, n_pages)
+                pairs = np.stack([rs.integers(0, n_blocks, n),
+                                  rs.choice(n_pages, n, replace=False)], 1)
+            _compare(case, a, topk, 5 + 2 * step, pairs=pairs, mode=mode)
     finally:
         case.close()
 
