@@ -326,7 +326,7 @@ def test_empty_batch_and_zero_pairs():
         case.close()
 
 
-@pytest.mark.parametrize("rb", [656, 64, 1024])
+@pytest.mark.parametrize("rb", [656, 64, 1024, 16, 48])
 def test_gather_entry_point(rb):
     import serving_memory_tier_amd as hs
     rs = np.random.default_rng(rb)
@@ -343,16 +343,17 @@ def test_gather_entry_point(rb):
     assert np.array_equal(out.cpu().numpy(), oracle.gather(pool, rows))
 
 
-def test_offload_entry_point():
+@pytest.mark.parametrize("page,rb", [(64, 656), (16, 16), (128, 48), (32, 1024)])
+def test_offload_entry_point(page, rb):
     import serving_memory_tier_amd as hs
-    rs = np.random.default_rng(9)
+    rs = np.random.default_rng(9 + page + rb)
     L, nb, nh = 4, 40, 30
-    pool = rs.integers(0, 256, size=(L, nb * 64, 656), dtype=np.uint8)
-    host = rs.integers(0, 256, size=(L, nh * 64, 656), dtype=np.uint8)
+    pool = rs.integers(0, 256, size=(L, nb * page, rb), dtype=np.uint8)
+    host = rs.integers(0, 256, size=(L, nh * page, rb), dtype=np.uint8)
     pairs = np.stack([rs.integers(0, nb, 12), rs.choice(nh, 12, replace=False)], 1).astype(np.int32)
     pairs[3] = [nb, 2]
     pairs[4] = [1, -1]
-    lay = hs.layout_of(64, 656, L, 64, nb * 64, nh * 64)
+    lay = hs.layout_of(page, rb, L, page, nb * page, nh * page)
     gp = torch.from_numpy(pool).cuda()
     hp = hs.HostPool(host.size)
     try:
@@ -360,7 +361,7 @@ def test_offload_entry_point():
         hv.copy_(torch.from_numpy(host))
         hs.hs_offload_prefix_pages(lay, gp, hp, torch.from_numpy(pairs).cuda(), 12)
         torch.cuda.synchronize()
-        oracle.offload(pool, host, pairs)
+        oracle.offload(pool, host, pairs, page=page)
         assert np.array_equal(hv.numpy(), host)
         assert np.array_equal(gp.cpu().numpy(), pool)
     finally:
@@ -383,8 +384,12 @@ GROUPED = [
 def test_random_grouped_cases(name, R, L, G, P, K, C, page, rb, n_pages, hostile, gather):
     """hs_resolve_grouped against the oracle's grouped resolve: state and lists
     per layer group, copies and gathered rows per layer."""
-    import serving_memory_tier_amd as hs
     rs = np.random.default_rng(zlib.crc32(name.encode()))
+    _run_grouped(rs, R, L, G, P, K, C, page, rb, n_pages, hostile, gather, name)
+
+
+def _run_grouped(rs, R, L, G, P, K, C, page, rb, n_pages, hostile, gather, label):
+    import serving_memory_tier_amd as hs
     n_blocks = R * (C // page) + n_pages * R // 2 + 8
     a = random_arrays(rs, R, L, C, page, rb, n_pages, n_blocks, n_pages, hostile)
     NG = L // G
@@ -394,7 +399,7 @@ def test_random_grouped_cases(name, R, L, G, P, K, C, page, rb, n_pages, hostile
                    a["tok"].copy(), a["stp"].copy(), C)
     try:
         for step in range(3):
-            _say(f"[edges] grouped {name} gather={gather} step {step}")
+            _say(f"[edges] grouped {label} gather={gather} step {step}")
             lists = random_lists(rs, R, NG, P, K, a["ctx"])
             topk = np.ascontiguousarray(lists[:, :, 0] if P == 1 else lists)
             stamp = 5 + 2 * step
@@ -418,6 +423,35 @@ def test_random_grouped_cases(name, R, L, G, P, K, C, page, rb, n_pages, hostile
             assert np.array_equal(pool, a["pool"])
     finally:
         case.close()
+
+
+def _grouped_sweep_shape(seed):
+    """Shape of grouped sweep case ``seed``, the pools kept under ~48 MB."""
+    rs = np.random.default_rng(5000 + seed)
+    page = int(rs.choice([16, 32, 64]))
+    C = page * int(rs.integers(1, 2048 // page + 1))
+    G = int(rs.integers(2, 5))
+    L = G * int(rs.integers(1, 4))
+    R = int(rs.integers(1, 9))
+    P = int(rs.choice([1, 1, 2]))
+    K = int(rs.integers(1, 1001))
+    rb = int(rs.choice([656, 656, 16, 48, 1024]))
+    n_pages = max(int(rs.integers(4, 201)), C // page + 1)  # slot tokens come from the span
+    while R > 1 and L * (R * (C // page) + n_pages * R // 2 + 8 + n_pages) * page * rb > 48 << 20:
+        R -= 1
+    return rs, R, L, G, P, K, C, page, rb, n_pages, bool(seed % 2), seed % 3 != 0
+
+
+GROUPED_SWEEP = list(range(24))
+
+
+@pytest.mark.parametrize("seed", GROUPED_SWEEP)
+def test_random_grouped_sweep(seed):
+    """Random shapes for hs_resolve_grouped (groups of 2-4 layers, 1-3 groups,
+    rows of 16 to 1024 bytes), with and without the gathered output."""
+    rs, R, L, G, P, K, C, page, rb, n_pages, hostile, gather = _grouped_sweep_shape(seed)
+    _run_grouped(rs, R, L, G, P, K, C, page, rb, n_pages, hostile, gather,
+                 f"sweep {seed} R={R} L={L} G={G} P={P} K={K} C={C} page={page} rb={rb}")
 
 
 @pytest.mark.parametrize("mode", stages.MODES)
