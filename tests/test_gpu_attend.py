@@ -109,6 +109,37 @@ def test_sparse_mla_matches_oracle(name):
     check(pool, ids, q, 1.0 / math.sqrt(576))
 
 
+def _sweep_case(seed):
+    """Shape and value ranges of attention sweep case ``seed``: tokens, heads
+    (multiples of 16), selected rows, pool size, query scale, the share of
+    unselected or out-of-range ids, and the latent values' largest exponent."""
+    rs = np.random.default_rng(7000 + seed)
+    T = int(rs.integers(1, 7))
+    H = 16 * int(rs.integers(1, 9))
+    K = int(rs.integers(1, 3001))
+    while T > 1 and T * H * K > 1_500_000:
+        T -= 1
+    n = int(rs.integers(K // 2 + 1, 4001))
+    mult = float(rs.choice([0.5, 1.0, 3.0, 8.0]))
+    bad = float(rs.choice([0.0, 0.02, 0.2, 0.9]))
+    max_exp = int(rs.choice([6, 8, 14]))
+    return rs, T, H, K, n, mult, bad, max_exp
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_sparse_mla_sweep(seed):
+    """Random shapes: 1-6 tokens, 16-128 heads, 1-3000 selected rows (so 1 to
+    many key splits and ragged last blocks), query scales up to 8 (peaky
+    scores), up to 90 % of the ids unselected or out of range."""
+    rs, T, H, K, n, mult, bad, max_exp = _sweep_case(seed)
+    pool = make_pool(rs, n, max_exp=max_exp)
+    q = make_q(rs, T, H, mult)
+    ids = rs.integers(0, n, size=(T, K)).astype(np.int32)
+    m = rs.random((T, K)) < bad
+    ids[m] = rs.choice(np.array([-1, -2, -3, n, n + 5], np.int32), size=int(m.sum()))
+    check(pool, ids, q, 1.0 / math.sqrt(576))
+
+
 def test_nothing_selected_and_empty_lists():
     rs = np.random.default_rng(7)
     pool = make_pool(rs, 10)

@@ -43,7 +43,7 @@ def _say(msg):
 class GpuCase:
     """One batch in device memory, built from the same numpy arrays the oracle gets."""
 
-    def __init__(self, page, pool, host, bt, hbt, ctx, hot, tok, stp, C):
+    def __init__(self, page, pool, host, bt, hbt, ctx, hot, tok, stp, C, fill_sync=False):
         import serving_memory_tier_amd as hs
         self.hs = hs
         L, pool_rows, rb = pool.shape
@@ -60,8 +60,11 @@ class GpuCase:
         self.tok = torch.from_numpy(tok).cuda()
         self.stp = torch.from_numpy(stp.view(np.int32)).cuda()
         self.layout = hs.layout_of(page, rb, L, C, pool_rows, host_rows)
+        # the early fill's work counters (zeroed once; every call leaves them zero)
+        self.sync = (torch.zeros(hs.HS_FILL_SYNC_WORDS, dtype=torch.int32, device="cuda")
+                     if fill_sync else None)
         self.batch = hs.batch_of(bt.shape[0], bt.shape[1], self.pool, self.host_pool, self.bt,
-                                 self.hbt, self.ctx, self.hot, self.tok, self.stp)
+                                 self.hbt, self.ctx, self.hot, self.tok, self.stp, self.sync)
 
     def resolve(self, topk: np.ndarray, stamp: int, gather=True, pairs=None, mode="call"):
         R, L = topk.shape[:2]
@@ -286,17 +289,19 @@ SWEEP = list(range(48))
 @pytest.mark.parametrize("seed", SWEEP)
 def test_random_shapes_sweep(seed):
     """Random shapes, one stage mode each (the modes in turn), three steps
-    with an offload in the second, hostile tables on odd seeds."""
+    with an offload in the second, hostile tables on odd seeds, the early
+    fill's work counters on half the seeds."""
     rs, R, L, P, K, C, page, rb, n_pages, hostile = _sweep_shape(seed)
     mode = stages.MODES[seed % len(stages.MODES)]
     n_blocks = R * (C // page) + n_pages * R // 2 + 8
     a = random_arrays(rs, R, L, C, page, rb, n_pages, n_blocks, n_pages, hostile)
+    sync = seed % 4 >= 2
     case = GpuCase(page, a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"], a["hot"],
-                   a["tok"].copy(), a["stp"].copy(), C)
+                   a["tok"].copy(), a["stp"].copy(), C, fill_sync=sync)
     try:
         for step in range(3):
             _say(f"[edges] sweep {seed} R={R} L={L} P={P} K={K} C={C} page={page} rb={rb} "
-                 f"pages={n_pages} hostile={hostile} {mode} step {step}")
+                 f"pages={n_pages} hostile={hostile} fill_sync={sync} {mode} step {step}")
             lists = random_lists(rs, R, L, P, K, a["ctx"])
             topk = lists[:, :, 0] if P == 1 else lists
             pairs = None
@@ -305,6 +310,8 @@ def test_random_shapes_sweep(seed):
                 pairs = np.stack([rs.integers(0, n_blocks, n),
                                   rs.choice(n_pages, n, replace=False)], 1)
             _compare(case, a, topk, 5 + 2 * step, pairs=pairs, mode=mode)
+            if sync:
+                assert int(torch.count_nonzero(case.sync)) == 0, "work counters left set"
     finally:
         case.close()
 
