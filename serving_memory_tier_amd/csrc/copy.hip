@@ -189,18 +189,29 @@ __global__ void __launch_bounds__(kT) commit_kernel(MoveParams p, int32_t chunks
   uint8_t* slot0 = p.pool_w + (int64_t)l0 * p.pool_stride;
   int32_t* stok = p.slot_token + (int64_t)rl * p.hot_capacity;
 
+  // the codes, the entries' tokens and (up to 64 of them) the request's hot
+  // blocks are loaded together, so a miss's slot row waits on one load
   const int32_t code = lane < ne ? rows[lane] : 0;
+  const int32_t tk = lane < ne ? topk[lane] : -1;
+  const int32_t nhb = p.hot_capacity >> ps;
+  const bool hot_in_lanes = nhb <= 64;  // the same for the whole launch
+  const int32_t hreg = hot_in_lanes && lane < nhb ? hot[lane] : -1;
+  const int32_t qq = code <= -8 ? (-code - 8) >> 1 : 0;
+  // every lane takes part in the exchange; lanes without a miss read lane 0
+  const int32_t hlane = hot_in_lanes
+      ? __builtin_amdgcn_ds_bpermute(((qq < p.hot_capacity ? qq >> ps : 0) & 63) << 2, hreg)
+      : -1;
   int32_t drow = -1;  // the slot's pool row, for a first entry
   bool copier = false;
   if (code <= -8) {
-    const int32_t q = (-code - 8) >> 1;
+    const int32_t q = qq;
     if (q < p.hot_capacity) {
-      const int32_t hblk = hot[q >> ps];
+      const int32_t hblk = hot_in_lanes ? hlane : hot[q >> ps];
       const int32_t row = (hblk << ps) | (q & pm);
       copier = ((-code - 8) & 1) != 0 && hblk >= 0 && hblk < (p.pool_rows >> ps);
       if (copier) {
         drow = row;
-        stok[q] = topk[lane];
+        stok[q] = tk;
       }
       rows[lane] = row;
     } else {
