@@ -316,6 +316,55 @@ def test_random_shapes_sweep(seed):
         case.close()
 
 
+def _wide_shape(seed):
+    """A launch of 130-400 request-layers with short lists: more workgroups
+    than the chip holds at once (interleaved resolvers and gathers, miss
+    workgroups taking many items), rows sized to keep the pools small."""
+    rs = np.random.default_rng(9000 + seed)
+    page = int(rs.choice([16, 64]))
+    C = page * int(rs.integers(1, 1024 // page + 1))
+    L = int(rs.integers(1, 4))
+    R = int(rs.integers(130 // L + 1, 400 // L + 1))
+    P = int(rs.choice([1, 2]))
+    K = int(rs.integers(1, 301))
+    n_pages = max(int(rs.integers(4, 40)), C // page + 1)
+    rb = 656
+    for cand in (656, 48, 16):
+        rb = cand
+        if L * (R * (C // page) + n_pages * R // 2 + 8 + n_pages) * page * rb <= 64 << 20:
+            break
+    return rs, R, L, P, K, C, page, rb, n_pages
+
+
+@pytest.mark.parametrize("seed", list(range(10)))
+def test_wide_launch_sweep(seed):
+    """Random wide launches in every stage mode (the modes in turn), half with
+    the fill's work counters, three steps with an offload in the second."""
+    rs, R, L, P, K, C, page, rb, n_pages = _wide_shape(seed)
+    mode = stages.MODES[seed % len(stages.MODES)]
+    n_blocks = R * (C // page) + n_pages * R // 2 + 8
+    a = random_arrays(rs, R, L, C, page, rb, n_pages, n_blocks, n_pages, seed % 3 == 2)
+    sync = seed % 2 == 1
+    case = GpuCase(page, a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"], a["hot"],
+                   a["tok"].copy(), a["stp"].copy(), C, fill_sync=sync)
+    try:
+        for step in range(3):
+            _say(f"[edges] wide {seed} R={R} L={L} P={P} K={K} C={C} page={page} rb={rb} "
+                 f"fill_sync={sync} {mode} step {step}")
+            lists = random_lists(rs, R, L, P, K, a["ctx"])
+            topk = lists[:, :, 0] if P == 1 else lists
+            pairs = None
+            if step == 1:
+                n = min(4, n_pages)
+                pairs = np.stack([rs.integers(0, n_blocks, n),
+                                  rs.choice(n_pages, n, replace=False)], 1)
+            _compare(case, a, topk, 5 + 2 * step, pairs=pairs, mode=mode)
+            if sync:
+                assert int(torch.count_nonzero(case.sync)) == 0, "work counters left set"
+    finally:
+        case.close()
+
+
 def test_empty_batch_and_zero_pairs():
     import serving_memory_tier_amd as hs
     a = random_arrays(np.random.default_rng(1), 1, 1, 64, 64, 656, 4, 8, 4)
