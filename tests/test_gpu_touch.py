@@ -31,7 +31,7 @@ def _lib():
     hs.lib()
 
 
-def _gpu_touch(ctx, topk, stamp, use, entries=None):
+def _gpu_touch(ctx, topk, stamp, use, entries=None, page=PAGE):
     """hs_page_touch on device copies of the inputs; use is updated in place."""
     import serving_memory_tier_amd as hs
     R, mp = use.shape
@@ -39,7 +39,7 @@ def _gpu_touch(ctx, topk, stamp, use, entries=None):
     t = torch.from_numpy(np.ascontiguousarray(topk, np.int32).reshape(R, -1)).cuda()
     u = torch.from_numpy(use).cuda()
     E = t.shape[1] if entries is None else entries
-    lay = hs.layout_of(PAGE, hs_gen.ROW_BYTES, 1, 512, PAGE, 0)
+    lay = hs.layout_of(page, hs_gen.ROW_BYTES, 1, max(512, page), page, 0)
     batch = hs.HsBatch(R, mp, None, None, None, None, c.data_ptr(), None, None, None)
     print(f"[touch] R={R} max_pages={mp} entries={E} stamp={stamp}", flush=True)
     hs.hs_page_touch(lay, batch, t if t.numel() else None, E, stamp, u)
@@ -74,6 +74,26 @@ def test_page_touch_matches_oracle(name):
     _gpu_touch(ctx, topk, 0xFFFFFFF0, got)
     assert np.array_equal(got, exp)
     assert not np.array_equal(got, use0)
+
+
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_page_touch_sweep(seed):
+    """Random page sizes (1 to 4096 tokens), batches, table lengths and list
+    lengths (0 to 5000), stamps anywhere in 32 bits."""
+    rs = np.random.default_rng(3000 + seed)
+    page = int(rs.choice([1, 16, 64, 256, 4096]))
+    R = int(rs.integers(1, 41))
+    mp = int(rs.integers(1, 501))
+    E = int(rs.integers(0, 5001))
+    ctx = rs.integers(1, (mp + 3) * page + 1, size=R).astype(np.int32)
+    topk = rs.integers(-3, (mp + 4) * page, size=(R, E)).astype(np.int32)
+    use0 = rs.integers(0, 1 << 32, size=(R, mp), dtype=np.uint64).astype(np.uint32)
+    stamp = int(rs.integers(1, 1 << 32, dtype=np.uint64))
+    exp = use0.copy()
+    oracle.page_touch(ctx, topk, stamp, exp, page=page)
+    got = use0.copy()
+    _gpu_touch(ctx, topk, stamp, got, page=page)
+    assert np.array_equal(got, exp)
 
 
 def test_page_touch_with_nothing_to_do_changes_nothing():
