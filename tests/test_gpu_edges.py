@@ -232,6 +232,10 @@ CASES = [
     ("rb1024", 2, 3, 1, 513, 512, 64, 1024, 50, False),
     # rows of one 16-byte piece (the fill's piece division has no multiplier)
     ("rb16", 4, 2, 2, 431, 352, 32, 16, 193, True),
+    # pages of one token and of 1024 and 4096 tokens
+    ("page1", 3, 1, 1, 200, 64, 1, 656, 400, False),
+    ("page1024", 3, 1, 1, 700, 2048, 1024, 16, 12, False),
+    ("page4096_hostile", 2, 2, 2, 500, 4096, 4096, 48, 5, True),
     ("hostile", 4, 2, 3, 600, 2048, 64, 656, 100, True),
     ("hostile_small", 6, 1, 1, 37, 128, 32, 656, 12, True),
     # more request-layers than CUs: the fused launch interleaves its resolver
