@@ -48,6 +48,9 @@
  *              pad, dup, 0}; the first five count distinct tokens, pad and
  *              dup count entries; they always sum to P * K.
  *   gather_out uint8 [R][L][P][K][row_bytes].
+ *   kv_pool, host_pool, gather_out and the staging buffer start on 16-byte
+ *   boundaries, and with L > 1 both layer strides are multiples of 16 (the
+ *   kernels move 16-byte pieces); otherwise HS_ERR_INVALID_ARGUMENT.
  */
 #ifndef HISPARSE_H
 #define HISPARSE_H

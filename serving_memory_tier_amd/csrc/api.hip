@@ -22,6 +22,10 @@ int log2i(int64_t x) {
   return s;
 }
 
+// The kernels move 16-byte pieces: pools, outputs and layer strides are
+// 16-byte aligned.
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
 // Checks shared by every call that reads the pool layout.
 hs_status check_layout(const hs_layout* lay) {
   if (!lay) return HS_ERR_INVALID_ARGUMENT;
@@ -36,6 +40,8 @@ hs_status check_layout(const hs_layout* lay) {
   if (lay->num_layers > 1) {
     if (lay->pool_layer_stride < lay->pool_rows * lay->row_bytes) return HS_ERR_INVALID_ARGUMENT;
     if (lay->host_layer_stride < lay->host_rows * lay->row_bytes) return HS_ERR_INVALID_ARGUMENT;
+    if (lay->pool_layer_stride % 16 != 0 || lay->host_layer_stride % 16 != 0)
+      return HS_ERR_INVALID_ARGUMENT;
   }
   return HS_OK;
 }
@@ -135,6 +141,7 @@ hs_status check_resolve(const hs_layout* lay, const hs_batch* b, const int32_t* 
         !b->hot_blocks || !b->slot_token || !b->slot_stamp)
       return HS_ERR_INVALID_ARGUMENT;
     if (!b->host_pool && lay->host_rows > 0) return HS_ERR_INVALID_ARGUMENT;
+    if (!aligned16(b->kv_pool) || !aligned16(b->host_pool)) return HS_ERR_INVALID_ARGUMENT;
   }
   return HS_OK;
 }
@@ -262,6 +269,7 @@ hs_status resolve_common(const hs_layout* lay, const hs_batch* b, const int32_t*
   if (s != HS_OK) return s;
   if (group < 1 || lay->num_layers % group != 0) return HS_ERR_INVALID_ARGUMENT;
   if (!stats || stamp == 0) return HS_ERR_INVALID_ARGUMENT;
+  if (!aligned16(gather_out) || !aligned16(staging)) return HS_ERR_INVALID_ARGUMENT;
   if ((s = check_offload(n_offload)) != HS_OK) return s;
   if (n_offload > 0 && (!offload_pairs || !b->kv_pool || !b->host_pool))
     return HS_ERR_INVALID_ARGUMENT;
@@ -335,6 +343,7 @@ hs_status hs_resolve_decide(const hs_layout* layout, const hs_batch* batch, cons
   hs_status s = check_resolve(layout, batch, topk, num_pos, top_k, row_ids);
   if (s != HS_OK) return s;
   if (!stats || stamp == 0) return HS_ERR_INVALID_ARGUMENT;
+  if (!aligned16(gather_out)) return HS_ERR_INVALID_ARGUMENT;
   const int32_t N = num_pos * top_k;
   if (gather_out && !fetch_fits(layout, N)) return HS_ERR_UNSUPPORTED;
   return launch_decide(layout, batch, topk, N, stamp, row_ids, stats, stream, gather_out);
@@ -345,7 +354,7 @@ hs_status hs_resolve_fetch(const hs_layout* layout, const hs_batch* batch, const
                            hipStream_t stream) {
   hs_status s = check_resolve(layout, batch, topk, num_pos, top_k, topk);
   if (s != HS_OK) return s;
-  if (!gather_out) return HS_ERR_INVALID_ARGUMENT;
+  if (!gather_out || !aligned16(gather_out)) return HS_ERR_INVALID_ARGUMENT;
   if (!fetch_fits(layout, num_pos * top_k)) return HS_ERR_UNSUPPORTED;
   return launch_fetch(layout, batch, topk, num_pos * top_k, gather_out, stream);
 }
@@ -355,6 +364,7 @@ hs_status hs_resolve_move(const hs_layout* layout, const hs_batch* batch, const 
                           hipStream_t stream) {
   hs_status s = check_resolve(layout, batch, topk, num_pos, top_k, row_ids);
   if (s != HS_OK) return s;
+  if (!aligned16(gather_out)) return HS_ERR_INVALID_ARGUMENT;
   return launch_move_mode(layout, batch, topk, num_pos * top_k, row_ids, gather_out,
                           hs::kMoveFused, stream);
 }
@@ -364,7 +374,7 @@ hs_status hs_resolve_commit(const hs_layout* layout, const hs_batch* batch, cons
                             uint8_t* gather_out, hipStream_t stream) {
   hs_status s = check_resolve(layout, batch, topk, num_pos, top_k, row_ids);
   if (s != HS_OK) return s;
-  if (!gather_out) return HS_ERR_INVALID_ARGUMENT;
+  if (!gather_out || !aligned16(gather_out)) return HS_ERR_INVALID_ARGUMENT;
   return launch_move_mode(layout, batch, topk, num_pos * top_k, row_ids, gather_out,
                           hs::kMoveCommit, stream);
 }
@@ -378,6 +388,7 @@ hs_status hs_gather(const hs_layout* layout, const uint8_t* kv_pool, const int32
   const int64_t n_rl = (int64_t)num_reqs * layout->num_layers;
   if (n_rl == 0 || rows_per_req_layer == 0) return HS_OK;
   if (!kv_pool || !row_ids || !out) return HS_ERR_INVALID_ARGUMENT;
+  if (!aligned16(kv_pool) || !aligned16(out)) return HS_ERR_INVALID_ARGUMENT;
   if ((s = check_gather(layout, n_rl, rows_per_req_layer)) != HS_OK) return s;
   return from_hip(hs::launch_move(
       move_params(layout, kv_pool, const_cast<int32_t*>(row_ids), num_reqs, rows_per_req_layer,
@@ -393,6 +404,7 @@ hs_status hs_offload_prefix_pages(const hs_layout* layout, const uint8_t* kv_poo
   if ((s = check_offload(n)) != HS_OK) return s;
   if (n == 0) return HS_OK;
   if (!kv_pool || !host_pool || !pairs) return HS_ERR_INVALID_ARGUMENT;
+  if (!aligned16(kv_pool) || !aligned16(host_pool)) return HS_ERR_INVALID_ARGUMENT;
   return from_hip(hs::launch_offload(offload_params(layout, kv_pool, host_pool, pairs, n), stream),
                   "offload launch");
 }
@@ -434,7 +446,6 @@ hs::AttendParams attend_plan(int32_t num_tokens, int32_t num_heads, int32_t top_
   return p;
 }
 
-bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 }  // namespace
 

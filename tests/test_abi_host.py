@@ -79,9 +79,28 @@ def _resolve(lib, lay, bat, topk=0x1000, K=2048, stamp=1, rows=0x1000, stats=0x1
     (dict(pool_rows=0), 1), (dict(pool_rows=100), 1), (dict(host_rows=-64), 1),
     (dict(pool_rows=1 << 31), 1),
     (dict(num_layers=2, pool_layer_stride=10), 1),
+    (dict(num_layers=2, pool_layer_stride=64 * 100 * 656 + 8), 1),
+    (dict(num_layers=2, host_layer_stride=64 * 100 * 656 + 24), 1),
 ])
 def test_resolve_rejects_bad_layout(lib, kw, code):
     assert _resolve(lib, _layout(**kw), _batch()) == code
+
+
+def test_rejects_misaligned_buffers(lib):
+    lay = _layout()
+    b = _batch()
+    b.kv_pool = 0x1008
+    assert _resolve(lib, lay, b) == 1
+    b = _batch()
+    b.host_pool = 0x1004
+    assert _resolve(lib, lay, b) == 1
+    ok = _batch()
+    r = lambda out: lib.hs_resolve(ctypes.byref(lay), ctypes.byref(ok), 0x1000, 2048,
+                                   ctypes.c_uint32(1), 0x1000, out, 0x1000, None)
+    assert r(0x1008) == 1
+    assert lib.hs_gather(ctypes.byref(lay), 0x1008, 0x1000, 2, 16, 0x1000, None) == 1
+    assert lib.hs_gather(ctypes.byref(lay), 0x1000, 0x1000, 2, 16, 0x1001, None) == 1
+    assert lib.hs_offload_prefix_pages(ctypes.byref(lay), 0x1000, 0x1004, 0x1000, 3, None) == 1
 
 
 def test_resolve_rejects_bad_call(lib):

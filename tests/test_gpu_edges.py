@@ -43,15 +43,24 @@ def _say(msg):
 class GpuCase:
     """One batch in device memory, built from the same numpy arrays the oracle gets."""
 
-    def __init__(self, page, pool, host, bt, hbt, ctx, hot, tok, stp, C, fill_sync=False):
+    def __init__(self, page, pool, host, bt, hbt, ctx, hot, tok, stp, C, fill_sync=False,
+                 pad=0):
         import serving_memory_tier_amd as hs
         self.hs = hs
         L, pool_rows, rb = pool.shape
         host_rows = host.shape[1]
         self.page, self.rb, self.L, self.C = page, rb, L, C
-        self.pool = torch.from_numpy(pool).cuda()
-        self.host_pool = hs.HostPool(max(1, host.size))
-        self.host = self.host_pool.tensor[:host.size].view(host.shape)
+        # pad > 0: every layer of both pools is followed by `pad` bytes of
+        # 0xA5 that no call may touch (layer strides past the rows)
+        self.pad = pad
+        ps, hs_ = pool_rows * rb + pad, host_rows * rb + pad
+        self.pool_flat = torch.full((L * ps,), 0xA5, dtype=torch.uint8, device="cuda")
+        self.pool = torch.as_strided(self.pool_flat, (L, pool_rows, rb), (ps, rb, 1))
+        self.pool.copy_(torch.from_numpy(pool))
+        self.host_pool = hs.HostPool(max(1, L * hs_))
+        self.host_flat = self.host_pool.tensor[:L * hs_]
+        self.host_flat.fill_(0xA5)
+        self.host = torch.as_strided(self.host_flat, (L, host_rows, rb), (hs_, rb, 1))
         self.host.copy_(torch.from_numpy(host))
         self.bt = torch.from_numpy(bt).cuda()
         self.hbt = torch.from_numpy(hbt).cuda()
@@ -59,11 +68,11 @@ class GpuCase:
         self.hot = torch.from_numpy(hot).cuda()
         self.tok = torch.from_numpy(tok).cuda()
         self.stp = torch.from_numpy(stp.view(np.int32)).cuda()
-        self.layout = hs.layout_of(page, rb, L, C, pool_rows, host_rows)
+        self.layout = hs.layout_of(page, rb, L, C, pool_rows, host_rows, ps, hs_)
         # the early fill's work counters (zeroed once; every call leaves them zero)
         self.sync = (torch.zeros(hs.HS_FILL_SYNC_WORDS, dtype=torch.int32, device="cuda")
                      if fill_sync else None)
-        self.batch = hs.batch_of(bt.shape[0], bt.shape[1], self.pool, self.host_pool, self.bt,
+        self.batch = hs.batch_of(bt.shape[0], bt.shape[1], self.pool_flat, self.host_pool, self.bt,
                                  self.hbt, self.ctx, self.hot, self.tok, self.stp, self.sync)
 
     def resolve(self, topk: np.ndarray, stamp: int, gather=True, pairs=None, mode="call"):
@@ -83,11 +92,17 @@ class GpuCase:
                 None if out is None else out.cpu().numpy())
 
     def state(self):
+        if self.pad:
+            L = self.L
+            for flat in (self.pool_flat.cpu(), self.host_flat):
+                gaps = flat.view(L, -1)[:, -self.pad:]
+                assert bool((gaps == 0xA5).all()), "bytes past a layer's rows were written"
         return (self.tok.cpu().numpy(), self.stp.cpu().numpy().view(np.uint32),
                 self.pool.cpu().numpy(), self.host.numpy().copy())
 
     def close(self):
         self.host = None
+        self.host_flat = None
         self.host_pool.close()
 
 
@@ -365,6 +380,30 @@ def test_wide_launch_sweep(seed):
             _compare(case, a, topk, 5 + 2 * step, pairs=pairs, mode=mode)
             if sync:
                 assert int(torch.count_nonzero(case.sync)) == 0, "work counters left set"
+    finally:
+        case.close()
+
+
+@pytest.mark.parametrize("mode", stages.MODES)
+def test_padded_layer_strides(mode):
+    """Both pools with layer strides past their rows (4,112 bytes of
+    untouchable bytes after every layer): rows, stats, gathered bytes, state
+    and both pools as the oracle's, and the gaps unwritten, through every
+    path, offload included."""
+    rs = np.random.default_rng(zlib.crc32(f"padded-{mode}".encode()))
+    R, L, P, K, C, page, rb, n_pages = 3, 3, 2, 300, 512, 32, 656, 40
+    n_blocks = R * (C // page) + n_pages * R // 2 + 8
+    a = random_arrays(rs, R, L, C, page, rb, n_pages, n_blocks, n_pages, True)
+    case = GpuCase(page, a["pool"], a["host"], a["bt"], a["hbt"], a["ctx"], a["hot"],
+                   a["tok"].copy(), a["stp"].copy(), C, pad=4112)
+    try:
+        for step in range(3):
+            _say(f"[edges] padded strides {mode} step {step}")
+            topk = random_lists(rs, R, L, P, K, a["ctx"])
+            pairs = None
+            if step == 1:
+                pairs = np.stack([rs.integers(0, n_blocks, 4), rs.choice(n_pages, 4, replace=False)], 1)
+            _compare(case, a, topk, 5 + 2 * step, pairs=pairs, mode=mode)
     finally:
         case.close()
 
