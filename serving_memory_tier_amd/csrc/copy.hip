@@ -57,97 +57,85 @@ __global__ void __launch_bounds__(kT) move_kernel(MoveParams p, int32_t chunks_p
   const int64_t out_stride = (int64_t)N * p.row_bytes;  // between layers of the output
   constexpr bool kSlots = MODE == kMoveFused;
 
-  const int32_t* topk = nullptr;
-  const int32_t* hbt = nullptr;
-  const int32_t* hot = nullptr;
-  const uint8_t* host_l = nullptr;
-  uint8_t* slot_l = nullptr;
-  int32_t* stok = nullptr;
-  int64_t host_blocks = 0;
-  if (kSlots) {
-    topk = p.topk + (int64_t)rl * N + e0;
-    hot = p.hot_blocks + (int64_t)r * (p.hot_capacity >> ps);
-    stok = p.slot_token + (int64_t)rl * p.hot_capacity;
-  }
-  if (MODE == kMoveFused) {
-    hbt = p.host_block_table + (int64_t)r * p.max_pages;
-    host_blocks = p.host_rows >> ps;
+  // Each entry is resolved once, by lane `entry` of the wave, before any row
+  // moves: its code and token are loaded together, then its host block and
+  // its slot's hot block together; the piece loop below takes an entry's
+  // source and slot rows from that lane (ds_bpermute), so a piece's load
+  // waits on nothing but its address.
+  //   kind 0: zero row (or nothing without an output); 1: pool row; 2: host row
+  const bool has_e = lane < ne;
+  const int32_t code = has_e ? rows[lane] : 0;
+  const int32_t t = kSlots && has_e ? p.topk[(int64_t)rl * N + e0 + lane] : -1;
+  int32_t kind = 0, src = 0, drow = -1;  // drow: the slot's pool row, for a first entry
+  int32_t hblk = -1;                     // the slot's hot block, for an assigned miss
+  const int32_t q = code <= -8 ? (-code - 8) >> 1 : 0;
+  const bool copier = code <= -8 && ((-code - 8) & 1) != 0;
+  if (code >= 0) {
+    if (p.out && code < p.pool_rows) { kind = 1; src = code; }
+  } else if (kSlots && code <= -8 && q < p.hot_capacity) {
+    const int32_t* hot = p.hot_blocks + (int64_t)r * (p.hot_capacity >> ps);
+    hblk = hot[q >> ps];
+    int32_t hb = -1;
+    if (t >= 0 && (t >> ps) < p.max_pages) hb = p.host_block_table[(int64_t)r * p.max_pages + (t >> ps)];
+    if ((p.out || copier) && hb >= 0 && hb < (p.host_rows >> ps)) {
+      kind = 2;
+      src = (hb << ps) | (t & pm);
+      if (copier && hblk >= 0 && hblk < (p.pool_rows >> ps)) drow = (hblk << ps) | (q & pm);
+    }
   }
 
   for (int32_t lj = 0; lj < group; ++lj) {  // each layer of the group
-  const int32_t layer = l0 + lj;
-  const uint8_t* pool_l = p.pool + (int64_t)layer * p.pool_stride;
-  uint8_t* out = p.out ? p.out + ((int64_t)r * layers + layer) * out_stride +
-                             (int64_t)e0 * p.row_bytes
-                       : nullptr;
-  if (kSlots) slot_l = p.pool_w + (int64_t)layer * p.pool_stride;
-  if (MODE == kMoveFused) host_l = p.host + (int64_t)layer * p.host_stride;
-  for (int32_t base = 0; base < npieces; base += 64 * kU) {
-    u32x4 v[kU];
-    uint8_t* slot_dst[kU];
-    bool st[kU];
+    const int32_t layer = l0 + lj;
+    const uint8_t* pool_l = p.pool + (int64_t)layer * p.pool_stride;
+    uint8_t* out = p.out ? p.out + ((int64_t)r * layers + layer) * out_stride +
+                               (int64_t)e0 * p.row_bytes
+                         : nullptr;
+    uint8_t* slot_l = kSlots ? p.pool_w + (int64_t)layer * p.pool_stride : nullptr;
+    const uint8_t* host_l = kSlots ? p.host + (int64_t)layer * p.host_stride : nullptr;
+    for (int32_t base = 0; base < npieces; base += 64 * kU) {
+      u32x4 v[kU];
+      uint8_t* slot_dst[kU];
+      bool st[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int32_t g = base + u * 64 + lane;
-      v[u] = u32x4{0u, 0u, 0u, 0u};
-      slot_dst[u] = nullptr;
-      st[u] = false;
-      if (g < npieces) {
-        const int32_t el = g / pieces;
+      for (int u = 0; u < kU; ++u) {
+        const int32_t g = base + u * 64 + lane;
+        const bool in = g < npieces;
+        const int32_t el = in ? g / pieces : 0;
         const int32_t pc = g - el * pieces;
-        const int32_t code = rows[el];
-        if (code >= 0) {
-          st[u] = out != nullptr;
-          if (out && code < p.pool_rows)
-            v[u] = *reinterpret_cast<const u32x4*>(pool_l + (int64_t)code * p.row_bytes +
-                                                   pc * 16);
-        } else if (MODE == kMoveFused && code <= -8) {
-          st[u] = out != nullptr;
-          const int32_t q = (-code - 8) >> 1;
-          const bool copier = ((-code - 8) & 1) != 0;
-          if (out || copier) {
-            const int32_t t = topk[el];
-            if (t >= 0 && (t >> ps) < p.max_pages && q < p.hot_capacity) {
-              const int32_t hb = hbt[t >> ps];
-              if (hb >= 0 && hb < host_blocks) {
-                const int64_t srow = ((int64_t)hb << ps) | (t & pm);
-                v[u] = *reinterpret_cast<const u32x4*>(host_l + srow * p.row_bytes + pc * 16);
-                const int32_t hblk = hot[q >> ps];
-                if (copier && hblk >= 0 && hblk < (p.pool_rows >> ps)) {
-                  const int64_t drow = ((int64_t)hblk << ps) | (q & pm);
-                  slot_dst[u] = slot_l + drow * p.row_bytes + pc * 16;
-                }
-              }
-            }
-          }
-        } else {
-          st[u] = out != nullptr;  // zero row
+        // every lane takes part in the exchange (lanes past the pieces read entry 0)
+        const int32_t ek = __builtin_amdgcn_ds_bpermute(el << 2, kind);
+        const int32_t es = __builtin_amdgcn_ds_bpermute(el << 2, src);
+        const int32_t ed = kSlots ? __builtin_amdgcn_ds_bpermute(el << 2, drow) : -1;
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        slot_dst[u] = nullptr;
+        st[u] = in && out != nullptr;
+        if (in && ek == 1)
+          v[u] = *reinterpret_cast<const u32x4*>(pool_l + (int64_t)es * p.row_bytes + pc * 16);
+        if (kSlots && in && ek == 2) {
+          v[u] = *reinterpret_cast<const u32x4*>(host_l + (int64_t)es * p.row_bytes + pc * 16);
+          if (ed >= 0) slot_dst[u] = slot_l + (int64_t)ed * p.row_bytes + pc * 16;
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int32_t g = base + u * 64 + lane;
-      if (st[u])
-        __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + (int64_t)g * 16));
-      if (kSlots && slot_dst[u]) *reinterpret_cast<u32x4*>(slot_dst[u]) = v[u];
-    }
-  }
-  }  // layers of the group
-  if (kSlots && lane < ne) {
-    // only this wave reads these entries' codes, and all its reads are done
-    const int32_t code = rows[lane];
-    if (code <= -8) {
-      const int32_t q = (-code - 8) >> 1;
-      if (q < p.hot_capacity) {
-        if ((-code - 8) & 1) stok[q] = topk[lane];
-        rows[lane] = (int32_t)(((int64_t)hot[q >> ps] << ps) | (q & pm));
-      } else {
-        rows[lane] = -3;
+      for (int u = 0; u < kU; ++u) {
+        const int32_t g = base + u * 64 + lane;
+        if (st[u])
+          __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(out + (int64_t)g * 16));
+        if (kSlots && slot_dst[u]) *reinterpret_cast<u32x4*>(slot_dst[u]) = v[u];
       }
+    }
+  }  // layers of the group
+  if (kSlots && has_e && code <= -8) {
+    // only this wave reads these entries' codes, and it read them all above
+    if (q < p.hot_capacity) {
+      if (copier) p.slot_token[(int64_t)rl * p.hot_capacity + q] = t;
+      rows[lane] = (int32_t)(((int64_t)hblk << ps) | (q & pm));
+    } else {
+      rows[lane] = -3;
     }
   }
 }
+
 
 // Entries per wave of the commit: few enough that a chunk full of misses is
 // copied by a wave in a few rounds of loads (64 entries of 656-byte rows would
