@@ -247,6 +247,10 @@ CASES = [
     ("rb1024", 2, 3, 1, 513, 512, 64, 1024, 50, False),
     # rows of one 16-byte piece (the fill's piece division has no multiplier)
     ("rb16", 4, 2, 2, 431, 352, 32, 16, 193, True),
+    # the largest rows the resolving calls take (256 pieces), at the most
+    # entries a request-layer holds (the fill's piece counters at their largest)
+    ("rb4096", 2, 1, 2, 500, 256, 16, 4096, 20, True),
+    ("rb4096_max_entries", 1, 1, 4, 2048, 4096, 64, 4096, 80, False),
     # pages of one token and of 1024 and 4096 tokens
     ("page1", 3, 1, 1, 200, 64, 1, 656, 400, False),
     ("page1024", 3, 1, 1, 700, 2048, 1024, 16, 12, False),
