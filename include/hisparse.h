@@ -42,7 +42,8 @@
  *   slot_stamp uint32 [R][L][C]: LRU stamp of each slot, 0 = never used.
  *   topk       int32 [R][L][P][K] (P = 1 for hs_resolve); -1 = padding.
  *   row_ids    int32, same shape as topk:  >= 0 pool row;  -1 padding;
- *              -2 overflow (no hot slot left; only possible with P > 1);
+ *              -2 overflow (no usable hot slot left for the miss: never when
+ *              P = 1 and C >= K with every hot block usable);
  *              -3 invalid (outside [0, ctx), or neither resident nor on host).
  *   stats      int32 [R][L][8] = {resident, hit, miss, overflow, invalid,
  *              pad, dup, 0}; the first five count distinct tokens, pad and

@@ -295,6 +295,27 @@ def test_policy_driven_small(group):
     assert totals[2] > 0 and totals[1] > 0
 
 
+def _policy_sweep_params(seed):
+    """Random policy-driven workloads: batch, layers (in groups of 1 or 2),
+    list length, hot capacity, context range, growth a step and the pool's
+    slack, which sets how soon evictions and new leases start."""
+    rs = np.random.default_rng(4000 + seed)
+    group = int(rs.choice([1, 2]))
+    C = 64 * int(rs.integers(2, 17))
+    return dict(name=f"policy_sweep_{seed}", seed=5000 + seed, R=int(rs.integers(2, 11)),
+                L=group * int(rs.integers(1, 3)), K=int(rs.integers(16, 513)), C=C,
+                steps=int(rs.integers(8, 21)), ctx_lo=int(rs.integers(1024, 6000)),
+                ctx_hi=int(rs.integers(6000, 14000)), append=int(rs.integers(1, 80)),
+                slack=int(rs.integers(4, 40)), tail_pages=int(rs.integers(1, 6)), group=group)
+
+
+@pytest.mark.parametrize("seed", list(range(6)))
+def test_policy_driven_sweep(seed):
+    """Policy-driven runs of random shapes, every step against the oracle."""
+    wl, dec = policy_workload(**_policy_sweep_params(seed))
+    run_parity(wl)
+
+
 def test_policy_driven_decode():
     """The same at decode size: 32 requests at 60-80 k tokens, top-K 2048,
     hot buffer 4096, 64 tokens appended per step."""
