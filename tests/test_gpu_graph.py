@@ -67,7 +67,7 @@ def _restore(dev, snap):
         getattr(dev, k).copy_(snap[k])
 
 
-@pytest.mark.parametrize("wl_name", ["mixed_decode", "multi_layer"])
+@pytest.mark.parametrize("wl_name", ["mixed_decode", "multi_layer", "multi_layer_wide"])
 def test_graph_replays_match_eager(wl_name):
     from serving_memory_tier_amd.hipgraph import HipRuntime
     from serving_memory_tier_amd.runner import DeviceRun
@@ -78,11 +78,16 @@ def test_graph_replays_match_eager(wl_name):
         wl = hs_gen.mixed_decode(R=8, steps=20)
         warm, n_cap = 12, 6
         assert wl.steps[16].hbt_set.shape[0] == 8
-    else:
+    elif wl_name == "multi_layer":
         # turns with prefill, completed pages offloaded and pages leaving the tail
         wl = hs_gen.multi_layer(turns=4, R=4, L=4)
         warm, n_cap = 1, 3
         assert sum(s.offload.shape[0] + s.bt_set.shape[0] for s in wl.steps[1:]) > 0
+    else:
+        # 160 request-layers: more than half a round of resolver workgroups, so
+        # the captured fused launches interleave resolvers and gathers
+        wl = hs_gen.multi_layer(turns=3, R=40, L=4)
+        warm, n_cap = 1, 2
     hip = HipRuntime()
     runs = [DeviceRun(wl), DeviceRun(wl)]
     eager, graphed = runs
