@@ -8,8 +8,9 @@ their rows, hot-block leases and the reset of a re-leased hot buffer -- as
 plain device-tensor writes; these are host-side residency policy, not part of
 the hot path.  Each step then calls the C ABI through the binding:
 ``hs_resolve`` (or ``hs_plan_replay`` for several query positions), whose
-gather runs on the same stream, and after the step ``hs_offload_prefix_pages``
-for the pages that completed.
+gather runs on the same stream, and ``hs_offload_prefix_pages`` for the pages
+that completed: in the launched steps on a second stream beside the resolve,
+joined before the step ends.
 """
 
 from __future__ import annotations
@@ -52,6 +53,11 @@ def update_runs(arr: np.ndarray):
     return min(cuts, key=len)
 
 
+# offloads from this size up run beside the resolve (launch_step): the
+# multi-layer turn's 505 MB, not a decode step's few pages
+OVERLAP_BYTES = 64 << 20
+
+
 class DeviceRun:
     def __init__(self, wl, device: str = "cuda", content_device: str | None = None,
                  fill_sync: bool = True):
@@ -90,6 +96,10 @@ class DeviceRun:
         self.entries = N
         self.topk = [None] * len(wl.steps)
         self.pairs = [None] * len(wl.steps)
+        # a step's prefix-page offload runs on a second stream, beside its
+        # resolve (device -> host against the resolve's host -> device reads);
+        # default priority, forked and joined by events inside the step
+        self.side = torch.cuda.Stream(device=dev)
 
     # -- scheduler side (between steps) ------------------------------------
     def upload_steps(self) -> None:
@@ -205,10 +215,19 @@ class DeviceRun:
                 hip.memcpy2d_h2d(dst, pitch, src, 4, 4, n, stream)
 
     def launch_step(self, i: int, hip, stream: int, stats=None, serial: bool = False,
-                    offload: bool = True) -> None:
+                    offload: bool = True, overlap: bool = True) -> None:
         """Step ``i`` on ``stream`` with no host work: the scheduler's table
-        updates as copies from pinned memory, then one hs_plan_replay
-        call (resolve, gather, offload of the pages the step completed).
+        updates as copies from pinned memory, then the resolve (one
+        hs_plan_replay call: fused resolve and gather, commit) and the offload
+        of the pages the step completed.
+        ``overlap``: an offload of at least OVERLAP_BYTES runs on a second
+        stream beside the resolve, forked after the table updates and joined
+        before the step ends (the link carries the offload's writes to host
+        and the misses' reads from it at once; the offloaded pages are
+        resident, so the resolve reads them in place, never their host copies
+        being written).  Smaller offloads, or False: one hs_plan_replay call
+        with the offload pairs, the offload after the commit on ``stream``
+        (the fork and join cost more than a short offload gives back).
         ``serial``: the decide and move stages one after the other instead
         (the path the library takes without a gather output, with one).
         ``offload``: False leaves out the step's prefix-page offload."""
@@ -217,6 +236,16 @@ class DeviceRun:
         self._table_updates(i, hip, stream)
         st = self.stats if stats is None else stats
         n_off = s.offload.shape[0] if offload else 0
+        join = None
+        if n_off and overlap and not serial and n_off * wl.L * PAGE * ROW >= OVERLAP_BYTES:
+            fork, join = hip.new_event(), hip.new_event()  # owned by `hip`
+            side = self.side.cuda_stream
+            hip.record(fork, stream)
+            hip.wait(side, fork)
+            hs_offload_prefix_pages(self.layout, self.pool, self.host_pool, self.pairs[i], n_off,
+                                    side)
+            hip.record(join, side)
+            n_off = 0  # the resolve below carries no offload
         if wl.G > 1:
             assert not serial, "layer groups have no serial staged form"
             hs_resolve_grouped(self.layout, self.batches[i], wl.G, self.topk[i], wl.P, wl.K,
@@ -234,6 +263,8 @@ class DeviceRun:
             hs_plan_replay(self.layout, self.batches[i], self.topk[i], wl.P, wl.K, s.stamp,
                            self.rows, self.out, st, self.pairs[i] if n_off else None, n_off,
                            stream)
+        if join is not None:
+            hip.wait(stream, join)
 
     def launch_step_timed(self, i: int, hip, stream: int, ev, stats=None,
                           offload: bool = True) -> None:

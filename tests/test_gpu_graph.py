@@ -156,3 +156,50 @@ def test_graph_replays_match_eager(wl_name):
         hip.close()
         for d in runs:
             d.close()
+
+
+@pytest.mark.parametrize("wl_name", ["mixed_decode", "multi_layer"])
+def test_offload_beside_the_resolve_matches_in_order(wl_name):
+    """A step whose offload runs on a second stream beside the resolve (the
+    runner's default) leaves every byte -- rows, stats, gathered rows, state,
+    both pools -- as the same step with the offload after the commit on one
+    stream, step after step."""
+    from serving_memory_tier_amd.hipgraph import HipRuntime
+    from serving_memory_tier_amd.runner import DeviceRun
+
+    if wl_name == "mixed_decode":
+        wl = hs_gen.mixed_decode(R=8, steps=20)
+        steps = range(12, 20)                     # step 16 offloads a completed page
+    else:
+        wl = hs_gen.multi_layer(turns=4, R=4, L=4)
+        steps = range(4)
+    assert sum(wl.steps[i].offload.shape[0] for i in steps) > 0
+    import serving_memory_tier_amd.runner as runner
+    hip = HipRuntime()
+    a, b = DeviceRun(wl), DeviceRun(wl)
+    saved = runner.OVERLAP_BYTES
+    runner.OVERLAP_BYTES = 0          # every offload beside the resolve in `a`
+    try:
+        for d in (a, b):
+            d.upload_steps()
+            d.stage_steps()
+        sp = torch.cuda.current_stream().cuda_stream
+        for d in (a, b):
+            for i in range(steps[0]):
+                d.launch_step(i, hip, sp, overlap=False)
+        torch.cuda.synchronize()
+        for i in steps:
+            print(f"[graph] {wl_name}: offload beside the resolve, step {i}", flush=True)
+            a.launch_step(i, hip, sp, overlap=True)
+            b.launch_step(i, hip, sp, overlap=False)
+            torch.cuda.synchronize()
+            for x, y in ((a.rows, b.rows), (a.stats, b.stats), (a.out, b.out), (a.tok, b.tok),
+                         (a.stp, b.stp), (a.pool, b.pool), (a.bt, b.bt), (a.hbt, b.hbt)):
+                assert torch.equal(x, y), f"step {i}"
+            assert np.array_equal(a.host.numpy(), b.host.numpy()), f"host pool, step {i}"
+    finally:
+        runner.OVERLAP_BYTES = saved
+        a.close()
+        b.close()
+        hip.close()
+
