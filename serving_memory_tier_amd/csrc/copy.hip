@@ -251,27 +251,33 @@ __global__ void __launch_bounds__(kT) commit_kernel(MoveParams p, int32_t chunks
   }
 }
 
-// One workgroup copies one page of one layer: blockIdx.x = pair, blockIdx.y = layer.
+// Workgroup b copies the pages of (pair, layer) items b, b + G, b + 2G, ...
+// (G workgroups, item = layer * n + pair); G is bounded, so that an offload
+// running beside other kernels leaves them most of the chip -- the link, not
+// the number of workgroups, sets its rate.
 __global__ void __launch_bounds__(kT) offload_kernel(OffloadParams p) {
-  const int32_t i = blockIdx.x;
-  const int32_t layer = blockIdx.y;
-  const int64_t db = p.pairs[2 * i];
-  const int64_t hb = p.pairs[2 * i + 1];
-  if (db < 0 || db >= p.pool_blocks || hb < 0 || hb >= p.host_blocks) return;
-  const uint8_t* src = p.pool + (int64_t)layer * p.pool_stride + db * p.page_bytes;
-  uint8_t* dst = p.host + (int64_t)layer * p.host_stride + hb * p.page_bytes;
+  const int64_t items = (int64_t)p.n * p.num_layers;
   const int32_t n = (int32_t)(p.page_bytes >> 4);
-  for (int32_t b = threadIdx.x; b < n; b += kT * kU) {
-    u32x4 v[kU];
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int32_t layer = (int32_t)(it / p.n);
+    const int32_t i = (int32_t)(it - (int64_t)layer * p.n);
+    const int64_t db = p.pairs[2 * i];
+    const int64_t hb = p.pairs[2 * i + 1];
+    if (db < 0 || db >= p.pool_blocks || hb < 0 || hb >= p.host_blocks) continue;
+    const uint8_t* src = p.pool + (int64_t)layer * p.pool_stride + db * p.page_bytes;
+    uint8_t* dst = p.host + (int64_t)layer * p.host_stride + hb * p.page_bytes;
+    for (int32_t b = threadIdx.x; b < n; b += kT * kU) {
+      u32x4 v[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int32_t g = b + u * kT;
-      if (g < n) v[u] = *reinterpret_cast<const u32x4*>(src + (int64_t)g * 16);
-    }
+      for (int u = 0; u < kU; ++u) {
+        const int32_t g = b + u * kT;
+        if (g < n) v[u] = *reinterpret_cast<const u32x4*>(src + (int64_t)g * 16);
+      }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int32_t g = b + u * kT;
-      if (g < n) *reinterpret_cast<u32x4*>(dst + (int64_t)g * 16) = v[u];
+      for (int u = 0; u < kU; ++u) {
+        const int32_t g = b + u * kT;
+        if (g < n) *reinterpret_cast<u32x4*>(dst + (int64_t)g * 16) = v[u];
+      }
     }
   }
 }
@@ -311,8 +317,9 @@ hipError_t launch_move(const MoveParams& p, MoveMode mode, hipStream_t stream) {
 
 hipError_t launch_offload(const OffloadParams& p, hipStream_t stream) {
   if (p.n == 0 || p.num_layers == 0) return hipSuccess;
-  return launch_kernel(offload_kernel, dim3((uint32_t)p.n, (uint32_t)p.num_layers), dim3(kT), 0,
-                       stream, p);
+  const int64_t items = (int64_t)p.n * p.num_layers;
+  const int64_t grid = items < kOffloadGroups ? items : kOffloadGroups;
+  return launch_kernel(offload_kernel, dim3((uint32_t)grid), dim3(kT), 0, stream, p);
 }
 
 }  // namespace hs

@@ -18,6 +18,10 @@ constexpr int kResolveThreads = HS_RESOLVE_THREADS;
 // per iteration.
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
+// Workgroups of the prefix-page offload, at most (each loops over its pages):
+// 32 x 256 threads with 4 stores in flight each keep the link's device-to-host
+// direction full and leave the rest of the chip to a resolve running beside
+constexpr int64_t kOffloadGroups = 32;
 
 struct ResolveParams {
   // layout
