@@ -12,8 +12,9 @@
 // Both kernels are bound by memory bandwidth -- HBM for the gather, the host
 // link for miss rows and offloaded pages -- not by arithmetic.  They move
 // 16-byte pieces, consecutive lanes on consecutive pieces, several loads in
-// flight per lane before any store, on grids that cover all 256 CUs many
-// times over.  In the mover each wave owns kMoveEntriesPerWave whole entries:
+// flight per lane before any store; the mover's grid covers all 256 CUs many
+// times over, the offload's is a few workgroups that loop, which is enough
+// for the link.  In the mover each wave owns kMoveEntriesPerWave whole entries:
 // host-link reads of the misses and HBM reads of the resident and hot rows
 // are interleaved across every wave of the chip, so the two links run at the
 // same time instead of one after the other.
