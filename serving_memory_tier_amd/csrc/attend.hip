@@ -133,11 +133,19 @@ struct BlockRegs {
 __device__ __forceinline__ void fetch_block(const AttendParams& p, const AttendLds& s,
                                             int32_t k0, BlockRegs& b) {
   const int tid = threadIdx.x;
+  // every round's row id first (a key inside the block for each lane, so the
+  // reads need no branch and are issued together), then the row loads
+  int32_t ids[kFetchRounds];
+#pragma unroll
+  for (int i = 0; i < kFetchRounds; ++i) {
+    const int q = tid + kT * i;
+    ids[i] = s.ids[k0 + (q < kBlockPieces ? q / kPieces : 0)];
+  }
 #pragma unroll
   for (int i = 0; i < kFetchRounds; ++i) {
     const int q = tid + kT * i;
     const int k = q / kPieces, pc = q - k * kPieces;
-    const int32_t id = q < kBlockPieces ? s.ids[k0 + k] : -1;
+    const int32_t id = q < kBlockPieces ? ids[i] : -1;
     b.id[i] = id;
     if (p.pool_rows > 0 && q < kBlockPieces)
       b.v[i] = *reinterpret_cast<const u32x4*>(p.kv + (int64_t)(id >= 0 ? id : 0) * kRowBytes +
@@ -267,14 +275,23 @@ __global__ void __launch_bounds__(kT) attend_kernel(AttendParams p) {
             acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp[h], qb[16 + h], acc[4], 0, 0, 0);
         }
       }
+      // the four keys' scales and row ids read together, before any score
+      // is written (the writes would otherwise order each read after them)
+      f32x4 sc4[4];
+      int32_t sel[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = half * 16 + 4 * g + r;
-        const f32x4 sc4 = *reinterpret_cast<const f32x4*>(cb.rows + slot(key) * kRowBytes + kLatent);
+        sc4[r] = *reinterpret_cast<const f32x4*>(cb.rows + slot(key) * kRowBytes + kLatent);
+        sel[r] = s.ids[bi * kBlockKeys + key];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = half * 16 + 4 * g + r;
         float v = acc[4][r];
 #pragma unroll
-        for (int tl = 0; tl < 4; ++tl) v += sc4[tl] * acc[tl][r];
-        xs[ht][key][col] = s.ids[bi * kBlockKeys + key] >= 0 ? v * qk_scale : -INFINITY;
+        for (int tl = 0; tl < 4; ++tl) v += sc4[r][tl] * acc[tl][r];
+        xs[ht][key][col] = sel[r] >= 0 ? v * qk_scale : -INFINITY;
       }
     }
     HS_ATTEND_MARK(1);
