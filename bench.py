@@ -242,8 +242,15 @@ def main():
 
     # per-kernel durations: the next KE steps launched as hs_plan_replay's
     # stages on the launch stream (the fused resolve-and-fill launch, the
-    # commit, the offload), HIP events on that stream around every kernel
-    events = [[hev.new_event() for _ in range(4)] for _ in range(KE)]
+    # commit, the offload), HIP events on that stream around every kernel.
+    # The events before the offload release to device scope only (a
+    # system-scope release at each record adds about a microsecond to the
+    # kernel it closes); the one after it, whose kernel writes host memory,
+    # keeps the system scope.
+    def step_events():
+        return [hev.new_event(system_fence=False) for _ in range(3)] + [hev.new_event()]
+
+    events = [step_events() for _ in range(KE)]
     busy = QueueFiller()
     for j in range(KE):
         busy.fill()
@@ -292,7 +299,7 @@ def main():
     cold = None
     if NC:
         scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        cev = [[hev.new_event() for _ in range(4)] for _ in range(NC)]
+        cev = [step_events() for _ in range(NC)]
         cst = torch.zeros((NC, wl.R, wl.NG, 8), dtype=torch.int32, device="cuda")
         for j in range(NC):
             scrub.fill_(j & 0xFF)
@@ -313,7 +320,7 @@ def main():
     # every non-resident token hits, no host traffic, HBM-bound
     last = W + K + KE + NC - 1
     NR = args.hit_replays
-    rep = [[hev.new_event() for _ in range(4)] for _ in range(NR)]
+    rep = [step_events() for _ in range(NR)]
     rep_stats = torch.zeros((wl.R, wl.NG, 8), dtype=torch.int32, device="cuda")
     for j in range(NR):
         busy.fill()
@@ -531,7 +538,9 @@ def consumer_cost(wl, hev, stream: int, busy, n_steps: int = 16, heads: int = 12
             "consumer shapes must match the batch's row ids and gathered rows"
         assert dev.out.shape[-1] == ROW
         lay_kv = hs.layout_of(1, ROW, 1, 64, wl.pool_rows if mode == "in_place" else T * K, 0)
-        ev = [(hev.new_event(), hev.new_event(), hev.new_event()) for _ in range(n_steps)]
+        # the middle event closes a call whose offload writes host memory
+        ev = [(hev.new_event(system_fence=False), hev.new_event(), hev.new_event(system_fence=False))
+              for _ in range(n_steps)]
         for i in range(n_steps):
             s = wl.steps[i]
             dev.pre(i)
@@ -594,7 +603,7 @@ def miss_path_cost(hev, stream: int, busy, reps: int = 8):
     dev = DeviceRun(wl)
     dev.upload_steps()
     dev.stage_steps()
-    ev = [[hev.new_event() for _ in range(4)] for _ in range(reps)]
+    ev = [[hev.new_event(system_fence=False) for _ in range(4)] for _ in range(reps)]
     stats = torch.zeros((reps, wl.R, wl.NG, 8), dtype=torch.int32, device="cuda")
     for j in range(reps):
         dev.tok.fill_(-1)
@@ -628,7 +637,7 @@ def probe_ceilings(hev, stream: int, busy):
     def best(fn, nbytes, reps=3):
         t = []
         for _ in range(reps):
-            a, b = hev.new_event(), hev.new_event()
+            a, b = hev.new_event(), hev.new_event()   # copies to and from host memory
             busy.fill()
             hev.record(a, stream)
             fn()
@@ -704,7 +713,7 @@ def touch_cost(wl, dev, hev, stream: int, i: int, n: int, busy=None):
                           cap.cuda_stream)
     finally:
         hev.end_capture(cap.cuda_stream)
-    a, b = hev.new_event(), hev.new_event()
+    a, b = hev.new_event(system_fence=False), hev.new_event(system_fence=False)
     hev.launch(stream)                    # warm replay
     torch.cuda.synchronize()
     if busy is not None:

@@ -14,6 +14,7 @@ import ctypes
 
 _CAPTURE_RELAXED = 2
 _H2D = 1
+_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
 
 def _runtime() -> ctypes.CDLL:
@@ -30,6 +31,7 @@ class HipRuntime:
         self.ct = ct
         self.hip = hip = _runtime()
         hip.hipEventCreate.argtypes = [ct.POINTER(ct.c_void_p)]
+        hip.hipEventCreateWithFlags.argtypes = [ct.POINTER(ct.c_void_p), ct.c_uint]
         hip.hipEventRecord.argtypes = [ct.c_void_p, ct.c_void_p]
         hip.hipStreamWaitEvent.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_uint]
         hip.hipEventElapsedTime.argtypes = [ct.POINTER(ct.c_float), ct.c_void_p, ct.c_void_p]
@@ -50,9 +52,15 @@ class HipRuntime:
         self.graph = self.exec = None
 
     # -- events -------------------------------------------------------------
-    def new_event(self):
+    def new_event(self, system_fence: bool = True):
+        """An event; ``system_fence`` False: its records release to device
+        scope only (hipEventDisableSystemFence), for events that only time
+        kernels -- the system-scope release costs each record about a
+        microsecond that would be counted as kernel time."""
         e = self.ct.c_void_p()
-        if self.hip.hipEventCreate(self.ct.byref(e)) != 0:
+        rc = (self.hip.hipEventCreate(self.ct.byref(e)) if system_fence else
+              self.hip.hipEventCreateWithFlags(self.ct.byref(e), _EVENT_DISABLE_SYSTEM_FENCE))
+        if rc != 0:
             raise RuntimeError("hipEventCreate failed")
         self.made.append(e)
         return e
